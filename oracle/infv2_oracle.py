@@ -1,0 +1,331 @@
+"""fp64 CPU oracle for InfLLM-V2 dense-sparse switchable attention (forward).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the test suite, the smoke check and the benchmark's
+CPU-baseline leg use it.  It shares no code with the HIP library.
+
+Plain NumPy, float64 throughout.  Every function follows one passage of the
+pages, named in its docstring as  [page title, section].  The pages are:
+
+  * "Infllm V2 Dense Sparse Switchable Attention" (skill page), with the
+    sections Architecture Overview; Step 1: Dense Attention Layer Foundation;
+    Step 2: Sparse Pattern Selection Module; Step 3: Switchable Attention with
+    Pattern Router; Practical Guidance (When NOT to Use, Common Pitfalls).
+  * "InfLLM-V2: Dense-Sparse Switchable Attention for Seamless Short-to-Long
+    Adaptation" (paper page), Abstract.
+  * The InfLLM-V2 news summary (reportify), sections Model Advantages and
+    Technical Mechanism.
+
+Readings where the pages are silent or contradict one another are stated in
+each docstring (they are listed together in the design notes of the repo).
+
+Conventions
+-----------
+* Tensors are [B, H, S, D] (skill page, Step 2, shape docstrings).  bf16
+  inputs arrive as uint16 bit patterns and are widened exactly to float64.
+* Query head h uses KV head h // G, G = H_q / H_kv (consecutive GQA groups).
+* Query row r sits at absolute position i = (S_k - S_q) + r (bottom-right
+  alignment, so one decode query is the last token of the cache).
+* Block j holds key positions [j*BS, (j+1)*BS).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# bf16 <-> float64
+# ---------------------------------------------------------------------------
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (uint16) to float64."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16(x) -> np.ndarray:
+    """Round float64 directly to bf16 (8 significant bits), nearest-even.
+
+    Returns uint16 bit patterns.  The rounding is done in float64 on the
+    integer significand (np.round rounds halves to even), so there is no
+    intermediate float32 rounding step.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                      # x = m * 2**e, 0.5 <= |m| < 1
+    e = np.maximum(e, -125)                 # below 2**-126 bf16 is subnormal
+    quantum = np.ldexp(1.0, e - 8)          # weight of the last kept bit
+    r = np.round(x / quantum) * quantum     # exact: quantum is a power of two
+    with np.errstate(over="ignore"):
+        r32 = r.astype(np.float32)          # exact (<= 8 significant bits) or inf
+    return (r32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# a1: key compression
+# ---------------------------------------------------------------------------
+
+
+def compress_k(k: np.ndarray, block_size: int) -> tuple[np.ndarray, np.ndarray]:
+    """Block-mean compression of the keys.
+
+    [skill page, Step 2: Sparse Pattern Selection Module, compressed_attention]:
+    pad the sequence with zeros to a multiple of the block size, view it as
+    non-overlapping blocks and take the mean over each block's tokens.  The
+    divisor is the block size also for the zero-padded last block.
+
+    Reading: only K is compressed on the hot path (the compressed keys feed
+    block selection); the mean is rounded once to bf16, nearest-even.
+
+    k: float64 [B, H, S, D].  Returns (k_cmp_bits uint16, k_cmp float64), both
+    [B, H, ceil(S/BS), D]; k_cmp holds the bf16 values widened back.
+    """
+    B, H, S, D = k.shape
+    nb = (S + block_size - 1) // block_size
+    padded = np.zeros((B, H, nb * block_size, D), dtype=np.float64)
+    padded[:, :, :S, :] = k
+    mean = padded.reshape(B, H, nb, block_size, D).mean(axis=3)
+    bits = f64_to_bf16(mean)
+    return bits, bf16_to_f64(bits)
+
+
+# ---------------------------------------------------------------------------
+# a2: group-summed block scores
+# ---------------------------------------------------------------------------
+
+
+def visible_blocks(i: int, block_size: int) -> int:
+    """Number of compressed blocks fully at or before position i: floor((i+1)/BS).
+
+    Reading: a compressed key stands for its whole block, so a query may only
+    score blocks whose every token is visible to it; the pages require the
+    sparse patterns to stay causal [skill page, Practical Guidance, When NOT
+    to Use].  The unmasked softmax of compressed_attention is not followed.
+    """
+    return (i + 1) // block_size
+
+
+def group_scores(q: np.ndarray, k_cmp: np.ndarray, b: int, g: int, i: int,
+                 r: int, G: int, scale: float, block_size: int) -> np.ndarray:
+    """Group score sigma_j of every fully visible block j for one query row.
+
+    [skill page, Architecture Overview, Hardware Kernel] sums normalised scores
+    over the heads of a head group, the normalisation being a log-sum-exp;
+    [skill page, Step 2, compressed_attention] gives the scores themselves:
+    softmax over the scaled products of the query with the compressed keys.
+
+    For each head h of group g:  z_hj = scale * <q_h, k_cmp_j>,
+    p_hj = exp(z_hj - logsumexp_j z_hj); then sigma_j = sum_h p_hj.
+    The log-sum-exp is exact (the pages leave its approximation undefined).
+
+    Returns float64 [nv]; empty when no block is fully visible.
+    """
+    nv = visible_blocks(i, block_size)
+    if nv == 0:
+        return np.zeros(0)
+    qh = q[b, g * G:(g + 1) * G, r, :]                 # [G, D]
+    z = scale * (qh @ k_cmp[b, g, :nv, :].T)            # [G, nv]
+    zmax = z.max(axis=1, keepdims=True)
+    lse = zmax + np.log(np.exp(z - zmax).sum(axis=1, keepdims=True))
+    p = np.exp(z - lse)
+    return p.sum(axis=0)
+
+
+# ---------------------------------------------------------------------------
+# a3: top-k block selection
+# ---------------------------------------------------------------------------
+
+
+def candidates(i: int, block_size: int, n_init: int, n_local: int) -> np.ndarray:
+    """Candidate blocks of the query at position i: n_init <= j <= qb - n_local.
+
+    The initial blocks and the sliding-window blocks are always attended
+    (see forced_blocks), so they are not candidates; every candidate is fully
+    visible because n_local >= 1.
+    """
+    qb = i // block_size
+    lo, hi = n_init, qb - n_local
+    if hi < lo:
+        return np.zeros(0, dtype=np.int64)
+    return np.arange(lo, hi + 1, dtype=np.int64)
+
+
+def select_row(sigma: np.ndarray, i: int, block_size: int, topk: int,
+               n_init: int, n_local: int) -> np.ndarray:
+    """Top-k candidate blocks of one query row, ascending, -1 padded to topk.
+
+    [skill page, Step 2, selected_attention] keeps the top-k per query
+    position; [news summary, Technical Mechanism] makes the unit of selection
+    a block.  Order: larger sigma first; equal sigma goes to the lower block
+    index.  With fewer candidates than topk all of them are kept.
+    """
+    c = candidates(i, block_size, n_init, n_local)
+    out = np.full(topk, -1, dtype=np.int32)
+    if topk == 0 or c.size == 0:
+        return out
+    order = np.lexsort((c, -sigma[c]))           # primary -sigma, then index
+    chosen = np.sort(c[order[:min(topk, c.size)]])
+    out[:chosen.size] = chosen
+    return out
+
+
+def select_blocks(q: np.ndarray, k_cmp: np.ndarray, S_k: int, topk: int,
+                  n_init: int, n_local: int, block_size: int, scale: float,
+                  rows=None, return_scores: bool = False):
+    """Selected block indices for every (b, KV group g, query row r).
+
+    q float64 [B, H_q, S_q, D]; k_cmp float64 [B, H_kv, NB, D].
+    Returns int32 [B, H_kv, len(rows), topk]; with return_scores also a list
+    (same order) of the float64 sigma vectors per row.
+    """
+    B, H_q, S_q, _ = q.shape
+    H_kv = k_cmp.shape[1]
+    G = H_q // H_kv
+    off = S_k - S_q
+    rows = np.arange(S_q) if rows is None else np.asarray(rows)
+    idx = np.full((B, H_kv, rows.size, topk), -1, dtype=np.int32)
+    scores = {}
+    for b in range(B):
+        for g in range(H_kv):
+            for n, r in enumerate(rows):
+                i = off + int(r)
+                sig = group_scores(q, k_cmp, b, g, i, int(r), G, scale, block_size)
+                idx[b, g, n] = select_row(sig, i, block_size, topk, n_init, n_local)
+                if return_scores:
+                    scores[(b, g, int(r))] = sig
+    return (idx, scores) if return_scores else idx
+
+
+# ---------------------------------------------------------------------------
+# a4: block-sparse attention
+# ---------------------------------------------------------------------------
+
+
+def forced_blocks(i: int, block_size: int, n_init: int, n_local: int) -> list[int]:
+    """Blocks every query attends regardless of scores.
+
+    Reading: the first n_init blocks (initial / sink blocks) and a causal,
+    block-granular sliding window made of the query's own block and the
+    n_local - 1 blocks before it.  [skill page, Step 2, sliding_attention]
+    keeps local context; [skill page, Practical Guidance, When NOT to Use]
+    requires the window to respect causality, so its symmetric token window
+    is not followed.
+    """
+    qb = i // block_size
+    f = set(range(0, min(n_init, qb + 1)))
+    f.update(range(max(qb - n_local + 1, 0), qb + 1))
+    return sorted(f)
+
+
+def attend_keys(i: int, blocks, block_size: int, S_k: int) -> np.ndarray:
+    """Key positions t <= i inside the given blocks (causal within a block)."""
+    ts = [np.arange(j * block_size, min((j + 1) * block_size, S_k)) for j in sorted(set(blocks))]
+    t = np.concatenate(ts) if ts else np.zeros(0, dtype=np.int64)
+    return t[t <= i]
+
+
+def _softmax_attend(qh: np.ndarray, kk: np.ndarray, vv: np.ndarray, scale: float):
+    """softmax(scale * q k^T) v and its natural-log log-sum-exp, per head.
+
+    [skill page, Step 1: Dense Attention Layer Foundation]: scores are the
+    scaled query-key products, weights their softmax, the context the weighted
+    sum of values.  qh [G, D], kk/vv [T, D].
+    """
+    z = scale * (qh @ kk.T)                                  # [G, T]
+    zmax = z.max(axis=1, keepdims=True)
+    w = np.exp(z - zmax)
+    l = w.sum(axis=1, keepdims=True)
+    return (w / l) @ vv, (zmax + np.log(l))[:, 0]
+
+
+def sparse_attn(q, k, v, blk_idx, block_size: int, n_init: int, n_local: int,
+                scale: float, rows=None):
+    """Attention restricted to the forced blocks and the selected blocks.
+
+    [news summary, Technical Mechanism]: attention is computed only on the
+    selected subsets of key-value blocks.  Attended set of the query at
+    position i: forced_blocks(i) union the row's selected blocks (entries
+    >= 0 of blk_idx); keys beyond i are masked (causal).
+
+    q [B,H_q,S_q,D]; k, v [B,H_kv,S_k,D]; blk_idx int [B,H_kv,n_rows,topk]
+    aligned with ``rows``.  Returns (out [B,H_q,n_rows,D], lse [B,H_q,n_rows]).
+    """
+    B, H_q, S_q, D = q.shape
+    H_kv, S_k = k.shape[1], k.shape[2]
+    G = H_q // H_kv
+    off = S_k - S_q
+    rows = np.arange(S_q) if rows is None else np.asarray(rows)
+    out = np.zeros((B, H_q, rows.size, D))
+    lse = np.zeros((B, H_q, rows.size))
+    for b in range(B):
+        for g in range(H_kv):
+            for n, r in enumerate(rows):
+                i = off + int(r)
+                sel = [int(j) for j in blk_idx[b, g, n] if j >= 0]
+                t = attend_keys(i, forced_blocks(i, block_size, n_init, n_local) + sel,
+                                block_size, S_k)
+                o, m = _softmax_attend(q[b, g * G:(g + 1) * G, int(r), :],
+                                       k[b, g, t, :], v[b, g, t, :], scale)
+                out[b, g * G:(g + 1) * G, n, :] = o
+                lse[b, g * G:(g + 1) * G, n] = m
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# a5: dense attention and the switch
+# ---------------------------------------------------------------------------
+
+
+def dense_attn(q, k, v, scale: float, causal: bool = True, rows=None):
+    """Full (causal) GQA attention.
+
+    [skill page, Step 1: Dense Attention Layer Foundation]: softmax of the
+    scaled products over all keys, then the weighted sum of values.  Causal
+    here means key t is visible to the query at position i iff t <= i.
+    Returns (out [B,H_q,n_rows,D], lse [B,H_q,n_rows]).
+    """
+    B, H_q, S_q, D = q.shape
+    H_kv, S_k = k.shape[1], k.shape[2]
+    G = H_q // H_kv
+    off = S_k - S_q
+    rows = np.arange(S_q) if rows is None else np.asarray(rows)
+    out = np.zeros((B, H_q, rows.size, D))
+    lse = np.zeros((B, H_q, rows.size))
+    for b in range(B):
+        for g in range(H_kv):
+            for n, r in enumerate(rows):
+                i = off + int(r)
+                t = np.arange(i + 1) if causal else np.arange(S_k)
+                o, m = _softmax_attend(q[b, g * G:(g + 1) * G, int(r), :],
+                                       k[b, g, t, :], v[b, g, t, :], scale)
+                out[b, g * G:(g + 1) * G, n, :] = o
+                lse[b, g * G:(g + 1) * G, n] = m
+    return out, lse
+
+
+def uses_dense(S_k: int, switch_len: int) -> bool:
+    """[skill page, Step 3: Switchable Attention with Pattern Router]: a
+    sequence no longer than the threshold takes the dense path (<=)."""
+    return S_k <= switch_len
+
+
+def attention(q, k, v, block_size: int, topk: int, n_init: int, n_local: int,
+              switch_len: int, scale: float | None = None, rows=None):
+    """The switch: dense causal attention for S_k <= switch_len, otherwise
+    compress -> select -> block-sparse attention.
+
+    [paper page, Abstract]: dense attention for short inputs, sparse for long.
+    [news summary, Technical Mechanism]: block selection, then attention on
+    the selected subsets.  Returns dict(out, lse, path, blk_idx, k_cmp_bits).
+    """
+    D = q.shape[-1]
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    S_k = k.shape[2]
+    if uses_dense(S_k, switch_len):
+        o, l = dense_attn(q, k, v, scale, causal=True, rows=rows)
+        return dict(out=o, lse=l, path="dense", blk_idx=None, k_cmp_bits=None)
+    bits, kc = compress_k(k, block_size)
+    idx = select_blocks(q, kc, S_k, topk, n_init, n_local, block_size, scale, rows=rows)
+    o, l = sparse_attn(q, k, v, idx, block_size, n_init, n_local, scale, rows=rows)
+    return dict(out=o, lse=l, path="sparse", blk_idx=idx, k_cmp_bits=bits)

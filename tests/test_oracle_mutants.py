@@ -1,0 +1,99 @@
+"""Planted mistakes in the oracle must make a pin fail (CPU only).
+
+Each mutant replaces one oracle function with a plausible wrong version (a
+dropped term, an off-by-one index, a flipped tie rule, a wrong head mapping)
+and runs the pins that should catch it.  The real oracle is restored after
+each case by monkeypatch.
+"""
+import numpy as np
+import pytest
+
+import oracle.infv2_oracle as impl
+import tests.test_oracle_pins as pins
+
+
+def _scores_no_normalisation(q, k_cmp, b, g, i, r, G, scale, block_size):
+    nv = impl.visible_blocks(i, block_size)
+    qh = q[b, g * G:(g + 1) * G, r, :]
+    return np.exp(scale * (qh @ k_cmp[b, g, :nv, :].T)).sum(axis=0)
+
+
+def _scores_wrong_head(q, k_cmp, b, g, i, r, G, scale, block_size):
+    nv = impl.visible_blocks(i, block_size)
+    if nv == 0:
+        return np.zeros(0)
+    qh = q[b, g::max(q.shape[1] // G, 1), r, :][:G]       # strided instead of consecutive heads
+    z = scale * (qh @ k_cmp[b, g, :nv, :].T)
+    p = np.exp(z - z.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    return p.sum(0)
+
+
+def _visible_off_by_one(i, block_size):
+    return i // block_size
+
+
+def _select_ties_high(sigma, i, block_size, topk, n_init, n_local):
+    c = impl.candidates(i, block_size, n_init, n_local)
+    out = np.full(topk, -1, dtype=np.int32)
+    if topk == 0 or c.size == 0:
+        return out
+    order = np.lexsort((-c, -sigma[c]))
+    chosen = np.sort(c[order[:min(topk, c.size)]])
+    out[:chosen.size] = chosen
+    return out
+
+
+def _forced_window_short(i, block_size, n_init, n_local):
+    qb = i // block_size
+    f = set(range(0, min(n_init, qb + 1)))
+    f.update(range(max(qb - n_local + 2, 0), qb + 1))
+    return sorted(f)
+
+
+def _compress_divide_by_count(k, block_size):
+    B, H, S, D = k.shape
+    nb = (S + block_size - 1) // block_size
+    out = np.zeros((B, H, nb, D))
+    for j in range(nb):
+        out[:, :, j] = k[:, :, j * block_size:(j + 1) * block_size].mean(axis=2)
+    bits = impl.f64_to_bf16(out)
+    return bits, impl.bf16_to_f64(bits)
+
+
+def _bf16_truncate(x):
+    x = np.asarray(x, dtype=np.float64).astype(np.float32)
+    return (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _softmax_attend_no_max_in_lse(qh, kk, vv, scale):
+    z = scale * (qh @ kk.T)
+    zmax = z.max(axis=1, keepdims=True)
+    w = np.exp(z - zmax)
+    l = w.sum(axis=1, keepdims=True)
+    return (w / l) @ vv, np.log(l)[:, 0]
+
+
+MUTANTS = [
+    ("group_scores", _scores_no_normalisation, [pins.test_scores_sum_to_group_size_and_nonnegative,
+                                                pins.test_scores_hand_derived_golden]),
+    ("group_scores", _scores_wrong_head, [pins.test_scores_group_uses_its_consecutive_heads_only]),
+    ("visible_blocks", _visible_off_by_one, [pins.test_scores_single_head_is_causal_softmax_over_compressed_keys]),
+    ("select_row", _select_ties_high, [pins.test_select_exhaustive_tiny,
+                                       pins.test_select_characterisation_random]),
+    ("forced_blocks", _forced_window_short, [pins.test_sparse_with_no_selection_is_sink_plus_window]),
+    ("compress_k", _compress_divide_by_count, [pins.test_compress_tail_zero_padded_divides_by_block_size]),
+    ("f64_to_bf16", _bf16_truncate, [pins.test_bf16_rounding_hand_cases]),
+    ("_softmax_attend", _softmax_attend_no_max_in_lse, [pins.test_dense_matches_torch_sdpa_fp64]),
+]
+
+
+@pytest.mark.parametrize("name,mutant,catchers", MUTANTS, ids=[m[0] + ":" + m[1].__name__ for m in MUTANTS])
+def test_pin_catches_mutant(monkeypatch, name, mutant, catchers):
+    monkeypatch.setattr(impl, name, mutant)
+    for pin in catchers:
+        with pytest.raises(AssertionError):
+            if pin is pins.test_dense_matches_torch_sdpa_fp64:
+                pin(96, 96, True)
+            else:
+                pin()
