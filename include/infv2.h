@@ -1,0 +1,160 @@
+/*
+ * infv2.h — C ABI of the InfLLM-V2 block-sparse attention forward path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages: "Infllm V2 Dense Sparse Switchable Attention", skill
+ * page; "InfLLM-V2: Dense-Sparse Switchable Attention for Seamless
+ * Short-to-Long Adaptation", paper page; the InfLLM-V2 news summary):
+ * keys are compressed into per-block means, every query token scores the
+ * blocks with a per-head softmax over the compressed keys summed over its
+ * GQA head group, picks the top-k blocks, and attends only to those blocks
+ * plus the initial blocks and a causal sliding window of blocks.  Short
+ * sequences take dense causal attention instead.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are contiguous, row-major, [B][H][S][D] (batch, heads, sequence,
+ *    head dim), as in the shape docstrings of the skill page, Step 2.
+ *    bf16 tensors are passed as raw 16-bit patterns (void*).
+ *  - All tensor pointers are DEVICE pointers owned by the caller; every
+ *    pointer must be 16-byte aligned.  Outputs must not alias inputs.
+ *  - GQA: query head h reads KV head h / G with G = H_q / H_kv.
+ *  - Query row r sits at absolute position i = (S_k - S_q) + r (bottom-right
+ *    alignment; a single decode query is the last token of its cache).
+ *  - Block j covers key positions [j*block_size, (j+1)*block_size);
+ *    NB = ceil(S_k / block_size).
+ *  - softmax_scale <= 0 selects 1/sqrt(D) (skill page, Step 1).
+ *  - stream is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on that stream and returns; it never allocates device
+ *    memory, never frees, never synchronises.  Device faults surface at the
+ *    caller's next synchronisation.
+ *  - Return value: INFV2_OK or an error code.  All argument checks run before
+ *    any HIP call; on an error nothing is launched and outputs are untouched.
+ *    Supported on the GPU: D = 128, block_size = 64, 1 <= G <= 16,
+ *    0 <= topk <= 256; other values give INFV2_ERR_UNSUPPORTED.
+ *  - Calls on distinct streams are independent; the library keeps no state
+ *    between calls apart from a per-process cache of device properties.
+ */
+#ifndef INFV2_H
+#define INFV2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum infv2_status {
+  INFV2_OK = 0,
+  INFV2_ERR_INVALID = 1,      /* null/misaligned pointer, bad size or count */
+  INFV2_ERR_UNSUPPORTED = 2,  /* valid, but outside what the kernels support */
+  INFV2_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required  */
+  INFV2_ERR_HIP = 4           /* the HIP runtime reported an error on launch */
+};
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* infv2_status_string(int status);
+
+/* ABI version; bumped whenever a signature or a layout changes. */
+int infv2_abi_version(void);
+
+/*
+ * Key compression (skill page, Step 2, compressed_attention: zero-pad to a
+ * multiple of the block size, mean over each block's tokens).
+ *   k      bf16 [B][H_kv][S_k][D]             (input)
+ *   k_cmp  bf16 [B][H_kv][NB][D]              (output)
+ * k_cmp[b,g,j,:] = bf16_RNE( sum_{t in block j, t < S_k} k[b,g,t,:] / block_size ).
+ * The tail block is zero-padded: its divisor is block_size, not its length.
+ * Sums are accumulated in fp64 and rounded once to bf16, nearest-even.
+ */
+int infv2_compress_k(const void* k, void* k_cmp,
+                     int B, int H_kv, int S_k, int D, int block_size,
+                     void* stream);
+
+/*
+ * Block selection: group-summed block scores and top-k (skill page,
+ * Architecture Overview: the kernel sums log-sum-exp–normalised scores over
+ * each head group; Step 2, selected_attention: top-k per query position; the
+ * news summary, Technical Mechanism: the unit of selection is a block).
+ *   q          bf16  [B][H_q][S_q][D]
+ *   k_cmp      bf16  [B][H_kv][NB][D]      (from infv2_compress_k)
+ *   blk_idx    int32 [B][H_kv][S_q][topk]  (output)
+ *   blk_score  fp32  [B][H_kv][S_q][topk]  (optional output, may be NULL)
+ * For query position i: nv = floor((i+1)/block_size) blocks are fully visible;
+ * per head h of group g, z_hj = scale*<q_h, k_cmp_j>, p_hj = exp(z_hj -
+ * logsumexp_{j<nv} z_hj) (exact log-sum-exp), sigma_j = sum_h p_hj.
+ * Candidates are n_init <= j <= floor(i/block_size) - n_local; the
+ * min(topk, #candidates) largest sigma are kept, equal sigma going to the
+ * lower index.  Indices are written ascending, the rest of the row is -1;
+ * blk_score holds sigma of each kept index (0 for padding).
+ * Requires n_init >= 0, n_local >= 1.  No workspace is needed.
+ */
+int infv2_select_blocks(const void* q, const void* k_cmp,
+                        int32_t* blk_idx, float* blk_score,
+                        int B, int H_q, int H_kv, int S_q, int S_k, int D,
+                        int block_size, int topk, int n_init, int n_local,
+                        float softmax_scale, void* stream);
+
+/*
+ * Block-sparse attention forward (news summary, Technical Mechanism:
+ * attention computed only on the selected key-value blocks; skill page,
+ * Step 2, sliding_attention, made causal and block-granular).
+ *   q        bf16  [B][H_q][S_q][D]
+ *   k, v     bf16  [B][H_kv][S_k][D]
+ *   blk_idx  int32 [B][H_kv][S_q][topk]   entries in [0, NB) or -1 (ignored);
+ *                                          duplicates and forced blocks are
+ *                                          allowed and counted once
+ *   out      bf16  [B][H_q][S_q][D]       (output)
+ *   lse      fp32  [B][H_q][S_q]          (optional output, natural log)
+ * Query position i attends keys t <= i of the blocks
+ *   {0..n_init-1} U {qb-n_local+1 .. qb} U {selected},  qb = floor(i/block_size).
+ * workspace: device memory of at least infv2_sparse_workspace_bytes(...)
+ * bytes, 256-byte aligned (holds a block-transposed copy of V and split
+ * partials); its contents on entry do not matter.
+ */
+size_t infv2_sparse_workspace_bytes(int B, int H_q, int H_kv, int S_q, int S_k,
+                                    int D, int block_size, int topk);
+int infv2_sparse_attn_fwd(const void* q, const void* k, const void* v,
+                          const int32_t* blk_idx, void* out, float* lse,
+                          int B, int H_q, int H_kv, int S_q, int S_k, int D,
+                          int block_size, int topk, int n_init, int n_local,
+                          float softmax_scale,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Dense attention forward (skill page, Step 1: Dense Attention Layer
+ * Foundation), GQA, causal (keys t <= i) or not (all S_k keys).
+ * Same tensor layouts as infv2_sparse_attn_fwd; workspace of at least
+ * infv2_dense_workspace_bytes(...) bytes, 256-byte aligned.
+ */
+size_t infv2_dense_workspace_bytes(int B, int H_q, int H_kv, int S_q, int S_k, int D);
+int infv2_dense_attn_fwd(const void* q, const void* k, const void* v,
+                         void* out, float* lse,
+                         int B, int H_q, int H_kv, int S_q, int S_k, int D,
+                         float softmax_scale, int causal,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The dense/sparse switch (skill page, Step 3: a sequence no longer than the
+ * threshold runs dense; paper page, Abstract: dense for short inputs, sparse
+ * for long ones).  Causal.  If S_k <= switch_len: infv2_dense_attn_fwd.
+ * Otherwise compress -> select -> sparse; k_cmp, blk_idx and the sparse
+ * workspace are carved from `workspace`.
+ * blk_idx_out (optional, may be NULL) receives the selection
+ * int32 [B][H_kv][S_q][topk] when the sparse path runs.
+ */
+size_t infv2_attn_workspace_bytes(int B, int H_q, int H_kv, int S_q, int S_k,
+                                  int D, int block_size, int topk, int switch_len);
+int infv2_attn_fwd(const void* q, const void* k, const void* v,
+                   void* out, float* lse, int32_t* blk_idx_out,
+                   int B, int H_q, int H_kv, int S_q, int S_k, int D,
+                   int block_size, int topk, int n_init, int n_local,
+                   float softmax_scale, int switch_len,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INFV2_H */

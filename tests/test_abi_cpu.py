@@ -1,0 +1,129 @@
+"""The C-ABI library loads, exports what include/infv2.h declares, and rejects
+bad arguments before touching the GPU (CPU only: no compute call here ever
+passes validation, so nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import trainable_block_sparse_mean_amd as tb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "infv2.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(tb.LIB_PATH), reason="libinfv2.so not built")
+
+FAKE = 0x10000      # aligned, non-null; only ever passed where validation fails first
+FAKE_MIS = 0x10004  # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(infv2_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for n in ["infv2_compress_k", "infv2_select_blocks", "infv2_sparse_attn_fwd", "infv2_dense_attn_fwd",
+              "infv2_attn_fwd", "infv2_status_string"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(tb.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert set(tb.SIGNATURES) == set(declared_functions())
+
+
+def test_status_strings_and_version():
+    lib = tb.load_library()
+    assert lib.infv2_abi_version() == 1
+    assert lib.infv2_status_string(0) == b"ok"
+    assert lib.infv2_status_string(3) == b"workspace missing or too small"
+    assert lib.infv2_status_string(99) == b"unknown status"
+
+
+def _sparse(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, idx=FAKE, out=FAKE, lse=None, B=1, H_q=32, H_kv=2, S_q=128, S_k=128,
+             D=128, bs=64, topk=4, n_init=1, n_local=2, scale=0.0, ws=FAKE, wsb=0, stream=None)
+    a.update(kw)
+    return lib.infv2_sparse_attn_fwd(a["q"], a["k"], a["v"], a["idx"], a["out"], a["lse"], a["B"], a["H_q"],
+                                     a["H_kv"], a["S_q"], a["S_k"], a["D"], a["bs"], a["topk"], a["n_init"],
+                                     a["n_local"], a["scale"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_sparse_validation_codes():
+    lib = tb.load_library()
+    assert _sparse(lib, H_q=31) == tb.ERR_INVALID              # H_q % H_kv
+    assert _sparse(lib, S_q=129) == tb.ERR_INVALID             # S_q > S_k
+    assert _sparse(lib, n_local=0) == tb.ERR_INVALID           # the diagonal block must be attended
+    assert _sparse(lib, n_init=-1) == tb.ERR_INVALID
+    assert _sparse(lib, topk=-1) == tb.ERR_INVALID
+    assert _sparse(lib, B=-1) == tb.ERR_INVALID
+    assert _sparse(lib, D=64) == tb.ERR_UNSUPPORTED
+    assert _sparse(lib, bs=32) == tb.ERR_UNSUPPORTED
+    assert _sparse(lib, topk=257) == tb.ERR_UNSUPPORTED
+    assert _sparse(lib, H_q=64, H_kv=2) == tb.ERR_UNSUPPORTED  # G = 32 > 16
+    assert _sparse(lib, q=None) == tb.ERR_INVALID
+    assert _sparse(lib, out=FAKE_MIS) == tb.ERR_INVALID
+    assert _sparse(lib, wsb=10) == tb.ERR_WORKSPACE            # too small
+    assert _sparse(lib, ws=None, wsb=1 << 30) == tb.ERR_WORKSPACE
+    # empty inputs are valid no-ops (return before any HIP call)
+    assert _sparse(lib, B=0) == tb.OK
+    assert _sparse(lib, S_q=0) == tb.OK
+
+
+def test_workspace_sizes():
+    lib = tb.load_library()
+    # block-transposed V: B * H_kv * NB * 64 * 128 * 2 bytes, rounded to 256
+    assert lib.infv2_sparse_workspace_bytes(1, 32, 2, 100, 1000, 128, 64, 8) == 2 * 16 * 64 * 128 * 2
+    assert lib.infv2_sparse_workspace_bytes(1, 32, 2, 100, 1000, 64, 64, 8) == 0   # unsupported -> 0
+    d = lib.infv2_dense_workspace_bytes(2, 8, 1, 64, 64, 128)
+    assert d == 2 * 1 * 1 * 64 * 128 * 2
+    dense = lib.infv2_attn_workspace_bytes(1, 32, 2, 4096, 4096, 128, 64, 16, 4096)
+    sparse = lib.infv2_attn_workspace_bytes(1, 32, 2, 4097, 4097, 128, 64, 16, 4096)
+    assert dense == lib.infv2_dense_workspace_bytes(1, 32, 2, 4096, 4096, 128)
+    assert sparse > lib.infv2_sparse_workspace_bytes(1, 32, 2, 4097, 4097, 128, 64, 16)
+
+
+def test_other_entry_points_validate():
+    lib = tb.load_library()
+    assert lib.infv2_compress_k(FAKE, FAKE, 1, 2, 100, 96, 64, None) == tb.ERR_UNSUPPORTED
+    assert lib.infv2_compress_k(FAKE, None, 1, 2, 100, 128, 64, None) == tb.ERR_INVALID
+    assert lib.infv2_compress_k(FAKE, FAKE, 1, 0, 100, 128, 64, None) == tb.ERR_INVALID
+    assert lib.infv2_compress_k(FAKE, FAKE, 0, 2, 100, 128, 64, None) == tb.OK
+    sel = lib.infv2_select_blocks
+    assert sel(FAKE, FAKE, FAKE, None, 1, 32, 2, 10, 200000, 128, 64, 8, 1, 2, 0.0, None) == tb.ERR_UNSUPPORTED
+    assert sel(FAKE, FAKE, FAKE, FAKE_MIS, 1, 32, 2, 10, 2000, 128, 64, 8, 1, 2, 0.0, None) == tb.ERR_INVALID
+    assert sel(FAKE, FAKE, None, None, 1, 32, 2, 10, 2000, 128, 64, 8, 1, 2, 0.0, None) == tb.ERR_INVALID
+    assert sel(FAKE, FAKE, FAKE, None, 1, 32, 2, 10, 2000, 128, 64, 8, 1, 0, 0.0, None) == tb.ERR_INVALID
+    dense = lib.infv2_dense_attn_fwd
+    assert dense(FAKE, FAKE, FAKE, FAKE, None, 1, 8, 1, 64, 64, 128, 0.0, 2, FAKE, 1 << 20, None) == tb.ERR_INVALID
+    assert dense(FAKE, FAKE, FAKE, FAKE, None, 1, 8, 1, 64, 64, 128, 0.0, 1, FAKE, 16, None) == tb.ERR_WORKSPACE
+    assert dense(FAKE, FAKE, FAKE, FAKE, None, 1, 8, 3, 64, 64, 128, 0.0, 1, FAKE, 1 << 20, None) == tb.ERR_INVALID
+    sw = lib.infv2_attn_fwd
+    # dense branch (S_k <= switch_len) and sparse branch both validate first
+    assert sw(FAKE, FAKE, FAKE, FAKE, None, None, 1, 32, 2, 64, 64, 128, 64, 4, 1, 2, 0.0, 64, FAKE, 8,
+              None) == tb.ERR_WORKSPACE
+    assert sw(FAKE, FAKE, FAKE, FAKE, None, None, 1, 32, 2, 128, 128, 128, 64, 4, 1, 2, 0.0, 64, FAKE, 8,
+              None) == tb.ERR_WORKSPACE
+    assert sw(FAKE, FAKE, FAKE, FAKE, None, None, 1, 32, 2, 128, 128, 128, 64, 4, 1, 0, 0.0, 64, FAKE, 1 << 30,
+              None) == tb.ERR_INVALID
+
+
+def test_binding_refuses_cpu_tensors():
+    q = torch.zeros(1, 2, 64, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        tb.compress_k(q)
+    with pytest.raises(ValueError, match="GPU"):
+        tb.dense_attn_fwd(q, q[:, :1].contiguous(), q[:, :1].contiguous())
+
+
+def test_binding_raises_when_library_missing(tmp_path, monkeypatch):
+    monkeypatch.setattr(tb, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        tb.load_library(str(tmp_path / "nope.so"))

@@ -1,0 +1,261 @@
+"""GPU (HIP, through the C ABI) vs the fp64 oracle, stage by stage.
+
+Stage isolation: each GPU stage is compared with the oracle run on the GPU's
+own output of the previous stage (select on the GPU's k_cmp, attention on
+the GPU's blk_idx), so a failure names its stage.  Inputs come from
+workloads.py (seeded).  Tolerances are in tests/parity.py.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.infv2_oracle as O
+import trainable_block_sparse_mean_amd as tb
+import workloads
+from tests.parity import assert_attn_close, check_selection, np64, sparse_rows_q
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_inputs(w):
+    x = workloads.make_inputs(w)
+    return {k: t.to(DEV) for k, t in x.items()}
+
+
+def bits_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+# ------------------------------------------------------------- compress ----
+
+@pytest.mark.parametrize("B,H,S,values", [(1, 2, 4096, "normal"), (2, 1, 1000, "normal"),
+                                          (1, 1, 512, "integer"), (1, 1, 63, "normal")])
+def test_compress_bit_exact(B, H, S, values):
+    w = workloads.TINY.with_(B=B, H_q=H, H_kv=H, S_q=S, S_k=S, values=values)
+    log("compress", w)
+    x = gpu_inputs(w)
+    kc = tb.compress_k(x["k"])
+    torch.cuda.synchronize()
+    ref_bits, _ = O.compress_k(np64(x["k"]), 64)
+    np.testing.assert_array_equal(bits_np(kc), ref_bits)
+
+
+# --------------------------------------------------------------- select ----
+
+SELECT_CASES = [
+    ("tiny_2k_g8", workloads.TINY, None),
+    ("switch_4k_g16", workloads.SWITCH_SPARSE.with_(S_q=4096, S_k=4096, switch_len=0), np.arange(0, 4096, 5)),
+    ("ragged_sq37_sk3000", workloads.TINY.with_(H_q=32, H_kv=2, S_q=37, S_k=3000, topk=9), None),
+    ("g4_topk40", workloads.TINY.with_(H_q=8, H_kv=2, S_q=1500, S_k=1500, topk=40, n_init=2, n_local=3), None),
+]
+
+
+@pytest.mark.parametrize("name,w,rows", SELECT_CASES, ids=[c[0] for c in SELECT_CASES])
+def test_select_matches_oracle(name, w, rows):
+    log("select", name, w)
+    x = gpu_inputs(w)
+    kc = tb.compress_k(x["k"])
+    idx, score = tb.select_blocks(x["q"], kc, w.S_k, w.topk, w.n_init, w.n_local, return_scores=True)
+    torch.cuda.synchronize()
+    rows = np.arange(w.S_q) if rows is None else rows
+    q64 = sparse_rows_q(x["q"], rows)
+    ref, scores = O.select_blocks(q64, np64(kc), w.S_k, w.topk, w.n_init, w.n_local, 64,
+                                  1 / math.sqrt(w.D), rows=rows, return_scores=True)
+    gidx = idx.cpu().numpy()[:, :, rows]
+    counts = check_selection(gidx, ref, scores, rows, w.S_q, w.S_k, w.topk, w.n_init, w.n_local)
+    log("  selection rows:", counts)
+    # the returned scores are the group scores of the kept blocks
+    gs = score.cpu().numpy()[:, :, rows]
+    for (b, g, r), sig in list(scores.items())[:: max(1, len(scores) // 200)]:
+        n = int(np.searchsorted(rows, r))
+        sel = gidx[b, g, n]
+        for e, j in enumerate(sel):
+            if j >= 0:
+                assert abs(gs[b, g, n, e] - sig[j]) <= 1e-4 * max(sig[j], 1e-3), (b, g, r, j)
+            else:
+                assert gs[b, g, n, e] == 0.0
+    assert counts["near_tie"] <= 0.02 * sum(counts.values())
+
+
+def test_select_all_ties_is_bit_exact():
+    w = workloads.TINY.with_(H_q=32, H_kv=2, S_q=2048, S_k=2048, topk=12, values="constant_k")
+    log("select ties", w)
+    x = gpu_inputs(w)
+    kc = tb.compress_k(x["k"])
+    idx = tb.select_blocks(x["q"], kc, w.S_k, w.topk, w.n_init, w.n_local).cpu().numpy()
+    for r in range(w.S_q):
+        cand = list(O.candidates(r, 64, w.n_init, w.n_local))
+        want = cand[: w.topk] + [-1] * (w.topk - min(w.topk, len(cand)))
+        assert list(idx[0, 0, r]) == want and list(idx[0, 1, r]) == want, r
+
+
+# ------------------------------------------------------ sparse attention ----
+
+SPARSE_CASES = [
+    ("tiny_2k_g8", workloads.TINY),
+    ("g16_4k_topk16", workloads.SWITCH_SPARSE.with_(S_q=4096, S_k=4096, values="normal")),
+    ("ragged_sq37_sk3000", workloads.TINY.with_(H_q=32, H_kv=2, S_q=37, S_k=3000, topk=9)),
+    ("ragged_sq1000_sk1000_b2", workloads.TINY.with_(B=2, H_q=6, H_kv=3, S_q=1000, S_k=1000, topk=5)),
+    ("topk0", workloads.TINY.with_(S_q=1024, S_k=1024, topk=0)),
+    ("g1", workloads.TINY.with_(H_q=2, H_kv=2, S_q=700, S_k=700, topk=3, n_init=0, n_local=1)),
+]
+
+
+@pytest.mark.parametrize("name,w", SPARSE_CASES, ids=[c[0] for c in SPARSE_CASES])
+def test_sparse_attention_matches_oracle(name, w):
+    log("sparse", name, w)
+    x = gpu_inputs(w)
+    kc = tb.compress_k(x["k"])
+    if w.topk > 0:
+        idx = tb.select_blocks(x["q"], kc, w.S_k, w.topk, w.n_init, w.n_local)
+    else:
+        idx = torch.empty(w.B, w.H_kv, w.S_q, 0, dtype=torch.int32, device=DEV)
+    out, lse = tb.sparse_attn_fwd(x["q"], x["k"], x["v"], idx, w.n_init, w.n_local)
+    torch.cuda.synchronize()
+    rows = np.arange(w.S_q) if w.S_q <= 2048 else np.arange(0, w.S_q, 3)
+    q64 = sparse_rows_q(x["q"], rows)
+    gidx = idx.cpu().numpy()[:, :, rows]
+    ro, rl = O.sparse_attn(q64, np64(x["k"]), np64(x["v"]), gidx, 64, w.n_init, w.n_local,
+                           1 / math.sqrt(w.D), rows=rows)
+    r = torch.as_tensor(rows, device=DEV)
+    stats = assert_attn_close(out[:, :, r], lse[:, :, r], ro, rl, name)
+    log("  ", stats)
+
+
+def test_sparse_attention_arbitrary_indices_duplicates_and_forced():
+    # selection rows that repeat blocks, name forced blocks and hold -1 gaps
+    w = workloads.TINY.with_(H_q=16, H_kv=1, S_q=900, S_k=900, topk=6)
+    log("sparse arbitrary idx", w)
+    x = gpu_inputs(w)
+    rng = np.random.default_rng(0)
+    idx = np.full((1, 1, w.S_q, w.topk), -1, dtype=np.int32)
+    for r in range(w.S_q):
+        qb = r // 64
+        picks = rng.integers(0, qb + 1, size=w.topk)
+        picks[rng.random(w.topk) < 0.3] = -1
+        idx[0, 0, r] = picks
+    out, lse = tb.sparse_attn_fwd(x["q"], x["k"], x["v"], torch.from_numpy(idx).to(DEV), w.n_init, w.n_local)
+    torch.cuda.synchronize()
+    ro, rl = O.sparse_attn(np64(x["q"]), np64(x["k"]), np64(x["v"]), idx, 64, w.n_init, w.n_local,
+                           1 / math.sqrt(128))
+    assert_attn_close(out, lse, ro, rl, "arbitrary idx")
+
+
+def test_sparse_equals_dense_when_topk_covers_every_block():
+    w = workloads.TINY.with_(H_q=32, H_kv=2, S_q=1536, S_k=1536, topk=24)
+    log("sparse == dense", w)
+    x = gpu_inputs(w)
+    kc = tb.compress_k(x["k"])
+    idx = tb.select_blocks(x["q"], kc, w.S_k, w.topk, w.n_init, w.n_local)
+    so, sl = tb.sparse_attn_fwd(x["q"], x["k"], x["v"], idx, w.n_init, w.n_local)
+    do, dl = tb.dense_attn_fwd(x["q"], x["k"], x["v"], causal=True)
+    torch.cuda.synchronize()
+    # same blocks, same order, same kernel arithmetic: identical bits
+    assert torch.equal(so, do)
+    assert torch.equal(sl, dl)
+
+
+def test_value_probe_structure():
+    # V[t] = one-hot(block(t)): output column j of a head is its attention mass on block j
+    w = workloads.TINY.with_(H_q=16, H_kv=1, S_q=4096, S_k=4096, topk=8)
+    log("value probe", w)
+    x = gpu_inputs(w)
+    v = torch.zeros(1, 1, w.S_k, 128)
+    v[0, 0, torch.arange(w.S_k), torch.arange(w.S_k) // 64] = 1.0
+    v = v.to(torch.bfloat16).to(DEV)
+    kc = tb.compress_k(x["k"])
+    idx = tb.select_blocks(x["q"], kc, w.S_k, w.topk, w.n_init, w.n_local)
+    out, _ = tb.sparse_attn_fwd(x["q"], x["k"], v, idx, w.n_init, w.n_local)
+    o = np64(out)[0]
+    gi = idx.cpu().numpy()[0, 0]
+    for r in range(0, w.S_q, 7):
+        qb = r // 64
+        want = {0, qb, max(qb - 1, 0)} | {int(j) for j in gi[r] if j >= 0}
+        for h in range(16):
+            got = set(np.nonzero(o[h, r] > 0)[0].tolist())
+            assert got == want, (r, h, sorted(got ^ want))
+
+
+# ------------------------------------------------------- dense attention ----
+
+DENSE_CASES = [
+    ("causal_g16_2k", workloads.TINY.with_(H_q=32, H_kv=2, S_q=2048, S_k=2048), True),
+    ("causal_g8_ragged_1000", workloads.TINY.with_(S_q=1000, S_k=1000), True),
+    ("bottom_right_sq100_sk1000", workloads.TINY.with_(H_q=16, H_kv=1, S_q=100, S_k=1000), True),
+    ("noncausal_sq77_sk300", workloads.TINY.with_(H_q=4, H_kv=2, S_q=77, S_k=300), False),
+    ("decode_b4", workloads.TINY.with_(B=4, H_q=32, H_kv=2, S_q=1, S_k=2000), True),
+]
+
+
+@pytest.mark.parametrize("name,w,causal", DENSE_CASES, ids=[c[0] for c in DENSE_CASES])
+def test_dense_attention_matches_oracle(name, w, causal):
+    log("dense", name, w)
+    x = gpu_inputs(w)
+    out, lse = tb.dense_attn_fwd(x["q"], x["k"], x["v"], causal=causal)
+    torch.cuda.synchronize()
+    rows = np.arange(w.S_q) if w.S_q <= 1024 else np.arange(0, w.S_q, 4)
+    ro, rl = O.dense_attn(sparse_rows_q(x["q"], rows), np64(x["k"]), np64(x["v"]), 1 / math.sqrt(128),
+                          causal=causal, rows=rows)
+    r = torch.as_tensor(rows, device=DEV)
+    log("  ", assert_attn_close(out[:, :, r], lse[:, :, r], ro, rl, name))
+
+
+# -------------------------------------------------------------- switch ----
+
+@pytest.mark.parametrize("w", [workloads.SWITCH_DENSE, workloads.SWITCH_SPARSE], ids=lambda w: w.name)
+def test_switch_and_planted_blocks(w):
+    log("switch", w)
+    x = gpu_inputs(w)
+    res = tb.attn_fwd(x["q"], x["k"], x["v"], 64, w.topk, w.n_init, w.n_local, w.switch_len, return_idx=True)
+    torch.cuda.synchronize()
+    assert res["path"] == ("dense" if w.S_k <= w.switch_len else "sparse")
+    rows = np.arange(0, w.S_q, 61)
+    q64 = sparse_rows_q(x["q"], rows)
+    ref = O.attention(q64, np64(x["k"]), np64(x["v"]), 64, w.topk, w.n_init, w.n_local, w.switch_len,
+                      rows=rows)
+    assert ref["path"] == res["path"]
+    r = torch.as_tensor(rows, device=DEV)
+    if res["path"] == "sparse":
+        gidx = res["blk_idx"].cpu().numpy()
+        # every token of a planted chunk selects the planted block
+        plan = workloads.planted_targets(w)
+        for (b, g, c), p in plan.items():
+            for rr in (c * 64, c * 64 + 63):
+                assert p in set(gidx[b, g, rr].tolist()), (g, c, p)
+        # attention parity on the GPU's own selection
+        ro, rl = O.sparse_attn(q64, np64(x["k"]), np64(x["v"]), gidx[:, :, rows], 64, w.n_init, w.n_local,
+                               1 / math.sqrt(128), rows=rows)
+        log("  ", assert_attn_close(res["out"][:, :, r], res["lse"][:, :, r], ro, rl, w.name))
+    else:
+        log("  ", assert_attn_close(res["out"][:, :, r], res["lse"][:, :, r], ref["out"], ref["lse"], w.name))
+
+
+def test_switch_boundary_exactly_at_threshold():
+    w = workloads.TINY.with_(H_q=32, H_kv=2, S_q=1024, S_k=1024, topk=4)
+    x = gpu_inputs(w)
+    a = tb.attn_fwd(x["q"], x["k"], x["v"], 64, 4, 1, 2, switch_len=1024)
+    d, _ = tb.dense_attn_fwd(x["q"], x["k"], x["v"])
+    b = tb.attn_fwd(x["q"], x["k"], x["v"], 64, 4, 1, 2, switch_len=1023)
+    torch.cuda.synchronize()
+    assert a["path"] == "dense" and torch.equal(a["out"], d)
+    assert b["path"] == "sparse" and not torch.equal(b["out"], d)
+
+
+def test_determinism_bitwise():
+    w = workloads.TINY.with_(H_q=32, H_kv=2, S_q=3000, S_k=3000, topk=16)
+    x = gpu_inputs(w)
+    r1 = tb.attn_fwd(x["q"], x["k"], x["v"], 64, w.topk, 1, 2, 0, return_idx=True)
+    r2 = tb.attn_fwd(x["q"], x["k"], x["v"], 64, w.topk, 1, 2, 0, return_idx=True)
+    torch.cuda.synchronize()
+    assert torch.equal(r1["blk_idx"], r2["blk_idx"])
+    assert torch.equal(r1["out"], r2["out"]) and torch.equal(r1["lse"], r2["lse"])

@@ -1,0 +1,200 @@
+"""InfLLM-V2 block-sparse attention for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libinfv2.so`` (include/infv2.h).
+Every function only checks and marshals arguments: all work runs in the HIP
+kernels, enqueued on torch's current stream.  There is no CPU fallback: the
+functions raise if the library has not been built or the tensors are not on
+the GPU.
+
+Names follow the C entry points without their ``infv2_`` prefix:
+``compress_k``, ``select_blocks``, ``sparse_attn_fwd``, ``dense_attn_fwd``,
+``attn_fwd``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libinfv2.so")
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+
+_c_int, _c_size, _c_float, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
+
+# name -> (restype, argtypes), mirroring include/infv2.h
+SIGNATURES = {
+    "infv2_status_string": (ctypes.c_char_p, [_c_int]),
+    "infv2_abi_version": (_c_int, []),
+    "infv2_compress_k": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
+    "infv2_select_blocks": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 10 + [_c_float, _vp]),
+    "infv2_sparse_workspace_bytes": (_c_size, [_c_int] * 8),
+    "infv2_sparse_attn_fwd": (_c_int, [_vp] * 6 + [_c_int] * 10 + [_c_float, _vp, _c_size, _vp]),
+    "infv2_dense_workspace_bytes": (_c_size, [_c_int] * 6),
+    "infv2_dense_attn_fwd": (_c_int, [_vp] * 5 + [_c_int] * 6 + [_c_float, _c_int, _vp, _c_size, _vp]),
+    "infv2_attn_workspace_bytes": (_c_size, [_c_int] * 9),
+    "infv2_attn_fwd": (_c_int, [_vp] * 6 + [_c_int] * 10 + [_c_float, _c_int, _vp, _c_size, _vp]),
+}
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libinfv2.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m trainable_block_sparse_mean_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+class Infv2Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = load_library().infv2_status_string(status).decode()
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+        self.status = status
+
+
+def _call(name: str, *args):
+    st = getattr(load_library(), name)(*args)
+    if st != OK:
+        raise Infv2Error(name, st)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device}); there is no CPU path")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
+
+
+def _scale(softmax_scale):
+    return 0.0 if softmax_scale is None else float(softmax_scale)
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def compress_k(k: torch.Tensor, block_size: int = 64) -> torch.Tensor:
+    """Per-block key means, bf16 [B, H_kv, ceil(S_k/block_size), D]."""
+    _need(k, "k", torch.bfloat16, 4)
+    B, H_kv, S_k, D = k.shape
+    nb = (S_k + block_size - 1) // block_size
+    k_cmp = torch.empty(B, H_kv, nb, D, dtype=torch.bfloat16, device=k.device)
+    _call("infv2_compress_k", _ptr(k), _ptr(k_cmp), B, H_kv, S_k, D, block_size, _stream())
+    return k_cmp
+
+
+def select_blocks(q: torch.Tensor, k_cmp: torch.Tensor, S_k: int, topk: int, n_init: int = 1,
+                  n_local: int = 2, softmax_scale=None, block_size: int = 64, return_scores: bool = False):
+    """Top-k blocks per (batch, KV group, query row): int32 [B, H_kv, S_q, topk],
+    ascending, -1 padded; optionally also the group scores of those blocks."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k_cmp, "k_cmp", torch.bfloat16, 4)
+    B, H_q, S_q, D = q.shape
+    H_kv = k_cmp.shape[1]
+    idx = torch.empty(B, H_kv, S_q, topk, dtype=torch.int32, device=q.device)
+    score = torch.empty_like(idx, dtype=torch.float32) if return_scores else None
+    _call("infv2_select_blocks", _ptr(q), _ptr(k_cmp), _ptr(idx), _ptr(score), B, H_q, H_kv, S_q, S_k, D,
+          block_size, topk, n_init, n_local, _scale(softmax_scale), _stream())
+    return (idx, score) if return_scores else idx
+
+
+def sparse_attn_fwd(q, k, v, blk_idx, n_init: int = 1, n_local: int = 2, softmax_scale=None,
+                    block_size: int = 64, return_lse: bool = True):
+    """Attention over the initial, sliding-window and selected blocks.
+    Returns (out bf16 [B,H_q,S_q,D], lse fp32 [B,H_q,S_q] or None)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, 4)
+    _need(blk_idx, "blk_idx", torch.int32, 4)
+    B, H_q, S_q, D = q.shape
+    H_kv, S_k = k.shape[1], k.shape[2]
+    topk = blk_idx.shape[3]
+    out = torch.empty_like(q)
+    lse = torch.empty(B, H_q, S_q, dtype=torch.float32, device=q.device) if return_lse else None
+    nbytes = load_library().infv2_sparse_workspace_bytes(B, H_q, H_kv, S_q, S_k, D, block_size, topk)
+    ws = _workspace(nbytes, q.device)
+    _call("infv2_sparse_attn_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(blk_idx), _ptr(out), _ptr(lse),
+          B, H_q, H_kv, S_q, S_k, D, block_size, topk, n_init, n_local, _scale(softmax_scale),
+          _ptr(ws), ws.numel(), _stream())
+    return out, lse
+
+
+def dense_attn_fwd(q, k, v, causal: bool = True, softmax_scale=None, return_lse: bool = True):
+    """Dense (causal) GQA attention.  Returns (out, lse or None)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, 4)
+    B, H_q, S_q, D = q.shape
+    H_kv, S_k = k.shape[1], k.shape[2]
+    out = torch.empty_like(q)
+    lse = torch.empty(B, H_q, S_q, dtype=torch.float32, device=q.device) if return_lse else None
+    ws = _workspace(load_library().infv2_dense_workspace_bytes(B, H_q, H_kv, S_q, S_k, D), q.device)
+    _call("infv2_dense_attn_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H_q, H_kv, S_q, S_k, D,
+          _scale(softmax_scale), int(bool(causal)), _ptr(ws), ws.numel(), _stream())
+    return out, lse
+
+
+class AttnPlan:
+    """Pre-sized buffers for repeated ``attn_fwd`` calls on one shape."""
+
+    def __init__(self, B, H_q, H_kv, S_q, S_k, D=128, block_size=64, topk=64, n_init=1, n_local=2,
+                 switch_len=0, softmax_scale=None, device="cuda", with_lse=True, with_idx=False):
+        self.args = (B, H_q, H_kv, S_q, S_k, D, block_size, topk, n_init, n_local)
+        self.switch_len = switch_len
+        self.scale = _scale(softmax_scale)
+        self.dense = S_k <= switch_len
+        nbytes = load_library().infv2_attn_workspace_bytes(B, H_q, H_kv, S_q, S_k, D, block_size, topk,
+                                                           switch_len)
+        self.ws = _workspace(nbytes, device)
+        self.out = torch.empty(B, H_q, S_q, D, dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty(B, H_q, S_q, dtype=torch.float32, device=device) if with_lse else None
+        self.idx = (torch.empty(B, H_kv, S_q, topk, dtype=torch.int32, device=device)
+                    if with_idx and not self.dense else None)
+
+    def run(self, q, k, v):
+        B, H_q, H_kv, S_q, S_k, D, bs, topk, n_init, n_local = self.args
+        _call("infv2_attn_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(self.out), _ptr(self.lse), _ptr(self.idx),
+              B, H_q, H_kv, S_q, S_k, D, bs, topk, n_init, n_local, self.scale, self.switch_len,
+              _ptr(self.ws), self.ws.numel(), _stream())
+        return self.out, self.lse
+
+
+def attn_fwd(q, k, v, block_size: int = 64, topk: int = 64, n_init: int = 1, n_local: int = 2,
+             switch_len: int = 0, softmax_scale=None, return_idx: bool = False):
+    """The dense/sparse switch: dense causal attention if S_k <= switch_len,
+    else compress -> select -> sparse.  Returns dict(out, lse, path, blk_idx)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, 4)
+    B, H_q, S_q, D = q.shape
+    H_kv, S_k = k.shape[1], k.shape[2]
+    plan = AttnPlan(B, H_q, H_kv, S_q, S_k, D, block_size, topk, n_init, n_local, switch_len, softmax_scale,
+                    q.device, True, return_idx)
+    out, lse = plan.run(q, k, v)
+    return dict(out=out, lse=lse, path="dense" if plan.dense else "sparse", blk_idx=plan.idx)
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)

@@ -1,0 +1,220 @@
+// C ABI of the InfLLM-V2 sparse attention path (declared in include/infv2.h):
+// argument validation, workspace sizing and kernel dispatch.  Every check runs
+// before the first HIP call, so an invalid call launches nothing.
+#include <math.h>
+
+#include "infv2.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using infv2::AttnShape;
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int kMaxTopk = 256;
+constexpr int kMaxSelectBlocks = 2048;  // select keeps each token's scores in LDS
+constexpr int kMaxSparseBlocks = 8192;  // sparse keeps a per-block member mask in LDS
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int num_blocks(int S_k, int block_size) { return (S_k + block_size - 1) / block_size; }
+
+// shape checks shared by every attention-type entry point
+int check_shape(int B, int H_q, int H_kv, int S_q, int S_k, int D) {
+  if (B < 0 || H_q < 1 || H_kv < 1 || S_q < 0 || S_k < 0 || D < 1) return INFV2_ERR_INVALID;
+  if (H_q % H_kv != 0 || S_q > S_k) return INFV2_ERR_INVALID;
+  if (D != infv2::kD) return INFV2_ERR_UNSUPPORTED;
+  if (H_q / H_kv > infv2::kMaxG) return INFV2_ERR_UNSUPPORTED;
+  // element offsets are computed in 64 bits; keep sequence indices in int range
+  if (static_cast<long long>(S_k) * D >= (1LL << 31)) return INFV2_ERR_UNSUPPORTED;
+  return INFV2_OK;
+}
+
+int check_sparse_params(int block_size, int topk, int n_init, int n_local) {
+  if (block_size < 1 || topk < 0 || n_init < 0 || n_local < 1) return INFV2_ERR_INVALID;
+  if (block_size != infv2::kBS || topk > kMaxTopk) return INFV2_ERR_UNSUPPORTED;
+  return INFV2_OK;
+}
+
+bool tensor_ok(const void* p) { return p != nullptr && aligned(p, 16); }
+
+float scale_log2(float softmax_scale, int D) {
+  const float sc = softmax_scale > 0.f ? softmax_scale : 1.f / sqrtf(static_cast<float>(D));
+  return sc * infv2::kLog2e;
+}
+
+AttnShape make_shape(int B, int H_q, int H_kv, int S_q, int S_k, int block_size, int topk,
+                     int n_init, int n_local, float sl2, int causal) {
+  AttnShape s;
+  s.B = B;
+  s.H_q = H_q;
+  s.H_kv = H_kv;
+  s.S_q = S_q;
+  s.S_k = S_k;
+  s.G = H_q / H_kv;
+  s.NB = num_blocks(S_k, block_size);
+  s.topk = topk;
+  s.n_init = n_init;
+  s.n_local = n_local;
+  s.scale_log2 = sl2;
+  s.causal = causal;
+  return s;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? INFV2_OK : INFV2_ERR_HIP; }
+
+size_t sparse_ws(int B, int H_q, int H_kv, int S_q, int S_k, int block_size, int topk) {
+  const AttnShape s = make_shape(B, H_q, H_kv, S_q, S_k, block_size, topk, 0, 1, 1.f, 1);
+  return round_up(infv2::attn_workspace_bytes(s), 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* infv2_status_string(int status) {
+  switch (status) {
+    case INFV2_OK: return "ok";
+    case INFV2_ERR_INVALID: return "invalid argument";
+    case INFV2_ERR_UNSUPPORTED: return "unsupported configuration";
+    case INFV2_ERR_WORKSPACE: return "workspace missing or too small";
+    case INFV2_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int infv2_abi_version(void) { return kAbiVersion; }
+
+int infv2_compress_k(const void* k, void* k_cmp, int B, int H_kv, int S_k, int D, int block_size,
+                     void* stream) {
+  if (B < 0 || H_kv < 1 || S_k < 0 || D < 1 || block_size < 1) return INFV2_ERR_INVALID;
+  if (D != infv2::kD || block_size != infv2::kBS) return INFV2_ERR_UNSUPPORTED;
+  if (static_cast<long long>(S_k) * D >= (1LL << 31)) return INFV2_ERR_UNSUPPORTED;
+  if (B == 0 || S_k == 0) return INFV2_OK;
+  if (!tensor_ok(k) || !tensor_ok(k_cmp)) return INFV2_ERR_INVALID;
+  return hip_status(infv2::launch_compress_k(static_cast<const uint16_t*>(k), static_cast<uint16_t*>(k_cmp),
+                                             B, H_kv, S_k, static_cast<hipStream_t>(stream)));
+}
+
+int infv2_select_blocks(const void* q, const void* k_cmp, int32_t* blk_idx, float* blk_score, int B,
+                        int H_q, int H_kv, int S_q, int S_k, int D, int block_size, int topk,
+                        int n_init, int n_local, float softmax_scale, void* stream) {
+  int st = check_shape(B, H_q, H_kv, S_q, S_k, D);
+  if (st != INFV2_OK) return st;
+  st = check_sparse_params(block_size, topk, n_init, n_local);
+  if (st != INFV2_OK) return st;
+  if (num_blocks(S_k, block_size) > kMaxSelectBlocks) return INFV2_ERR_UNSUPPORTED;
+  if (B == 0 || S_q == 0 || topk == 0) return INFV2_OK;
+  if (!tensor_ok(q) || !tensor_ok(k_cmp) || !tensor_ok(blk_idx)) return INFV2_ERR_INVALID;
+  if (blk_score && !aligned(blk_score, 16)) return INFV2_ERR_INVALID;
+  const AttnShape s = make_shape(B, H_q, H_kv, S_q, S_k, block_size, topk, n_init, n_local,
+                                 scale_log2(softmax_scale, D), 1);
+  return hip_status(infv2::launch_select_blocks(static_cast<const uint16_t*>(q),
+                                                static_cast<const uint16_t*>(k_cmp), blk_idx, blk_score,
+                                                s, static_cast<hipStream_t>(stream)));
+}
+
+size_t infv2_sparse_workspace_bytes(int B, int H_q, int H_kv, int S_q, int S_k, int D, int block_size,
+                                    int topk) {
+  if (check_shape(B, H_q, H_kv, S_q, S_k, D) != INFV2_OK || block_size != infv2::kBS || topk < 0) return 0;
+  return sparse_ws(B, H_q, H_kv, S_q, S_k, block_size, topk);
+}
+
+int infv2_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* blk_idx, void* out,
+                          float* lse, int B, int H_q, int H_kv, int S_q, int S_k, int D, int block_size,
+                          int topk, int n_init, int n_local, float softmax_scale, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int st = check_shape(B, H_q, H_kv, S_q, S_k, D);
+  if (st != INFV2_OK) return st;
+  st = check_sparse_params(block_size, topk, n_init, n_local);
+  if (st != INFV2_OK) return st;
+  if (num_blocks(S_k, block_size) > kMaxSparseBlocks) return INFV2_ERR_UNSUPPORTED;
+  if (B == 0 || S_q == 0) return INFV2_OK;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(out)) return INFV2_ERR_INVALID;
+  if (topk > 0 && !tensor_ok(blk_idx)) return INFV2_ERR_INVALID;
+  if (lse && !aligned(lse, 16)) return INFV2_ERR_INVALID;
+  const size_t need = sparse_ws(B, H_q, H_kv, S_q, S_k, block_size, topk);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return INFV2_ERR_WORKSPACE;
+  if (workspace && !aligned(workspace, 256)) return INFV2_ERR_INVALID;
+  const AttnShape s = make_shape(B, H_q, H_kv, S_q, S_k, block_size, topk, n_init, n_local,
+                                 scale_log2(softmax_scale, D), 1);
+  return hip_status(infv2::launch_sparse_attn(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+      blk_idx, static_cast<uint16_t*>(out), lse, s, workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t infv2_dense_workspace_bytes(int B, int H_q, int H_kv, int S_q, int S_k, int D) {
+  if (check_shape(B, H_q, H_kv, S_q, S_k, D) != INFV2_OK) return 0;
+  return sparse_ws(B, H_q, H_kv, S_q, S_k, infv2::kBS, 0);
+}
+
+int infv2_dense_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                         int H_q, int H_kv, int S_q, int S_k, int D, float softmax_scale, int causal,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_shape(B, H_q, H_kv, S_q, S_k, D);
+  if (st != INFV2_OK) return st;
+  if (causal != 0 && causal != 1) return INFV2_ERR_INVALID;
+  if (B == 0 || S_q == 0) return INFV2_OK;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(out)) return INFV2_ERR_INVALID;
+  if (lse && !aligned(lse, 16)) return INFV2_ERR_INVALID;
+  const size_t need = sparse_ws(B, H_q, H_kv, S_q, S_k, infv2::kBS, 0);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return INFV2_ERR_WORKSPACE;
+  if (workspace && !aligned(workspace, 256)) return INFV2_ERR_INVALID;
+  const AttnShape s = make_shape(B, H_q, H_kv, S_q, S_k, infv2::kBS, 0, 0, 1,
+                                 scale_log2(softmax_scale, D), causal);
+  return hip_status(infv2::launch_dense_attn(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                             static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse,
+                                             s, workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t infv2_attn_workspace_bytes(int B, int H_q, int H_kv, int S_q, int S_k, int D, int block_size, int topk,
+                                  int switch_len) {
+  if (check_shape(B, H_q, H_kv, S_q, S_k, D) != INFV2_OK || block_size != infv2::kBS || topk < 0) return 0;
+  if (S_k <= switch_len) return infv2_dense_workspace_bytes(B, H_q, H_kv, S_q, S_k, D);
+  const size_t kc = round_up(static_cast<size_t>(B) * H_kv * num_blocks(S_k, block_size) * D * 2, 256);
+  const size_t idx = round_up(static_cast<size_t>(B) * H_kv * S_q * topk * 4, 256);
+  return kc + idx + sparse_ws(B, H_q, H_kv, S_q, S_k, block_size, topk);
+}
+
+int infv2_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int32_t* blk_idx_out,
+                   int B, int H_q, int H_kv, int S_q, int S_k, int D, int block_size, int topk, int n_init,
+                   int n_local, float softmax_scale, int switch_len, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  if (S_k <= switch_len)
+    return infv2_dense_attn_fwd(q, k, v, out, lse, B, H_q, H_kv, S_q, S_k, D, softmax_scale, 1, workspace,
+                                workspace_bytes, stream);
+  int st = check_shape(B, H_q, H_kv, S_q, S_k, D);
+  if (st != INFV2_OK) return st;
+  st = check_sparse_params(block_size, topk, n_init, n_local);
+  if (st != INFV2_OK) return st;
+  if (num_blocks(S_k, block_size) > kMaxSelectBlocks) return INFV2_ERR_UNSUPPORTED;
+  if (B == 0 || S_q == 0) return INFV2_OK;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(out)) return INFV2_ERR_INVALID;
+  if (lse && !aligned(lse, 16)) return INFV2_ERR_INVALID;
+  if (blk_idx_out && !aligned(blk_idx_out, 16)) return INFV2_ERR_INVALID;
+  const size_t need = infv2_attn_workspace_bytes(B, H_q, H_kv, S_q, S_k, D, block_size, topk, switch_len);
+  if (workspace == nullptr || workspace_bytes < need) return INFV2_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return INFV2_ERR_INVALID;
+
+  char* ws = static_cast<char*>(workspace);
+  const size_t kc_bytes = round_up(static_cast<size_t>(B) * H_kv * num_blocks(S_k, block_size) * D * 2, 256);
+  const size_t idx_bytes = round_up(static_cast<size_t>(B) * H_kv * S_q * topk * 4, 256);
+  void* k_cmp = ws;
+  int32_t* idx = blk_idx_out ? blk_idx_out : reinterpret_cast<int32_t*>(ws + kc_bytes);
+  void* rest = ws + kc_bytes + idx_bytes;
+  const size_t rest_bytes = workspace_bytes - kc_bytes - idx_bytes;
+
+  st = infv2_compress_k(k, k_cmp, B, H_kv, S_k, D, block_size, stream);
+  if (st != INFV2_OK) return st;
+  if (topk > 0) {
+    st = infv2_select_blocks(q, k_cmp, idx, nullptr, B, H_q, H_kv, S_q, S_k, D, block_size, topk, n_init,
+                             n_local, softmax_scale, stream);
+    if (st != INFV2_OK) return st;
+  }
+  return infv2_sparse_attn_fwd(q, k, v, idx, out, lse, B, H_q, H_kv, S_q, S_k, D, block_size, topk, n_init,
+                               n_local, softmax_scale, rest, rest_bytes, stream);
+}
+
+}  // extern "C"

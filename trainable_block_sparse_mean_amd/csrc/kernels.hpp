@@ -1,0 +1,36 @@
+// Internal launch functions of the gfx950 kernels (called by api.hip after
+// argument validation).  Shapes here are already checked: D = 128,
+// block size 64, 1 <= G <= 16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace infv2 {
+
+struct AttnShape {
+  int B, H_q, H_kv, S_q, S_k, G, NB;
+  int topk, n_init, n_local;
+  float scale_log2;  // softmax scale * log2(e)
+  int causal;
+};
+
+hipError_t launch_compress_k(const uint16_t* k, uint16_t* k_cmp, int B, int H_kv, int S_k,
+                             hipStream_t stream);
+
+hipError_t launch_select_blocks(const uint16_t* q, const uint16_t* k_cmp, int32_t* blk_idx,
+                                float* blk_score, const AttnShape& s, hipStream_t stream);
+
+// bytes of workspace the attention kernels need (V relayout + split partials)
+size_t attn_workspace_bytes(const AttnShape& s);
+
+hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const int32_t* blk_idx, uint16_t* out, float* lse,
+                              const AttnShape& s, void* workspace, hipStream_t stream);
+
+hipError_t launch_dense_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             uint16_t* out, float* lse, const AttnShape& s, void* workspace,
+                             hipStream_t stream);
+
+}  // namespace infv2
