@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const uint16_t* __r
   // ---- per-token state (this wave's T tokens) -------------------------------
   bf16x8 qf[T][4];
   floatx4 o[T][8];
-  float m[T], l[T];
+  float m[T], l[T], lr[T];  // l: this lane's fp32 row sum, lr: of the bf16-rounded P
   int ipos[T];
   uint32_t valid_mask = 0;
 #pragma unroll
@@ -156,6 +156,7 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const uint16_t* __r
     for (int dt = 0; dt < 8; ++dt) o[t][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
     m[t] = -INFINITY;
     l[t] = 0.f;
+    lr[t] = 0.f;
   }
 
   // ---- stream the blocks -----------------------------------------------------
@@ -200,7 +201,11 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const uint16_t* __r
       }
     }
 
-    // online softmax (log2 domain); P rounded to bf16, row sums of the rounded P
+    // online softmax (log2 domain).  P is rounded to bf16 for the PV product.
+    // Row sums stay per lane (each lane holds 16 of a head's 64 keys) and are
+    // reduced across the four lanes of a head once, after the last block: l
+    // sums the fp32 P (for the log-sum-exp), lr the rounded P (O is divided
+    // by lr, so its weights are exactly those the MFMA applied).
     bf16x8 pf[T][2];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -223,16 +228,16 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const uint16_t* __r
       const float mn = fmaxf(m[t], mx);
       const float alpha = exp2f(m[t] - mn);  // m = -inf on the first block: 0
       uint32_t pw[8];
-      float rs = 0.f;
+      float rs = 0.f, rsr = 0.f;
 #pragma unroll
       for (int c2 = 0; c2 < 8; ++c2) {
         const float p0 = exp2f(z[2 * c2] - mn), p1 = exp2f(z[2 * c2 + 1] - mn);
         pw[c2] = pack_bf16x2(p0, p1);
-        rs += bf16_lo(pw[c2]) + bf16_hi(pw[c2]);
+        rs += p0 + p1;
+        rsr += bf16_lo(pw[c2]) + bf16_hi(pw[c2]);
       }
-      rs += shfl_xor(rs, 16);
-      rs += shfl_xor(rs, 32);
       l[t] = l[t] * alpha + rs;
+      lr[t] = lr[t] * alpha + rsr;
       m[t] = mn;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) o[t][dt] *= alpha;
@@ -257,10 +262,17 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const uint16_t* __r
   // ---- epilogue ---------------------------------------------------------------
 #pragma unroll
   for (int t = 0; t < T; ++t) {
+    l[t] += shfl_xor(l[t], 16);
+    l[t] += shfl_xor(l[t], 32);
+    lr[t] += shfl_xor(lr[t], 16);
+    lr[t] += shfl_xor(lr[t], 32);
+  }
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
     if (!(valid_mask >> t & 1u) || hl >= s.G) continue;
     const int r = r0 + wave * T + t;
     const int h = g * s.G + hl;
-    const float inv = 1.f / l[t];
+    const float inv = 1.f / lr[t];
     uint16_t* orow = out + (static_cast<size_t>(b * s.H_q + h) * s.S_q + r) * kD + 4 * gq;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
