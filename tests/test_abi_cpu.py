@@ -18,6 +18,10 @@ pytestmark = pytest.mark.skipif(not os.path.exists(tb.LIB_PATH), reason="libinfv
 FAKE = 0x10000      # aligned, non-null; only ever passed where validation fails first
 FAKE_MIS = 0x10004  # misaligned
 
+# calls with fake pointers must never reach a kernel; as a second guard they
+# only run where no GPU is visible
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="fake-pointer validation tests run GPU-less only")
+
 
 def declared_functions():
     text = open(HEADER).read()
@@ -56,6 +60,7 @@ def _sparse(lib, **kw):
                                      a["n_local"], a["scale"], a["ws"], a["wsb"], a["stream"])
 
 
+@no_gpu
 def test_sparse_validation_codes():
     lib = tb.load_library()
     assert _sparse(lib, H_q=31) == tb.ERR_INVALID              # H_q % H_kv
@@ -70,8 +75,6 @@ def test_sparse_validation_codes():
     assert _sparse(lib, H_q=64, H_kv=2) == tb.ERR_UNSUPPORTED  # G = 32 > 16
     assert _sparse(lib, q=None) == tb.ERR_INVALID
     assert _sparse(lib, out=FAKE_MIS) == tb.ERR_INVALID
-    assert _sparse(lib, wsb=10) == tb.ERR_WORKSPACE            # too small
-    assert _sparse(lib, ws=None, wsb=1 << 30) == tb.ERR_WORKSPACE
     # empty inputs are valid no-ops (return before any HIP call)
     assert _sparse(lib, B=0) == tb.OK
     assert _sparse(lib, S_q=0) == tb.OK
@@ -79,17 +82,19 @@ def test_sparse_validation_codes():
 
 def test_workspace_sizes():
     lib = tb.load_library()
-    # block-transposed V: B * H_kv * NB * 64 * 128 * 2 bytes, rounded to 256
-    assert lib.infv2_sparse_workspace_bytes(1, 32, 2, 100, 1000, 128, 64, 8) == 2 * 16 * 64 * 128 * 2
-    assert lib.infv2_sparse_workspace_bytes(1, 32, 2, 100, 1000, 64, 64, 8) == 0   # unsupported -> 0
-    d = lib.infv2_dense_workspace_bytes(2, 8, 1, 64, 64, 128)
-    assert d == 2 * 1 * 1 * 64 * 128 * 2
+    # prefill attention needs no workspace; the switch carves k_cmp and blk_idx
+    assert lib.infv2_sparse_workspace_bytes(1, 32, 2, 100, 1000, 128, 64, 8) == 0
+    assert lib.infv2_dense_workspace_bytes(2, 8, 1, 64, 64, 128) == 0
     dense = lib.infv2_attn_workspace_bytes(1, 32, 2, 4096, 4096, 128, 64, 16, 4096)
     sparse = lib.infv2_attn_workspace_bytes(1, 32, 2, 4097, 4097, 128, 64, 16, 4096)
     assert dense == lib.infv2_dense_workspace_bytes(1, 32, 2, 4096, 4096, 128)
-    assert sparse > lib.infv2_sparse_workspace_bytes(1, 32, 2, 4097, 4097, 128, 64, 16)
+    kc = 2 * 65 * 128 * 2                       # bf16 [1][2][ceil(4097/64)][128]
+    idx = 2 * 4097 * 16 * 4                     # int32 [1][2][4097][16]
+    rnd = lambda x: (x + 255) // 256 * 256
+    assert sparse == rnd(kc) + rnd(idx) + lib.infv2_sparse_workspace_bytes(1, 32, 2, 4097, 4097, 128, 64, 16)
 
 
+@no_gpu
 def test_other_entry_points_validate():
     lib = tb.load_library()
     assert lib.infv2_compress_k(FAKE, FAKE, 1, 2, 100, 96, 64, None) == tb.ERR_UNSUPPORTED
@@ -103,12 +108,13 @@ def test_other_entry_points_validate():
     assert sel(FAKE, FAKE, FAKE, None, 1, 32, 2, 10, 2000, 128, 64, 8, 1, 0, 0.0, None) == tb.ERR_INVALID
     dense = lib.infv2_dense_attn_fwd
     assert dense(FAKE, FAKE, FAKE, FAKE, None, 1, 8, 1, 64, 64, 128, 0.0, 2, FAKE, 1 << 20, None) == tb.ERR_INVALID
-    assert dense(FAKE, FAKE, FAKE, FAKE, None, 1, 8, 1, 64, 64, 128, 0.0, 1, FAKE, 16, None) == tb.ERR_WORKSPACE
+    assert dense(FAKE, FAKE, None, FAKE, None, 1, 8, 1, 64, 64, 128, 0.0, 1, FAKE, 16, None) == tb.ERR_INVALID
+    assert dense(FAKE, FAKE, FAKE, FAKE, FAKE_MIS, 1, 8, 1, 64, 64, 128, 0.0, 1, FAKE, 16, None) == tb.ERR_INVALID
     assert dense(FAKE, FAKE, FAKE, FAKE, None, 1, 8, 3, 64, 64, 128, 0.0, 1, FAKE, 1 << 20, None) == tb.ERR_INVALID
     sw = lib.infv2_attn_fwd
     # dense branch (S_k <= switch_len) and sparse branch both validate first
-    assert sw(FAKE, FAKE, FAKE, FAKE, None, None, 1, 32, 2, 64, 64, 128, 64, 4, 1, 2, 0.0, 64, FAKE, 8,
-              None) == tb.ERR_WORKSPACE
+    assert sw(FAKE, FAKE, FAKE, None, None, None, 1, 32, 2, 64, 64, 128, 64, 4, 1, 2, 0.0, 64, FAKE, 8,
+              None) == tb.ERR_INVALID
     assert sw(FAKE, FAKE, FAKE, FAKE, None, None, 1, 32, 2, 128, 128, 128, 64, 4, 1, 2, 0.0, 64, FAKE, 8,
               None) == tb.ERR_WORKSPACE
     assert sw(FAKE, FAKE, FAKE, FAKE, None, None, 1, 32, 2, 128, 128, 128, 64, 4, 1, 0, 0.0, 64, FAKE, 1 << 30,

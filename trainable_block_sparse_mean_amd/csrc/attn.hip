@@ -21,66 +21,69 @@
 //   * S^T (keys x heads) leaves every lane with one head and four keys, so
 //     the online softmax needs only two cross-lane steps per row, and its
 //     output is already the B operand of V^T P^T once the 32 keys of a
-//     k-step are taken in the order the lanes hold them.  V is relaid out
-//     once per call into that block-transposed, key-permuted order so the
-//     V^T fragment of a lane is one 16-byte LDS read.
+//     k-step are taken in the order the lanes hold them.  The matching V^T
+//     operand is read straight from V's natural [key][dim] rows with the
+//     gfx950 transposing LDS read (ds_read_b64_tr_b16: each 16-lane group
+//     turns a 4-key x 16-dim tile into one 4-key column per lane).
+//   * K and V blocks go global -> LDS with asynchronous direct-to-LDS loads
+//     (global_load_lds_dwordx4) into a double buffer, so the next block is in
+//     flight while the current one is multiplied.  LDS rows are 256 bytes with
+//     their 16-byte chunks XOR-swizzled by row, which keeps both the 16-row
+//     K reads and the 8-row transposing V reads free of bank conflicts.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace infv2 {
 
 constexpr int kWaves = 4;
-constexpr int kKPitch = kD * 2 + 16;   // bytes per K row in LDS (pad: conflict-free 16-row reads)
-constexpr int kVPitch = kBS * 2 + 16;  // bytes per V^T row in LDS
-constexpr int kKBytes = kBS * kKPitch;
-constexpr int kVBytes = kD * kVPitch;
+constexpr int kRowBytes = kD * 2;                 // one K or V row in LDS
+constexpr int kTileBytes = kBS * kRowBytes;       // one 64-key block of K (or V)
+constexpr int kStageBytes = 2 * kTileBytes;       // K + V of one block
+constexpr int kStages = 2;
 
-// Key held in position p (0..63) of a relaid V^T row: within each 32-key
-// group, lane quad gq's eight slots are keys 4gq..4gq+3 and 16+4gq..16+4gq+3.
-__host__ __device__ constexpr int vt_key_of_pos(int p) {
-  return 32 * (p >> 5) + (((p & 7) < 4) ? (4 * ((p & 31) >> 3) + (p & 7))
-                                        : (16 + 4 * ((p & 31) >> 3) + (p & 7) - 4));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// 16-byte chunk slot of chunk c in LDS row r: c ^ swz(r).  Any 16 consecutive
+// rows get 16 distinct slots (conflict-free 16-lane K reads); any 8 rows of an
+// aligned group of 8 get distinct 32-byte pairs (conflict-free V reads).
+__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
-// vt[bg][blk][d][p] = v[bg][blk*64 + vt_key_of_pos(p)][d] (0 beyond S_k)
-__global__ __launch_bounds__(256) void v_relayout_kernel(const uint16_t* __restrict__ v,
-                                                         uint16_t* __restrict__ vt, int S_k, int NB) {
-  __shared__ __align__(16) uint16_t tile[kBS][kD + 8];
-  const int blk = blockIdx.x;
-  const size_t bg = blockIdx.y;
-  const int nvalid = min(kBS, S_k - blk * kBS);
-  for (int c = threadIdx.x; c < kBS * kD / 8; c += 256) {
-    const int key = c >> 4, col = (c & 15) * 8;
-    const u32x4 val = key < nvalid ? load16(v + (bg * S_k + static_cast<size_t>(blk) * kBS + key) * kD + col)
-                                   : u32x4{0u, 0u, 0u, 0u};
-    store16(&tile[key][col], val);
-  }
-  __syncthreads();
-  for (int c = threadIdx.x; c < kBS * kD / 8; c += 256) {
-    const int d = c >> 3, pc = c & 7;
-    uint32_t w[4];
+// Issue the direct-to-LDS loads of key block j (rows clamped to S_k - 1; the
+// clamped keys are masked, and they hold finite data) into one stage buffer.
+// Each wave moves 4 K and 4 V chunks of 4 rows (1 KB = 64 lanes x 16 B).
+__device__ __forceinline__ void stage_block(unsigned char* stage, const uint16_t* kg, const uint16_t* vg,
+                                            int j, int S_k, int wave, int lane) {
+  const int sub = lane >> 4;    // row within the 4-row chunk
+  const int slot = lane & 15;   // LDS chunk slot this lane fills
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int k0 = vt_key_of_pos(pc * 8 + 2 * e), k1 = vt_key_of_pos(pc * 8 + 2 * e + 1);
-      w[e] = static_cast<uint32_t>(tile[k0][d]) | (static_cast<uint32_t>(tile[k1][d]) << 16);
-    }
-    store16(vt + ((bg * NB + blk) * kD + d) * kBS + pc * 8, u32x4{w[0], w[1], w[2], w[3]});
+  for (int n = 0; n < 4; ++n) {
+    const int cc = wave * 4 + n;            // 4-row chunk 0..15
+    const int row = cc * 4 + sub;
+    const int grow = min(j * kBS + row, S_k - 1);
+    const size_t off = static_cast<size_t>(grow) * kD + (slot ^ swz(row)) * 8;
+    __builtin_amdgcn_global_load_lds((global_void*)(kg + off), (lds_void*)(stage + cc * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((global_void*)(vg + off), (lds_void*)(stage + kTileBytes + cc * 1024), 16, 0, 0);
   }
 }
 
 template <int T, bool DENSE>
 __global__ __launch_bounds__(256, 1) void attn_window_kernel(const uint16_t* __restrict__ q,
                                                              const uint16_t* __restrict__ k,
-                                                             const uint16_t* __restrict__ vt,
+                                                             const uint16_t* __restrict__ v,
                                                              const int32_t* __restrict__ blk_idx,
                                                              uint16_t* __restrict__ out,
                                                              float* __restrict__ lse, AttnShape s) {
   constexpr int W = kWaves * T;
-  extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* kbuf = smem;
-  unsigned char* vbuf = smem + kKBytes;
-  uint32_t* bmask = reinterpret_cast<uint32_t*>(smem + kKBytes + kVBytes);  // [NB], sparse only
-  int* blist = reinterpret_cast<int*>(bmask + s.NB);                        // [NB], sparse only
+  extern __shared__ __align__(1024) unsigned char smem[];
+  uint32_t* bmask = reinterpret_cast<uint32_t*>(smem + kStages * kStageBytes);  // [NB], sparse only
+  int* blist = reinterpret_cast<int*>(bmask + s.NB);                           // [NB], sparse only
   __shared__ int n_list;
 
   const int wave = threadIdx.x >> 6;
@@ -96,6 +99,8 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const uint16_t* __r
   const int off = s.S_k - s.S_q;
   const int i_last = off + min(r0 + W, s.S_q) - 1;
   const int qb_last = i_last / kBS;
+  const uint16_t* kg = k + bg * s.S_k * kD;
+  const uint16_t* vg = v + bg * s.S_k * kD;
 
   // ---- the union of attended blocks ---------------------------------------
   int nblk;
@@ -135,6 +140,9 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const uint16_t* __r
     nblk = n_list;
   }
 
+  // first block in flight while the queries load
+  if (nblk > 0) stage_block(smem, kg, vg, DENSE ? 0 : blist[0], s.S_k, wave, lane);
+
   // ---- per-token state (this wave's T tokens) -------------------------------
   bf16x8 qf[T][4];
   floatx4 o[T][8];
@@ -161,6 +169,11 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const uint16_t* __r
 
   // ---- stream the blocks -----------------------------------------------------
   for (int e = 0; e < nblk; ++e) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // block e is in LDS; every wave is done with block e - 1
+    if (e + 1 < nblk)
+      stage_block(smem + ((e + 1) & 1) * kStageBytes, kg, vg, DENSE ? e + 1 : blist[e + 1], s.S_k, wave, lane);
+
     const int j = DENSE ? e : blist[e];
     uint32_t wm;
     if constexpr (DENSE) {
@@ -171,18 +184,9 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const uint16_t* __r
     } else {
       wm = (bmask[j] >> (wave * T)) & ((1u << T) - 1u);
     }
-
-    __syncthreads();  // every wave is done with the previous block
-    for (int c = threadIdx.x; c < kBS * kD / 8; c += 256) {
-      const int row = c >> 4, col = c & 15;
-      const int kpos = j * kBS + row;
-      const u32x4 kv = kpos < s.S_k ? load16(k + (bg * s.S_k + kpos) * kD + col * 8) : u32x4{0u, 0u, 0u, 0u};
-      store16(kbuf + row * kKPitch + col * 16, kv);
-      const int d = c >> 3, pc = c & 7;
-      store16(vbuf + d * kVPitch + pc * 16, load16(vt + ((bg * s.NB + j) * kD + d) * kBS + pc * 8));
-    }
-    __syncthreads();
     if (wm == 0u) continue;
+    const unsigned char* kbuf = smem + (e & 1) * kStageBytes;
+    const unsigned char* vbuf = kbuf + kTileBytes;
 
     // S^T[key][head] = K Q^T for every member token
     floatx4 sacc[T][4];
@@ -192,9 +196,10 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const uint16_t* __r
       for (int kt = 0; kt < 4; ++kt) sacc[t][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
+      const int row = 16 * kt + hl;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = as_bf16x8(load16(kbuf + (16 * kt + hl) * kKPitch + ks * 64 + gq * 16));
+        const bf16x8 a = as_bf16x8(load16(kbuf + row * kRowBytes + (((ks * 4 + gq) ^ swz(row)) << 4)));
 #pragma unroll
         for (int t = 0; t < T; ++t)
           if (wm >> t & 1u) sacc[t][kt] = mfma_16x16x32(a, qf[t][ks], sacc[t][kt]);
@@ -226,12 +231,13 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const uint16_t* __r
       mx = fmaxf(mx, shfl_xor(mx, 16));
       mx = fmaxf(mx, shfl_xor(mx, 32));
       const float mn = fmaxf(m[t], mx);
-      const float alpha = exp2f(m[t] - mn);  // m = -inf on the first block: 0
+      const float alpha = __builtin_amdgcn_exp2f(m[t] - mn);  // m = -inf on the first block: 0
       uint32_t pw[8];
       float rs = 0.f, rsr = 0.f;
 #pragma unroll
       for (int c2 = 0; c2 < 8; ++c2) {
-        const float p0 = exp2f(z[2 * c2] - mn), p1 = exp2f(z[2 * c2 + 1] - mn);
+        const float p0 = __builtin_amdgcn_exp2f(z[2 * c2] - mn);
+        const float p1 = __builtin_amdgcn_exp2f(z[2 * c2 + 1] - mn);
         pw[c2] = pack_bf16x2(p0, p1);
         rs += p0 + p1;
         rsr += bf16_lo(pw[c2]) + bf16_hi(pw[c2]);
@@ -246,12 +252,21 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const uint16_t* __r
       pf[t][1] = as_bf16x8(u32x4{pw[4], pw[5], pw[6], pw[7]});
     }
 
-    // O^T[dim][head] += V^T P^T
+    // O^T[dim][head] += V^T P^T; the V^T operand of lane (hl, gq) for k-step
+    // s2 is keys 32*s2 + 4*gq + {0..3} and 32*s2 + 16 + 4*gq + {0..3} of dim
+    // 16*dt + hl: two transposing reads of 4-key x 16-dim tiles
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8 a = as_bf16x8(load16(vbuf + (16 * dt + hl) * kVPitch + s2 * 64 + gq * 16));
+        bf16x4 half[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int row = 32 * s2 + 16 * hh + 4 * gq + (hl >> 2);
+          const int chunk = 2 * dt + ((hl & 3) >> 1);
+          half[hh] = lds_read_tr(vbuf + row * kRowBytes + ((chunk ^ swz(row)) << 4) + ((hl & 1) << 3));
+        }
+        const bf16x8 a = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int t = 0; t < T; ++t)
           if (wm >> t & 1u) o[t][dt] = mfma_16x16x32(a, pf[t][s2], o[t][dt]);
@@ -286,43 +301,30 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const uint16_t* __r
 
 constexpr int kTokPerWave = 4;
 
-size_t attn_workspace_bytes(const AttnShape& s) {
-  return static_cast<size_t>(s.B) * s.H_kv * s.NB * kBS * kD * sizeof(uint16_t);
-}
+size_t attn_workspace_bytes(const AttnShape&) { return 0; }
 
-static hipError_t launch_relayout(const uint16_t* v, uint16_t* vt, const AttnShape& s, hipStream_t stream) {
-  hipLaunchKernelGGL(v_relayout_kernel, dim3(s.NB, s.B * s.H_kv), dim3(256), 0, stream, v, vt, s.S_k, s.NB);
+template <bool DENSE>
+static hipError_t launch_window(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* blk_idx,
+                                uint16_t* out, float* lse, const AttnShape& s, hipStream_t stream) {
+  constexpr int W = kWaves * kTokPerWave;
+  const dim3 grid((s.S_q + W - 1) / W, s.B * s.H_kv);
+  const size_t lds = kStages * kStageBytes + (DENSE ? 0 : 2 * sizeof(int) * static_cast<size_t>(s.NB));
+  hipLaunchKernelGGL((attn_window_kernel<kTokPerWave, DENSE>), grid, dim3(256), lds, stream, q, k, v, blk_idx,
+                     out, lse, s);
   return hipGetLastError();
 }
 
 hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               const int32_t* blk_idx, uint16_t* out, float* lse,
-                              const AttnShape& s, void* workspace, hipStream_t stream) {
+                              const AttnShape& s, void*, hipStream_t stream) {
   if (s.B == 0 || s.S_q == 0) return hipSuccess;
-  uint16_t* vt = static_cast<uint16_t*>(workspace);
-  hipError_t err = launch_relayout(v, vt, s, stream);
-  if (err != hipSuccess) return err;
-  constexpr int W = kWaves * kTokPerWave;
-  const dim3 grid((s.S_q + W - 1) / W, s.B * s.H_kv);
-  const size_t lds = kKBytes + kVBytes + 2 * sizeof(int) * static_cast<size_t>(s.NB);
-  hipLaunchKernelGGL((attn_window_kernel<kTokPerWave, false>), grid, dim3(256), lds, stream, q, k, vt,
-                     blk_idx, out, lse, s);
-  return hipGetLastError();
+  return launch_window<false>(q, k, v, blk_idx, out, lse, s, stream);
 }
 
 hipError_t launch_dense_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                             uint16_t* out, float* lse, const AttnShape& s, void* workspace,
-                             hipStream_t stream) {
+                             uint16_t* out, float* lse, const AttnShape& s, void*, hipStream_t stream) {
   if (s.B == 0 || s.S_q == 0) return hipSuccess;
-  uint16_t* vt = static_cast<uint16_t*>(workspace);
-  hipError_t err = launch_relayout(v, vt, s, stream);
-  if (err != hipSuccess) return err;
-  constexpr int W = kWaves * kTokPerWave;
-  const dim3 grid((s.S_q + W - 1) / W, s.B * s.H_kv);
-  const size_t lds = kKBytes + kVBytes;
-  hipLaunchKernelGGL((attn_window_kernel<kTokPerWave, true>), grid, dim3(256), lds, stream, q, k, vt,
-                     nullptr, out, lse, s);
-  return hipGetLastError();
+  return launch_window<true>(q, k, v, nullptr, out, lse, s, stream);
 }
 
 }  // namespace infv2
