@@ -1,0 +1,259 @@
+"""Benchmark of the InfLLM-V2 sparse attention forward path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = the whole sparse path on one batch resident in HBM: key
+compression -> group-summed block selection + top-k -> block-sparse attention
+(the dense/sparse switch entry point with the sequence above the switch
+length).  Default workload: long prefill, batch 1, 32768 tokens, 32 query /
+2 KV heads, head dim 128, block 64, top-64 + 1 initial + 2 sliding blocks.
+
+Prints ONE JSON line.  `value` is the effective attention throughput of the
+step: algorithmic attention FLOPs (4*D per query head and attended key) per
+second.  Per-stage times come from HIP events on the stream the kernels run
+on.  `roofline` describes the dominant kernel (the block-sparse attention);
+`cpu_baseline` times the fp64 oracle on a bounded sample of query rows.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_fwd_long_prefill_32k_traffic.json")
+ATTN_SOURCES = [os.path.join(ROOT, "trainable_block_sparse_mean_amd", "csrc", f)
+                for f in ("attn.hip", "common.hpp", "kernels.hpp")]
+
+
+def attended_keys(S_q, S_k, bs, topk, n_init, n_local):
+    """Keys attended by each query row (closed form of the attended set)."""
+    import numpy as np
+    i = (S_k - S_q) + np.arange(S_q, dtype=np.int64)
+    qb = i // bs
+    diag = i - bs * qb + 1
+    init = np.minimum(n_init, qb)                      # initial blocks below qb
+    win_lo = np.maximum(qb - n_local + 1, 0)           # window blocks below qb: win_lo .. qb-1
+    win = qb - win_lo
+    overlap = np.maximum(0, np.minimum(init, qb) - win_lo)   # initial blocks inside the window
+    n_cand = np.maximum(0, qb - n_local - n_init + 1)
+    sel = np.minimum(topk, n_cand)
+    return diag + bs * (init + win - overlap + sel)
+
+
+def flop_counts(w):
+    import numpy as np
+    keys = attended_keys(w.S_q, w.S_k, w.block_size, w.topk, w.n_init, w.n_local)
+    sparse = 4.0 * w.D * w.H_q * w.B * float(keys.sum())
+    i = (w.S_k - w.S_q) + np.arange(w.S_q, dtype=np.int64)
+    dense = 4.0 * w.D * w.H_q * w.B * float((i + 1).sum())
+    select = 2 * 2.0 * w.D * w.H_q * w.B * float(((i + 1) // w.block_size).sum())
+    return sparse, dense, select, keys
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for p in ATTN_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when the kernel sources changed since the counters were taken."""
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256") != source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, target_s=15.0):
+    """The fp64 oracle, as it is, on a bounded sample of query rows."""
+    import numpy as np
+    import oracle.infv2_oracle as O
+    try:
+        import threadpoolctl
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    q, k, v = (x[n] for n in ("q", "k", "v"))
+    t0 = time.perf_counter()
+    k64 = k.double().numpy()
+    v64 = v.double().numpy()
+    _, kc = O.compress_k(k64, w.block_size)
+    t_compress = time.perf_counter() - t0
+    scale = 1 / math.sqrt(w.D)
+    keys = attended_keys(w.S_q, w.S_k, w.block_size, w.topk, w.n_init, w.n_local)
+    done_rows, flops, t_rows = 0, 0.0, 0.0
+    n = 8
+    rng = np.random.default_rng(0)
+    while t_rows < target_s:
+        rows = np.sort(rng.choice(w.S_q, size=n, replace=False))
+        q64 = np.zeros((w.B, w.H_q, w.S_q, w.D))
+        q64[:, :, rows, :] = q[:, :, rows, :].double().numpy()
+        t1 = time.perf_counter()
+        idx = O.select_blocks(q64, kc, w.S_k, w.topk, w.n_init, w.n_local, w.block_size, scale, rows=rows)
+        O.sparse_attn(q64, k64, v64, idx, w.block_size, w.n_init, w.n_local, scale, rows=rows)
+        t_rows += time.perf_counter() - t1
+        done_rows += n
+        flops += 4.0 * w.D * w.H_q * w.B * float(keys[rows].sum())
+        n = min(2 * n, 512)
+    # whole-step estimate: compression once + the per-row cost of every row
+    total_rows = w.S_q
+    step_s = t_compress + t_rows * total_rows / done_rows
+    sparse_flops = 4.0 * w.D * w.H_q * w.B * float(keys.sum())
+    return dict(value=sparse_flops / step_s / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+                sample=(f"{done_rows} random query rows (both KV groups) of {w.name}: select + attend "
+                        f"timed {t_rows:.1f} s, plus full key compression {t_compress:.2f} s; "
+                        f"scaled to all {total_rows} rows"),
+                step_s_estimate=step_s)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_prefill_32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--profile-attn", type=int, default=0,
+                    help="only launch the sparse attention kernel this many times (for counter runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import trainable_block_sparse_mean_amd as tb
+    import workloads
+
+    wl = {w.name: w for w in workloads.ALL}[args.workload]
+    wl = wl.with_(switch_len=0) if wl.S_k > wl.switch_len else wl
+    dev = torch.device("cuda:0")
+    x = workloads.make_inputs(wl)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    torch.cuda.synchronize()
+    sparse_flops, dense_flops, select_flops, _ = flop_counts(wl)
+
+    if args.profile_attn:
+        kc = tb.compress_k(k)
+        idx = tb.select_blocks(q, kc, wl.S_k, wl.topk, wl.n_init, wl.n_local)
+        # a plain copy of known size, to calibrate the HBM byte counters
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        bcopy = torch.empty_like(a)
+        bcopy.copy_(a)
+        for _ in range(args.profile_attn):
+            tb.sparse_attn_fwd(q, k, v, idx, wl.n_init, wl.n_local)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_attn_launches": args.profile_attn, "copy_bytes": 2 * a.numel()}))
+        return
+
+    plan = tb.AttnPlan(wl.B, wl.H_q, wl.H_kv, wl.S_q, wl.S_k, wl.D, wl.block_size, wl.topk, wl.n_init,
+                       wl.n_local, wl.switch_len, None, dev)
+    for _ in range(args.warmup):
+        plan.run(q, k, v)
+    torch.cuda.synchronize()
+
+    # ---- timed steps: the whole path, back to back -------------------------------
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        plan.run(q, k, v)
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # ---- per stage, HIP events around each entry point (one kernel each) --------
+    stages = {"compress": 0.0, "select": 0.0, "sparse_attn": 0.0}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    reps = max(3, args.steps)
+    for _ in range(reps):
+        ev[0].record()
+        kc = tb.compress_k(k)
+        ev[1].record()
+        idx = tb.select_blocks(q, kc, wl.S_k, wl.topk, wl.n_init, wl.n_local)
+        ev[2].record()
+        tb.sparse_attn_fwd(q, k, v, idx, wl.n_init, wl.n_local)
+        ev[3].record()
+        torch.cuda.synchronize()
+        stages["compress"] += ev[0].elapsed_time(ev[1]) / reps
+        stages["select"] += ev[1].elapsed_time(ev[2]) / reps
+        stages["sparse_attn"] += ev[2].elapsed_time(ev[3]) / reps
+
+    dense_ms = None
+    if not args.no_dense:
+        tb.dense_attn_fwd(q, k, v, causal=True)
+        torch.cuda.synchronize()
+        dreps = 3
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record()
+        for _ in range(dreps):
+            tb.dense_attn_fwd(q, k, v, causal=True)
+        d1.record()
+        torch.cuda.synchronize()
+        dense_ms = d0.elapsed_time(d1) / dreps
+
+    attn_tflops = sparse_flops / (stages["sparse_attn"] * 1e-3) / 1e12
+    value = sparse_flops / (ms_step * 1e-3) / 1e12
+    traffic = stored_traffic()
+    roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(wl, x)
+        cpu = {kk: cb[kk] for kk in ("value", "unit", "cores", "kind", "sample")}
+        cpu["value"] = round(cpu["value"], 6)
+
+    out = {
+        "metric": "sparse-attn fwd ms & effective TFLOP/s at 32k; speedup vs dense; % MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "S_q": wl.S_q, "S_k": wl.S_k, "H_q": wl.H_q,
+                   "H_kv": wl.H_kv, "D": wl.D, "block_size": wl.block_size, "topk": wl.topk,
+                   "n_init": wl.n_init, "n_local": wl.n_local, "values": wl.values,
+                   "parallelism": "none (1 GPU)"},
+        "stage_ms": {kk: round(vv, 4) for kk, vv in stages.items()},
+        "sparse_attn_ms": round(stages["sparse_attn"], 4),
+        "sparse_attn_tflops": round(attn_tflops, 2),
+        "mfma_peak_frac_attn": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "mfma_peak_frac_step": round(value / PEAK_BF16_TFLOPS, 4),
+        "dense_attn_ms": None if dense_ms is None else round(dense_ms, 4),
+        "dense_attn_tflops": None if dense_ms is None else round(dense_flops / (dense_ms * 1e-3) / 1e12, 2),
+        "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms_step, 3),
+        "algorithmic_flops": {"sparse_attn": sparse_flops, "dense_attn": dense_flops, "select": select_flops},
+        "wall_ms_per_step": round(wall_ms, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

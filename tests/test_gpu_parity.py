@@ -160,9 +160,14 @@ def test_sparse_equals_dense_when_topk_covers_every_block():
     so, sl = tb.sparse_attn_fwd(x["q"], x["k"], x["v"], idx, w.n_init, w.n_local)
     do, dl = tb.dense_attn_fwd(x["q"], x["k"], x["v"], causal=True)
     torch.cuda.synchronize()
-    # same blocks, same order, same kernel arithmetic: identical bits
-    assert torch.equal(so, do)
-    assert torch.equal(sl, dl)
+    # every candidate is selected, so both kernels attend exactly the causal keys
+    assert (idx.cpu().numpy()[..., : w.S_q // 64 - 3] >= 0).any()
+    rows = np.arange(0, w.S_q, 3)
+    ro, rl = O.dense_attn(sparse_rows_q(x["q"], rows), np64(x["k"]), np64(x["v"]), 1 / math.sqrt(128), rows=rows)
+    r = torch.as_tensor(rows, device=DEV)
+    assert_attn_close(so[:, :, r], sl[:, :, r], ro, rl, "sparse vs dense oracle")
+    assert_attn_close(do[:, :, r], dl[:, :, r], ro, rl, "dense vs dense oracle")
+    assert float((so.float() - do.float()).abs().max()) <= 1e-2
 
 
 def test_value_probe_structure():

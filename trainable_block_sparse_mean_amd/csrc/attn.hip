@@ -7,80 +7,345 @@
 // Use).  Dense: skill page, Step 1 (softmax of scaled products, weighted sum
 // of values).
 //
-// Work unit: one workgroup = one KV group of one batch entry x a window of
-// W consecutive query tokens; 4 waves, each owning T tokens.  For every
-// token, the 16 query heads of the group are the N = 16 columns of a
-// 16x16x32 bf16 MFMA, so no GQA head ever re-reads K/V on its own.
+// Work unit: one workgroup = one KV head of one batch entry x a window of
+// W = 16 consecutive query tokens; 8 waves (two per SIMD, so one wave's
+// matrix instructions overlap the other's softmax), each owning 2 tokens.
+// The G <= 16 query heads of the KV head share every K/V byte.
 //   * The workgroup builds the union of the blocks its tokens attend (a
 //     per-block bitmask of member tokens in LDS, compacted to an ascending
-//     list), and streams each block of the union once through LDS.
-//   * Each wave reads a block's K / V fragments from LDS once and applies
-//     them to each of its tokens that attends the block (S^T = K Q^T, then
-//     O^T += V^T P^T), so the LDS read of a fragment is shared by the member
-//     tokens of the wave.
-//   * S^T (keys x heads) leaves every lane with one head and four keys, so
-//     the online softmax needs only two cross-lane steps per row, and its
-//     output is already the B operand of V^T P^T once the 32 keys of a
-//     k-step are taken in the order the lanes hold them.  The matching V^T
-//     operand is read straight from V's natural [key][dim] rows with the
-//     gfx950 transposing LDS read (ds_read_b64_tr_b16: each 16-lane group
-//     turns a 4-key x 16-dim tile into one 4-key column per lane).
+//     list) and streams each block of the union once through LDS.
 //   * K and V blocks go global -> LDS with asynchronous direct-to-LDS loads
-//     (global_load_lds_dwordx4) into a double buffer, so the next block is in
-//     flight while the current one is multiplied.  LDS rows are 256 bytes with
-//     their 16-byte chunks XOR-swizzled by row, which keeps both the 16-row
-//     K reads and the 8-row transposing V reads free of bank conflicts.
+//     (global_load_lds_dwordx4) into a 4-stage ring, three blocks ahead of
+//     the one being multiplied.  LDS rows are 256 bytes whose 16-byte chunks
+//     are permuted by a 4-bit bit reversal of the row, which keeps every
+//     fragment read pattern below free of bank conflicts.
+//   * Scores are computed transposed, S^T = K Q^T (keys x heads): each lane
+//     then owns one head and a few keys, the row max needs only cross-lane
+//     swaps (v_permlane{16,32}_swap), and the softmax output is already the
+//     B operand of O^T += V^T P^T once the keys of a k-step are taken in the
+//     order the lanes hold them.  The matching V^T operand comes straight
+//     from V's natural [key][dim] rows through the transposing LDS read
+//     ds_read_b64_tr_b16 (each 16-lane group turns a 4-key x 16-dim tile into
+//     one 4-key column per lane).
+//   * Sparse: one token per MFMA column block (16x16x32 bf16, N = 16 heads),
+//     so a token that does not attend a block costs nothing.  Dense: every
+//     token attends every earlier block, so the two tokens of a wave share a
+//     32x32x16 bf16 MFMA (N = 2 tokens x 16 heads), the full-rate shape.
+//   * Online softmax in log2 units; the running max only moves when a block
+//     max exceeds it by more than 2^8, so the O rescale is rare.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace infv2 {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
+constexpr int kTokPerWave = 2;
+constexpr int kWin = kWaves * kTokPerWave;        // tokens per workgroup
 constexpr int kRowBytes = kD * 2;                 // one K or V row in LDS
 constexpr int kTileBytes = kBS * kRowBytes;       // one 64-key block of K (or V)
 constexpr int kStageBytes = 2 * kTileBytes;       // K + V of one block
-constexpr int kStages = 2;
+constexpr int kStages = 4;                        // LDS ring: 3 blocks in flight
+constexpr int kDmaPerBlock = 4;                   // direct-to-LDS loads per wave per block
+constexpr int kXcds = 8;                          // workgroups are dealt round-robin to 8 XCDs
+constexpr int kXcdGroup = 32;                     // windows kept together on one XCD (one per CU)
+constexpr float kRescaleSlack = 8.f;              // log2 units the running max may lag behind
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void global_void;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-// 16-byte chunk slot of chunk c in LDS row r: c ^ swz(r).  Any 16 consecutive
-// rows get 16 distinct slots (conflict-free 16-lane K reads); any 8 rows of an
-// aligned group of 8 get distinct 32-byte pairs (conflict-free V reads).
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// Slot of 16-byte chunk c in LDS row r: c ^ swz(r), swz = 4-bit bit reversal
+// of r.  16 aligned rows get 16 distinct slots (16-lane K reads), 8 aligned
+// rows distinct 32-byte pairs and 4 aligned rows distinct 64-byte quads
+// (transposing V reads of the 16x16 and 32x32 layouts).
+__device__ __forceinline__ int swz(int r) {
+  return ((r & 1) << 3) | ((r & 2) << 1) | ((r & 4) >> 1) | ((r & 8) >> 3);
+}
 
 __device__ __forceinline__ bf16x4 lds_read_tr(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
-// Issue the direct-to-LDS loads of key block j (rows clamped to S_k - 1; the
-// clamped keys are masked, and they hold finite data) into one stage buffer.
-// Each wave moves 4 K and 4 V chunks of 4 rows (1 KB = 64 lanes x 16 B).
-__device__ __forceinline__ void stage_block(unsigned char* stage, const uint16_t* kg, const uint16_t* vg,
+__device__ __forceinline__ floatx16 mfma_32x32x16(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
+}
+
+// reductions over lanes l, l^16 (the two rows of a row pair) and l, l^32
+// (the two wave halves): v_permlane{16,32}_swap of a value with itself
+// returns both partners' values
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One direct-to-LDS load: 64 lanes x 16 bytes land contiguously at LDS byte
+// address `lds` (M0).  Issued from asm so the compiler does not serialise the
+// later LDS reads behind it; completion is awaited explicitly (wait_dma) before
+// the workgroup barrier that publishes the block.  No output registers.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(gptr) : "memory", "m0");
+}
+
+// Wait until at most `in_flight` later blocks' loads of this wave are pending.
+__device__ __forceinline__ void wait_dma(int in_flight) {
+  if (in_flight >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if (in_flight == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+static_assert(kDmaPerBlock * (kStages - 2) == 8, "wait_dma counts assume 4 loads per block, 2 ahead");
+
+// Issue the loads of key block j (rows clamped to S_k - 1; the clamped keys
+// are masked and hold finite data) into one stage of the ring.  Each wave
+// moves 2 K and 2 V chunks of 4 rows (1 KB = 64 lanes x 16 B).
+__device__ __forceinline__ void stage_block(uint32_t stage_lds, const uint16_t* kg, const uint16_t* vg,
                                             int j, int S_k, int wave, int lane) {
   const int sub = lane >> 4;    // row within the 4-row chunk
   const int slot = lane & 15;   // LDS chunk slot this lane fills
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int cc = wave * 4 + n;            // 4-row chunk 0..15
+  for (int n = 0; n < 2; ++n) {
+    const int cc = wave * 2 + n;            // 4-row chunk 0..15
     const int row = cc * 4 + sub;
     const int grow = min(j * kBS + row, S_k - 1);
     const size_t off = static_cast<size_t>(grow) * kD + (slot ^ swz(row)) * 8;
-    __builtin_amdgcn_global_load_lds((global_void*)(kg + off), (lds_void*)(stage + cc * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((global_void*)(vg + off), (lds_void*)(stage + kTileBytes + cc * 1024), 16, 0, 0);
+    dma16(kg + off, stage_lds + cc * 1024);
+    dma16(vg + off, stage_lds + kTileBytes + cc * 1024);
   }
 }
 
-template <int T, bool DENSE>
-__global__ __launch_bounds__(256, 1) void attn_window_kernel(const uint16_t* __restrict__ q,
-                                                             const uint16_t* __restrict__ k,
-                                                             const uint16_t* __restrict__ v,
-                                                             const int32_t* __restrict__ blk_idx,
-                                                             uint16_t* __restrict__ out,
-                                                             float* __restrict__ lse, AttnShape s) {
-  constexpr int W = kWaves * T;
+// Workgroup -> (KV head, window).  The hardware deals workgroups to the XCDs
+// round-robin; this maps the k-th workgroup of every XCD so that each XCD
+// runs groups of kXcdGroup adjacent windows of one KV head together (they
+// stream the same K/V blocks through that XCD's L2), latest (heaviest)
+// windows first.  Returns false for padding workgroups.
+__device__ __forceinline__ bool map_window(int n, int nwin, int nheads, int& head, int& win) {
+  const int xcd = n % kXcds, k = n / kXcds;
+  const int rank = (k / kXcdGroup) * kXcds + xcd;  // index of a group of kXcdGroup windows
+  const int ngrp = (nwin + kXcdGroup - 1) / kXcdGroup;
+  head = rank % nheads;
+  const int grp = ngrp - 1 - rank / nheads;
+  win = grp * kXcdGroup + (k % kXcdGroup);
+  return grp >= 0 && win < nwin;
+}
+
+__host__ __device__ constexpr int padded_grid(int nwin, int nheads) {
+  // ranks needed: ngrp * nheads, rounded up to whole rounds of kXcds
+  return ((((nwin + kXcdGroup - 1) / kXcdGroup) * nheads + kXcds - 1) / kXcds) * kXcds * kXcdGroup;
+}
+
+// Wait for register values produced by global loads here, once, on every
+// path: afterwards they count as written by this (empty) asm, so no later
+// instruction inherits a wait on those loads -- which would also wait on the
+// block prefetches issued after them.
+__device__ __forceinline__ bf16x8 settle(bf16x8 x) {
+  u32x4 w = as_u32x4(x);
+  asm volatile("" : "+v"(w));
+  return as_bf16x8(w);
+}
+
+// ---------------------------------------------------------------------------
+// Sparse: 16x16x32 MFMAs, one token per 16-column block (lane = head hl,
+// key quad gq).  MASK says which of the wave's two tokens attend block j.
+// ---------------------------------------------------------------------------
+struct SparseState {
+  bf16x8 qf[kTokPerWave][4];     // Q^T B operands, k-steps of 32 dims
+  floatx4 o[kTokPerWave][8];     // O^T accumulators, 8 tiles of 16 dims
+  float m[kTokPerWave], l[kTokPerWave];
+  int lim[kTokPerWave];          // last visible key position of each token
+};
+
+template <int MASK>
+__device__ __forceinline__ void sparse_block(SparseState& st, const unsigned char* kbuf, const unsigned char* vbuf,
+                                             int j, float sl2, int hl, int gq) {
+  constexpr int T = kTokPerWave;
+  // S^T = K Q^T, one 16-key tile (4 MFMAs over 128 dims) at a time
+  floatx4 sacc[T][4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    const int row = 16 * kt + hl;
+    bf16x8 kf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      kf[ks] = as_bf16x8(load16(kbuf + row * kRowBytes + (((ks * 4 + gq) ^ swz(row)) << 4)));
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      if (!(MASK >> t & 1)) continue;
+      sacc[t][kt] = mfma_16x16x32(kf[0], st.qf[t][0], floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int ks = 1; ks < 4; ++ks) sacc[t][kt] = mfma_16x16x32(kf[ks], st.qf[t][ks], sacc[t][kt]);
+    }
+  }
+  // softmax; lane (hl, gq) holds keys 16*kt + 4*gq + e2 of head hl
+  bf16x8 pf[T][2];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    if (!(MASK >> t & 1)) continue;
+    const bool need_mask = j * kBS + kBS - 1 > st.lim[t];  // wave-uniform
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        if (need_mask && j * kBS + 16 * kt + 4 * gq + e2 > st.lim[t]) sacc[t][kt][e2] = -INFINITY;
+        mx = fmaxf(mx, sacc[t][kt][e2]);
+      }
+    mx = max_xor32(max_xor16(mx)) * sl2;
+    const bool grow = mx > st.m[t] + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float mn = grow ? mx : st.m[t];
+      const float alpha = __builtin_amdgcn_exp2f(st.m[t] - mn);  // m = -inf on a row's first block: 0
+      st.l[t] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) st.o[t][dt] *= alpha;
+      st.m[t] = mn;
+    }
+    const float nm = -st.m[t];
+    uint32_t pw[8];
+    float rs = 0.f;
+#pragma unroll
+    for (int c2 = 0; c2 < 8; ++c2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[t][c2 >> 1][(c2 & 1) * 2], sl2, nm));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[t][c2 >> 1][(c2 & 1) * 2 + 1], sl2, nm));
+      pw[c2] = pack_bf16x2(p0, p1);
+      rs += p0 + p1;
+    }
+    st.l[t] += rs;
+    // k-step s2 of PV takes S^T tiles 2*s2 (slots 0..3) and 2*s2+1 (slots 4..7)
+    pf[t][0] = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
+    pf[t][1] = as_bf16x8(u32x4{pw[4], pw[5], pw[6], pw[7]});
+  }
+  // O^T += V^T P^T.  The V^T operand of lane (hl, gq) for k-step s2 is keys
+  // 32*s2 + 4*gq + {0..3} and 32*s2 + 16 + 4*gq + {0..3} of dim 16*dt + hl.
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    bf16x8 vf[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      bf16x4 half[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int row = 32 * s2 + 16 * hh + 4 * gq + (hl >> 2);
+        const int chunk = 2 * dt + ((hl & 3) >> 1);
+        half[hh] = lds_read_tr(vbuf + row * kRowBytes + ((chunk ^ swz(row)) << 4) + ((hl & 1) << 3));
+      }
+      vf[s2] = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      if (!(MASK >> t & 1)) continue;
+      st.o[t][dt] = mfma_16x16x32(vf[0], pf[t][0], st.o[t][dt]);
+      st.o[t][dt] = mfma_16x16x32(vf[1], pf[t][1], st.o[t][dt]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dense: 32x32x16 MFMAs, the wave's two tokens side by side in the 32
+// columns (lane column c32 = 16 * token + head, key/dim half h2).
+// ---------------------------------------------------------------------------
+struct DenseState {
+  bf16x8 qf[8];        // Q^T B operands, k-steps of 16 dims
+  floatx16 o[4];       // O^T accumulators, 4 tiles of 32 dims
+  float m, l;
+  int lim;             // last visible key position of this lane's token
+};
+
+__device__ __forceinline__ void dense_block(DenseState& st, const unsigned char* kbuf, const unsigned char* vbuf,
+                                            int j, float sl2, bool need_mask, int lane) {
+  const int c32 = lane & 31, h2 = lane >> 5;
+  // S^T tile kt: rows = keys 32*kt + 8*(i/4) + 4*h2 + i%4 of accumulator value i
+  floatx16 sacc[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int row = 32 * kt + c32;
+    floatx16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 kf = as_bf16x8(load16(kbuf + row * kRowBytes + (((2 * ks + h2) ^ swz(row)) << 4)));
+      acc = mfma_32x32x16(kf, st.qf[ks], acc);
+    }
+    sacc[kt] = acc;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (need_mask && j * kBS + 32 * kt + 8 * (i >> 2) + 4 * h2 + (i & 3) > st.lim) sacc[kt][i] = -INFINITY;
+      mx = fmaxf(mx, sacc[kt][i]);
+    }
+  mx = max_xor32(mx) * sl2;
+  const bool grow = mx > st.m + kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(grow)) {
+    const float mn = grow ? mx : st.m;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
+    st.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) st.o[dt] *= alpha;
+    st.m = mn;
+  }
+  const float nm = -st.m;
+  // P^T k-step s (keys 16*s .. 16*s+15): values 8*(s%2) .. 8*(s%2)+7 of tile s/2
+  bf16x8 pf[4];
+  float rs = 0.f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    uint32_t pw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + 2 * e], sl2, nm));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + 2 * e + 1], sl2, nm));
+      pw[e] = pack_bf16x2(p0, p1);
+      rs += p0 + p1;
+    }
+    pf[s] = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
+  }
+  st.l += rs;
+  // O^T += V^T P^T; k-step s, slot e of half h2 is key 16*s + 8*(e/4) + 4*h2 + e%4,
+  // dim 32*dt + c32: two transposing reads of 4-key x 16-dim tiles
+  const int grp = lane >> 4, li = lane & 15;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x4 half[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int row = 16 * s + 8 * hh + 4 * h2 + (li >> 2);
+        const int chunk = 4 * dt + 2 * (grp & 1) + ((li & 3) >> 1);
+        half[hh] = lds_read_tr(vbuf + row * kRowBytes + ((chunk ^ swz(row)) << 4) + ((li & 1) << 3));
+      }
+      const bf16x8 vf = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+      st.o[dt] = mfma_32x32x16(vf, pf[s], st.o[dt]);
+    }
+  }
+}
+
+template <bool DENSE>
+__global__ __launch_bounds__(kWaves * 64, 1) void attn_window_kernel(const uint16_t* __restrict__ q,
+                                                                     const uint16_t* __restrict__ k,
+                                                                     const uint16_t* __restrict__ v,
+                                                                     const int32_t* __restrict__ blk_idx,
+                                                                     uint16_t* __restrict__ out,
+                                                                     float* __restrict__ lse, AttnShape s) {
+  constexpr int T = kTokPerWave;
+  constexpr int NT = kWaves * 64;
   extern __shared__ __align__(1024) unsigned char smem[];
   uint32_t* bmask = reinterpret_cast<uint32_t*>(smem + kStages * kStageBytes);  // [NB], sparse only
   int* blist = reinterpret_cast<int*>(bmask + s.NB);                           // [NB], sparse only
@@ -88,29 +353,71 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const uint16_t* __r
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int hl = lane & 15;
-  const int gq = lane >> 4;
-  const int nwin = (s.S_q + W - 1) / W;
-  const int win = nwin - 1 - static_cast<int>(blockIdx.x);  // latest (heaviest) windows first
-  const int g = blockIdx.y % s.H_kv;
-  const int b = blockIdx.y / s.H_kv;
-  const size_t bg = static_cast<size_t>(b) * s.H_kv + g;
-  const int r0 = win * W;
+  const int nwin = (s.S_q + kWin - 1) / kWin;
+  int bg_i, win;
+  if (!map_window(blockIdx.x, nwin, s.B * s.H_kv, bg_i, win)) return;
+  const int g = bg_i % s.H_kv;
+  const int b = bg_i / s.H_kv;
+  const size_t bg = static_cast<size_t>(bg_i);
+  const int r0 = win * kWin;
+  const int rw = r0 + wave * T;              // first token of this wave
   const int off = s.S_k - s.S_q;
-  const int i_last = off + min(r0 + W, s.S_q) - 1;
+  const int i_last = off + min(r0 + kWin, s.S_q) - 1;
   const int qb_last = i_last / kBS;
   const uint16_t* kg = k + bg * s.S_k * kD;
   const uint16_t* vg = v + bg * s.S_k * kD;
+  const uint32_t ring = lds_addr(smem);
+  const float sl2 = s.scale_log2;
+
+  // ---- per-token queries (the compiler waits for them once, in settle) -----
+  SparseState sp;
+  DenseState dn;
+  if constexpr (DENSE) {
+    const int c32 = lane & 31, h2 = lane >> 5;
+    const int tok = c32 >> 4, hd = c32 & 15;
+    const int r = rw + tok;
+    const bool valid = r < s.S_q && hd < s.G;
+    const uint16_t* qrow = q + (static_cast<size_t>(b * s.H_q + g * s.G + hd) * s.S_q + r) * kD + 8 * h2;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) dn.qf[ks] = valid ? as_bf16x8(load16(qrow + 16 * ks)) : bf16x8{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) dn.qf[ks] = settle(dn.qf[ks]);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) dn.o[dt] = floatx16{};
+    dn.m = -INFINITY;
+    dn.l = 0.f;
+    dn.lim = s.causal ? min(off + r, s.S_k - 1) : s.S_k - 1;
+  } else {
+    const int hl = lane & 15, gq = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int r = rw + t;
+      const bool valid = r < s.S_q && hl < s.G;
+      const uint16_t* qrow = q + (static_cast<size_t>(b * s.H_q + g * s.G + hl) * s.S_q + r) * kD + gq * 8;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) sp.qf[t][ks] = valid ? as_bf16x8(load16(qrow + ks * 32)) : bf16x8{};
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) sp.qf[t][ks] = settle(sp.qf[t][ks]);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) sp.o[t][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      sp.m[t] = -INFINITY;
+      sp.l[t] = 0.f;
+      sp.lim[t] = min(off + rw + t, s.S_k - 1);
+    }
+  }
 
   // ---- the union of attended blocks ---------------------------------------
   int nblk;
   if constexpr (DENSE) {
     nblk = s.causal ? qb_last + 1 : s.NB;
   } else {
-    for (int j = threadIdx.x; j <= qb_last; j += 256) bmask[j] = 0u;
+    for (int j = threadIdx.x; j <= qb_last; j += NT) bmask[j] = 0u;
     __syncthreads();
     const int per = s.topk + s.n_init + s.n_local;
-    for (int e = threadIdx.x; e < W * per; e += 256) {
+    for (int e = threadIdx.x; e < kWin * per; e += NT) {
       const int tok = e / per, slot = e - tok * per;
       const int r = r0 + tok;
       if (r >= s.S_q) continue;
@@ -139,178 +446,91 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const uint16_t* __r
     __syncthreads();
     nblk = n_list;
   }
+  auto block_at = [&](int e) { return DENSE ? e : blist[e]; };
 
-  // first block in flight while the queries load
-  if (nblk > 0) stage_block(smem, kg, vg, DENSE ? 0 : blist[0], s.S_k, wave, lane);
+  // prologue: the first kStages - 1 blocks in flight
+#pragma unroll
+  for (int e = 0; e < kStages - 1; ++e)
+    if (e < nblk) stage_block(ring + e * kStageBytes, kg, vg, block_at(e), s.S_k, wave, lane);
 
-  // ---- per-token state (this wave's T tokens) -------------------------------
-  bf16x8 qf[T][4];
-  floatx4 o[T][8];
-  float m[T], l[T], lr[T];  // l: this lane's fp32 row sum, lr: of the bf16-rounded P
-  int ipos[T];
-  uint32_t valid_mask = 0;
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const int r = r0 + wave * T + t;
-    const bool valid = r < s.S_q;
-    valid_mask |= valid ? (1u << t) : 0u;
-    ipos[t] = off + r;
-    const int h = g * s.G + hl;
-    const uint16_t* qrow = q + (static_cast<size_t>(b * s.H_q + h) * s.S_q + r) * kD + gq * 8;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qf[t][ks] = (valid && hl < s.G) ? as_bf16x8(load16(qrow + ks * 32)) : bf16x8{};
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[t][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    m[t] = -INFINITY;
-    l[t] = 0.f;
-    lr[t] = 0.f;
-  }
+  // dense: this wave's two tokens, their visibility limits and whether any
+  // of them is past the end of the queries
+  const int lim0 = s.causal ? min(off + rw, s.S_k - 1) : s.S_k - 1;
+  const int lim1 = rw + 1 < s.S_q ? (s.causal ? min(off + rw + 1, s.S_k - 1) : s.S_k - 1) : lim0;
 
   // ---- stream the blocks -----------------------------------------------------
   for (int e = 0; e < nblk; ++e) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_dma(min(kStages - 2, nblk - 1 - e));
     __syncthreads();  // block e is in LDS; every wave is done with block e - 1
-    if (e + 1 < nblk)
-      stage_block(smem + ((e + 1) & 1) * kStageBytes, kg, vg, DENSE ? e + 1 : blist[e + 1], s.S_k, wave, lane);
-
-    const int j = DENSE ? e : blist[e];
-    uint32_t wm;
-    if constexpr (DENSE) {
-      wm = 0u;
-#pragma unroll
-      for (int t = 0; t < T; ++t)
-        if ((valid_mask >> t & 1u) && (!s.causal || j * kBS <= ipos[t])) wm |= 1u << t;
-    } else {
-      wm = (bmask[j] >> (wave * T)) & ((1u << T) - 1u);
-    }
-    if (wm == 0u) continue;
-    const unsigned char* kbuf = smem + (e & 1) * kStageBytes;
+    if (e + kStages - 1 < nblk)
+      stage_block(ring + ((e + kStages - 1) % kStages) * kStageBytes, kg, vg, block_at(e + kStages - 1), s.S_k,
+                  wave, lane);
+    const int j = __builtin_amdgcn_readfirstlane(block_at(e));
+    const unsigned char* kbuf = smem + (e % kStages) * kStageBytes;
     const unsigned char* vbuf = kbuf + kTileBytes;
-
-    // S^T[key][head] = K Q^T for every member token
-    floatx4 sacc[T][4];
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) sacc[t][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int row = 16 * kt + hl;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = as_bf16x8(load16(kbuf + row * kRowBytes + (((ks * 4 + gq) ^ swz(row)) << 4)));
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-          if (wm >> t & 1u) sacc[t][kt] = mfma_16x16x32(a, qf[t][ks], sacc[t][kt]);
-      }
-    }
-
-    // online softmax (log2 domain).  P is rounded to bf16 for the PV product.
-    // Row sums stay per lane (each lane holds 16 of a head's 64 keys) and are
-    // reduced across the four lanes of a head once, after the last block: l
-    // sums the fp32 P (for the log-sum-exp), lr the rounded P (O is divided
-    // by lr, so its weights are exactly those the MFMA applied).
-    bf16x8 pf[T][2];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      if (!(wm >> t & 1u)) continue;
-      const int lim = DENSE && !s.causal ? s.S_k - 1 : min(ipos[t], s.S_k - 1);
-      const bool need_mask = j * kBS + kBS - 1 > lim;
-      float z[16];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          float zz = sacc[t][kt][e2] * s.scale_log2;
-          if (need_mask && j * kBS + 16 * kt + 4 * gq + e2 > lim) zz = -INFINITY;
-          z[kt * 4 + e2] = zz;
-          mx = fmaxf(mx, zz);
-        }
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float mn = fmaxf(m[t], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m[t] - mn);  // m = -inf on the first block: 0
-      uint32_t pw[8];
-      float rs = 0.f, rsr = 0.f;
-#pragma unroll
-      for (int c2 = 0; c2 < 8; ++c2) {
-        const float p0 = __builtin_amdgcn_exp2f(z[2 * c2] - mn);
-        const float p1 = __builtin_amdgcn_exp2f(z[2 * c2 + 1] - mn);
-        pw[c2] = pack_bf16x2(p0, p1);
-        rs += p0 + p1;
-        rsr += bf16_lo(pw[c2]) + bf16_hi(pw[c2]);
-      }
-      l[t] = l[t] * alpha + rs;
-      lr[t] = lr[t] * alpha + rsr;
-      m[t] = mn;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[t][dt] *= alpha;
-      // k-step s2 takes S^T tiles 2*s2 (slots 0..3) and 2*s2+1 (slots 4..7)
-      pf[t][0] = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
-      pf[t][1] = as_bf16x8(u32x4{pw[4], pw[5], pw[6], pw[7]});
-    }
-
-    // O^T[dim][head] += V^T P^T; the V^T operand of lane (hl, gq) for k-step
-    // s2 is keys 32*s2 + 4*gq + {0..3} and 32*s2 + 16 + 4*gq + {0..3} of dim
-    // 16*dt + hl: two transposing reads of 4-key x 16-dim tiles
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        bf16x4 half[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int row = 32 * s2 + 16 * hh + 4 * gq + (hl >> 2);
-          const int chunk = 2 * dt + ((hl & 3) >> 1);
-          half[hh] = lds_read_tr(vbuf + row * kRowBytes + ((chunk ^ swz(row)) << 4) + ((hl & 1) << 3));
-        }
-        const bf16x8 a = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-          if (wm >> t & 1u) o[t][dt] = mfma_16x16x32(a, pf[t][s2], o[t][dt]);
-      }
+    if constexpr (DENSE) {
+      if (rw >= s.S_q || j * kBS > lim1) continue;   // neither token sees block j
+      dense_block(dn, kbuf, vbuf, j, sl2, j * kBS + kBS - 1 > lim0, lane);
+    } else {
+      const uint32_t wm = __builtin_amdgcn_readfirstlane((bmask[j] >> (wave * T)) & 3u);
+      const int hl = lane & 15, gq = lane >> 4;
+      if (wm == 3u) sparse_block<3>(sp, kbuf, vbuf, j, sl2, hl, gq);
+      else if (wm == 1u) sparse_block<1>(sp, kbuf, vbuf, j, sl2, hl, gq);
+      else if (wm == 2u) sparse_block<2>(sp, kbuf, vbuf, j, sl2, hl, gq);
     }
   }
 
   // ---- epilogue ---------------------------------------------------------------
+  if constexpr (DENSE) {
+    const int c32 = lane & 31, h2 = lane >> 5;
+    const int tok = c32 >> 4, hd = c32 & 15;
+    const int r = rw + tok;
+    const float l = sum_xor32(dn.l);
+    if (r < s.S_q && hd < s.G) {
+      const int h = g * s.G + hd;
+      const float inv = 1.f / l;
+      uint16_t* orow = out + (static_cast<size_t>(b * s.H_q + h) * s.S_q + r) * kD + 4 * h2;
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    l[t] += shfl_xor(l[t], 16);
-    l[t] += shfl_xor(l[t], 32);
-    lr[t] += shfl_xor(lr[t], 16);
-    lr[t] += shfl_xor(lr[t], 32);
-  }
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    if (!(valid_mask >> t & 1u) || hl >= s.G) continue;
-    const int r = r0 + wave * T + t;
-    const int h = g * s.G + hl;
-    const float inv = 1.f / lr[t];
-    uint16_t* orow = out + (static_cast<size_t>(b * s.H_q + h) * s.S_q + r) * kD + 4 * gq;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const u32x2 w = {pack_bf16x2(o[t][dt][0] * inv, o[t][dt][1] * inv),
-                       pack_bf16x2(o[t][dt][2] * inv, o[t][dt][3] * inv)};
-      *reinterpret_cast<u32x2*>(orow + 16 * dt) = w;
+        for (int a = 0; a < 4; ++a) {
+          const u32x2 w = {pack_bf16x2(dn.o[dt][4 * a] * inv, dn.o[dt][4 * a + 1] * inv),
+                           pack_bf16x2(dn.o[dt][4 * a + 2] * inv, dn.o[dt][4 * a + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * a) = w;
+        }
+      if (lse && h2 == 0) lse[static_cast<size_t>(b * s.H_q + h) * s.S_q + r] = (dn.m + log2f(l)) * kLn2;
     }
-    if (lse && gq == 0) lse[static_cast<size_t>(b * s.H_q + h) * s.S_q + r] = (m[t] + log2f(l[t])) * kLn2;
+  } else {
+    const int hl = lane & 15, gq = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float l = sum_xor32(sum_xor16(sp.l[t]));
+      const int r = rw + t;
+      if (r >= s.S_q || hl >= s.G) continue;
+      const int h = g * s.G + hl;
+      const float inv = 1.f / l;
+      uint16_t* orow = out + (static_cast<size_t>(b * s.H_q + h) * s.S_q + r) * kD + 4 * gq;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const u32x2 w = {pack_bf16x2(sp.o[t][dt][0] * inv, sp.o[t][dt][1] * inv),
+                         pack_bf16x2(sp.o[t][dt][2] * inv, sp.o[t][dt][3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + 16 * dt) = w;
+      }
+      if (lse && gq == 0) lse[static_cast<size_t>(b * s.H_q + h) * s.S_q + r] = (sp.m[t] + log2f(l)) * kLn2;
+    }
   }
 }
-
-constexpr int kTokPerWave = 4;
 
 size_t attn_workspace_bytes(const AttnShape&) { return 0; }
 
 template <bool DENSE>
 static hipError_t launch_window(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* blk_idx,
                                 uint16_t* out, float* lse, const AttnShape& s, hipStream_t stream) {
-  constexpr int W = kWaves * kTokPerWave;
-  const dim3 grid((s.S_q + W - 1) / W, s.B * s.H_kv);
+  const int nwin = (s.S_q + kWin - 1) / kWin;
+  const dim3 grid(padded_grid(nwin, s.B * s.H_kv));
   const size_t lds = kStages * kStageBytes + (DENSE ? 0 : 2 * sizeof(int) * static_cast<size_t>(s.NB));
-  hipLaunchKernelGGL((attn_window_kernel<kTokPerWave, DENSE>), grid, dim3(256), lds, stream, q, k, v, blk_idx,
-                     out, lse, s);
+  hipLaunchKernelGGL((attn_window_kernel<DENSE>), grid, dim3(kWaves * 64), lds, stream, q, k, v, blk_idx, out,
+                     lse, s);
   return hipGetLastError();
 }
 
