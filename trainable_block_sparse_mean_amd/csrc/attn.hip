@@ -95,12 +95,13 @@ __device__ __forceinline__ float sum_xor32(float x) {
 }
 
 // One direct-to-LDS load: 64 lanes x 16 bytes land contiguously at LDS byte
-// address `lds` (M0).  Issued from asm so the compiler does not serialise the
-// later LDS reads behind it; completion is awaited explicitly (wait_dma) before
-// the workgroup barrier that publishes the block.  No output registers.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(gptr) : "memory", "m0");
+// address `lds` (M0), read from the scalar base address plus each lane's
+// 32-bit byte offset.  Issued from asm so the compiler does not serialise the
+// later LDS reads behind it; completion is awaited explicitly (wait_dma)
+// before the workgroup barrier that publishes the block.  No output registers.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(base) : "memory", "m0");
 }
 
 // Wait until at most `in_flight` later blocks' loads of this wave are pending.
@@ -111,21 +112,47 @@ __device__ __forceinline__ void wait_dma(int in_flight) {
 }
 static_assert(kDmaPerBlock * (kStages - 2) == 8, "wait_dma counts assume 4 loads per block, 2 ahead");
 
-// Issue the loads of key block j (rows clamped to S_k - 1; the clamped keys
-// are masked and hold finite data) into one stage of the ring.  Each wave
-// moves 2 K and 2 V chunks of 4 rows (1 KB = 64 lanes x 16 B).
-__device__ __forceinline__ void stage_block(uint32_t stage_lds, const uint16_t* kg, const uint16_t* vg,
-                                            int j, int S_k, int wave, int lane) {
-  const int sub = lane >> 4;    // row within the 4-row chunk
-  const int slot = lane & 15;   // LDS chunk slot this lane fills
+// Per-lane byte offsets, within a 64-key block, of the two 16-byte chunks
+// this lane moves (each wave moves 2 K and 2 V chunks of 4 rows: 1 KB = 64
+// lanes x 16 B per load).  A full block needs no clamping; in a partial
+// last block, rows past S_k - 1 re-read row S_k - 1 (finite data, masked).
+struct DmaLane {
+  uint32_t off[2];
+};
+__device__ __forceinline__ DmaLane dma_lane(int wave, int lane) {
+  DmaLane d;
+  const int sub = lane >> 4, slot = lane & 15;
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
-    const int cc = wave * 2 + n;            // 4-row chunk 0..15
-    const int row = cc * 4 + sub;
-    const int grow = min(j * kBS + row, S_k - 1);
-    const size_t off = static_cast<size_t>(grow) * kD + (slot ^ swz(row)) * 8;
-    dma16(kg + off, stage_lds + cc * 1024);
-    dma16(vg + off, stage_lds + kTileBytes + cc * 1024);
+    const int row = (wave * 2 + n) * 4 + sub;
+    d.off[n] = static_cast<uint32_t>(row * kRowBytes + ((slot ^ swz(row)) << 4));
+  }
+  return d;
+}
+
+// Issue the loads of key block j into one stage of the ring.
+__device__ __forceinline__ void stage_block(uint32_t stage_lds, const uint16_t* kg, const uint16_t* vg, int j,
+                                            int S_k, const DmaLane& d, int wave, int lane) {
+  const char* kb = reinterpret_cast<const char*>(kg) + static_cast<size_t>(j) * kTileBytes;
+  const char* vb = reinterpret_cast<const char*>(vg) + static_cast<size_t>(j) * kTileBytes;
+  if (j * kBS + kBS <= S_k) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const uint32_t lds = stage_lds + (wave * 2 + n) * 1024;
+      dma16(kb, d.off[n], lds);
+      dma16(vb, d.off[n], lds + kTileBytes);
+    }
+  } else {
+    const int sub = lane >> 4, slot = lane & 15;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int row = (wave * 2 + n) * 4 + sub;
+      const int crow = min(row, S_k - 1 - j * kBS);
+      const uint32_t off = static_cast<uint32_t>(crow * kRowBytes + ((slot ^ swz(row)) << 4));
+      const uint32_t lds = stage_lds + (wave * 2 + n) * 1024;
+      dma16(kb, off, lds);
+      dma16(vb, off, lds + kTileBytes);
+    }
   }
 }
 
@@ -170,19 +197,35 @@ struct SparseState {
   int lim[kTokPerWave];          // last visible key position of each token
 };
 
+// Per-lane LDS byte offsets of the sparse fragment reads within a stage:
+// K (A operand of S^T = K Q^T) for k-step ks at row hl (+16 rows per key
+// tile), and V (transposing reads, A operand of O^T += V^T P^T) for dim tile
+// dt at row 4*gq + hl/4 (+16 rows per half, +32 per k-step).
+struct SparseLane {
+  uint32_t k[4], v[8];
+};
+__device__ __forceinline__ SparseLane sparse_lane(int hl, int gq) {
+  SparseLane o;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) o.k[ks] = hl * kRowBytes + (((4 * ks + gq) ^ swz(hl)) << 4);
+  const int vr = 4 * gq + (hl >> 2);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+    o.v[dt] = vr * kRowBytes + (((2 * dt + ((hl & 3) >> 1)) ^ swz(vr)) << 4) + ((hl & 1) << 3);
+  return o;
+}
+
 template <int MASK>
-__device__ __forceinline__ void sparse_block(SparseState& st, const unsigned char* kbuf, const unsigned char* vbuf,
-                                             int j, float sl2, int hl, int gq) {
+__device__ __forceinline__ void sparse_block(SparseState& st, const SparseLane& ln, const unsigned char* kbuf,
+                                             const unsigned char* vbuf, int j, float sl2, int gq) {
   constexpr int T = kTokPerWave;
   // S^T = K Q^T, one 16-key tile (4 MFMAs over 128 dims) at a time
   floatx4 sacc[T][4];
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
-    const int row = 16 * kt + hl;
     bf16x8 kf[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      kf[ks] = as_bf16x8(load16(kbuf + row * kRowBytes + (((ks * 4 + gq) ^ swz(row)) << 4)));
+    for (int ks = 0; ks < 4; ++ks) kf[ks] = as_bf16x8(load16(kbuf + ln.k[ks] + kt * 16 * kRowBytes));
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       if (!(MASK >> t & 1)) continue;
@@ -196,15 +239,18 @@ __device__ __forceinline__ void sparse_block(SparseState& st, const unsigned cha
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     if (!(MASK >> t & 1)) continue;
-    const bool need_mask = j * kBS + kBS - 1 > st.lim[t];  // wave-uniform
-    float mx = -INFINITY;
+    if (j * kBS + kBS - 1 > st.lim[t]) {  // wave-uniform: the block reaches past the token
+      const int first = st.lim[t] - j * kBS - 4 * gq;  // keys 16*kt + e2 > first are masked
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        if (need_mask && j * kBS + 16 * kt + 4 * gq + e2 > st.lim[t]) sacc[t][kt][e2] = -INFINITY;
-        mx = fmaxf(mx, sacc[t][kt][e2]);
-      }
+        for (int e2 = 0; e2 < 4; ++e2)
+          if (16 * kt + e2 > first) sacc[t][kt][e2] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sacc[t][0][0], sacc[t][0][1]), fmaxf(sacc[t][0][2], sacc[t][0][3])),
+                     fmaxf(fmaxf(sacc[t][1][0], sacc[t][1][1]), fmaxf(sacc[t][1][2], sacc[t][1][3])));
+    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sacc[t][2][0], sacc[t][2][1]), fmaxf(sacc[t][2][2], sacc[t][2][3])),
+                         fmaxf(fmaxf(sacc[t][3][0], sacc[t][3][1]), fmaxf(sacc[t][3][2], sacc[t][3][3]))));
     mx = max_xor32(max_xor16(mx)) * sl2;
     const bool grow = mx > st.m[t] + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -217,15 +263,16 @@ __device__ __forceinline__ void sparse_block(SparseState& st, const unsigned cha
     }
     const float nm = -st.m[t];
     uint32_t pw[8];
-    float rs = 0.f;
+    float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int c2 = 0; c2 < 8; ++c2) {
       const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[t][c2 >> 1][(c2 & 1) * 2], sl2, nm));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[t][c2 >> 1][(c2 & 1) * 2 + 1], sl2, nm));
       pw[c2] = pack_bf16x2(p0, p1);
-      rs += p0 + p1;
+      rs0 += p0;
+      rs1 += p1;
     }
-    st.l[t] += rs;
+    st.l[t] += rs0 + rs1;
     // k-step s2 of PV takes S^T tiles 2*s2 (slots 0..3) and 2*s2+1 (slots 4..7)
     pf[t][0] = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
     pf[t][1] = as_bf16x8(u32x4{pw[4], pw[5], pw[6], pw[7]});
@@ -237,14 +284,8 @@ __device__ __forceinline__ void sparse_block(SparseState& st, const unsigned cha
     bf16x8 vf[2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      bf16x4 half[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int row = 32 * s2 + 16 * hh + 4 * gq + (hl >> 2);
-        const int chunk = 2 * dt + ((hl & 3) >> 1);
-        half[hh] = lds_read_tr(vbuf + row * kRowBytes + ((chunk ^ swz(row)) << 4) + ((hl & 1) << 3));
-      }
-      vf[s2] = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+      const unsigned char* p = vbuf + ln.v[dt] + s2 * 32 * kRowBytes;
+      vf[s2] = __builtin_shufflevector(lds_read_tr(p), lds_read_tr(p + 16 * kRowBytes), 0, 1, 2, 3, 4, 5, 6, 7);
     }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -266,31 +307,55 @@ struct DenseState {
   int lim;             // last visible key position of this lane's token
 };
 
-__device__ __forceinline__ void dense_block(DenseState& st, const unsigned char* kbuf, const unsigned char* vbuf,
-                                            int j, float sl2, bool need_mask, int lane) {
-  const int c32 = lane & 31, h2 = lane >> 5;
+// Per-lane LDS byte offsets of the dense fragment reads within a stage: K
+// for k-step ks at row c32 (+32 rows per key tile); V (transposing reads)
+// for dim tile dt and half hh at row 8*hh + 4*h2 + li/4 (+16 rows per k-step).
+struct DenseLane {
+  uint32_t k[8], v[4][2];
+};
+__device__ __forceinline__ DenseLane dense_lane(int lane) {
+  DenseLane o;
+  const int c32 = lane & 31, h2 = lane >> 5, grp = lane >> 4, li = lane & 15;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) o.k[ks] = c32 * kRowBytes + (((2 * ks + h2) ^ swz(c32)) << 4);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int vr = 8 * hh + 4 * h2 + (li >> 2);
+      const int chunk = 4 * dt + 2 * (grp & 1) + ((li & 3) >> 1);
+      o.v[dt][hh] = vr * kRowBytes + ((chunk ^ swz(vr)) << 4) + ((li & 1) << 3);
+    }
+  return o;
+}
+
+__device__ __forceinline__ void dense_block(DenseState& st, const DenseLane& ln, const unsigned char* kbuf,
+                                            const unsigned char* vbuf, int j, float sl2, bool need_mask, int h2) {
   // S^T tile kt: rows = keys 32*kt + 8*(i/4) + 4*h2 + i%4 of accumulator value i
   floatx16 sacc[2];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
-    const int row = 32 * kt + c32;
     floatx16 acc = {};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 kf = as_bf16x8(load16(kbuf + row * kRowBytes + (((2 * ks + h2) ^ swz(row)) << 4)));
-      acc = mfma_32x32x16(kf, st.qf[ks], acc);
-    }
+    for (int ks = 0; ks < 8; ++ks)
+      acc = mfma_32x32x16(as_bf16x8(load16(kbuf + ln.k[ks] + kt * 32 * kRowBytes)), st.qf[ks], acc);
     sacc[kt] = acc;
   }
-  float mx = -INFINITY;
+  if (need_mask) {  // wave-uniform: the block reaches past one of the tokens
+    const int first = st.lim - j * kBS - 4 * h2;
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (need_mask && j * kBS + 32 * kt + 8 * (i >> 2) + 4 * h2 + (i & 3) > st.lim) sacc[kt][i] = -INFINITY;
-      mx = fmaxf(mx, sacc[kt][i]);
-    }
-  mx = max_xor32(mx) * sl2;
+      for (int i = 0; i < 16; ++i)
+        if (32 * kt + 8 * (i >> 2) + (i & 3) > first) sacc[kt][i] = -INFINITY;
+  }
+  float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    mx0 = fmaxf(mx0, sacc[0][i]);
+    mx1 = fmaxf(mx1, sacc[1][i]);
+  }
+  const float mx = max_xor32(fmaxf(mx0, mx1)) * sl2;
   const bool grow = mx > st.m + kRescaleSlack;
   if (__builtin_amdgcn_ballot_w64(grow)) {
     const float mn = grow ? mx : st.m;
@@ -303,7 +368,7 @@ __device__ __forceinline__ void dense_block(DenseState& st, const unsigned char*
   const float nm = -st.m;
   // P^T k-step s (keys 16*s .. 16*s+15): values 8*(s%2) .. 8*(s%2)+7 of tile s/2
   bf16x8 pf[4];
-  float rs = 0.f;
+  float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     uint32_t pw[4];
@@ -312,26 +377,21 @@ __device__ __forceinline__ void dense_block(DenseState& st, const unsigned char*
       const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + 2 * e], sl2, nm));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + 2 * e + 1], sl2, nm));
       pw[e] = pack_bf16x2(p0, p1);
-      rs += p0 + p1;
+      rs0 += p0;
+      rs1 += p1;
     }
     pf[s] = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
   }
-  st.l += rs;
+  st.l += rs0 + rs1;
   // O^T += V^T P^T; k-step s, slot e of half h2 is key 16*s + 8*(e/4) + 4*h2 + e%4,
   // dim 32*dt + c32: two transposing reads of 4-key x 16-dim tiles
-  const int grp = lane >> 4, li = lane & 15;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      bf16x4 half[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int row = 16 * s + 8 * hh + 4 * h2 + (li >> 2);
-        const int chunk = 4 * dt + 2 * (grp & 1) + ((li & 3) >> 1);
-        half[hh] = lds_read_tr(vbuf + row * kRowBytes + ((chunk ^ swz(row)) << 4) + ((li & 1) << 3));
-      }
-      const bf16x8 vf = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 vf = __builtin_shufflevector(lds_read_tr(vbuf + ln.v[dt][0] + s * 16 * kRowBytes),
+                                                lds_read_tr(vbuf + ln.v[dt][1] + s * 16 * kRowBytes), 0, 1, 2,
+                                                3, 4, 5, 6, 7);
       st.o[dt] = mfma_32x32x16(vf, pf[s], st.o[dt]);
     }
   }
@@ -410,6 +470,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_window_kernel(const uint1
   }
 
   // ---- the union of attended blocks ---------------------------------------
+  // Sparse: list entry = block index | (16-bit member mask of the window's
+  // tokens) << 16, ascending by block.
   int nblk;
   if constexpr (DENSE) {
     nblk = s.causal ? qb_last + 1 : s.NB;
@@ -438,7 +500,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_window_kernel(const uint1
         const int j = base + lane;
         const uint32_t mk = j <= qb_last ? bmask[j] : 0u;
         const uint64_t bal = __ballot(mk != 0u);
-        if (mk) blist[cnt + mask_rank(bal)] = j;
+        if (mk) blist[cnt + mask_rank(bal)] = static_cast<int>(static_cast<uint32_t>(j) | (mk << 16));
         cnt += __popcll(bal);
       }
       if (lane == 0) n_list = cnt;
@@ -446,37 +508,53 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_window_kernel(const uint1
     __syncthreads();
     nblk = n_list;
   }
-  auto block_at = [&](int e) { return DENSE ? e : blist[e]; };
+  // entry e of the list (dense: every block in order)
+  auto entry_at = [&](int e) -> uint32_t {
+    if constexpr (DENSE) return static_cast<uint32_t>(e);
+    else return e < nblk ? static_cast<uint32_t>(blist[e]) : 0u;
+  };
 
+  const DmaLane dl = dma_lane(wave, lane);
   // prologue: the first kStages - 1 blocks in flight
 #pragma unroll
   for (int e = 0; e < kStages - 1; ++e)
-    if (e < nblk) stage_block(ring + e * kStageBytes, kg, vg, block_at(e), s.S_k, wave, lane);
+    if (e < nblk) stage_block(ring + e * kStageBytes, kg, vg, entry_at(e) & 0xffffu, s.S_k, dl, wave, lane);
 
-  // dense: this wave's two tokens, their visibility limits and whether any
-  // of them is past the end of the queries
+  // dense: this wave's two tokens' visibility limits (a token past the end of
+  // the queries takes its partner's)
   const int lim0 = s.causal ? min(off + rw, s.S_k - 1) : s.S_k - 1;
   const int lim1 = rw + 1 < s.S_q ? (s.causal ? min(off + rw + 1, s.S_k - 1) : s.S_k - 1) : lim0;
+  const SparseLane spl = sparse_lane(lane & 15, lane >> 4);
+  const DenseLane dnl = dense_lane(lane);
+
+  // list entries of blocks e .. e + kStages - 1 (scalar FIFO, read ahead)
+  uint32_t fifo[kStages];
+#pragma unroll
+  for (int f = 0; f < kStages; ++f) fifo[f] = __builtin_amdgcn_readfirstlane(entry_at(f));
 
   // ---- stream the blocks -----------------------------------------------------
   for (int e = 0; e < nblk; ++e) {
     wait_dma(min(kStages - 2, nblk - 1 - e));
     __syncthreads();  // block e is in LDS; every wave is done with block e - 1
     if (e + kStages - 1 < nblk)
-      stage_block(ring + ((e + kStages - 1) % kStages) * kStageBytes, kg, vg, block_at(e + kStages - 1), s.S_k,
-                  wave, lane);
-    const int j = __builtin_amdgcn_readfirstlane(block_at(e));
+      stage_block(ring + ((e + kStages - 1) % kStages) * kStageBytes, kg, vg, fifo[kStages - 1] & 0xffffu,
+                  s.S_k, dl, wave, lane);
+    const uint32_t ent = fifo[0];
+#pragma unroll
+    for (int f = 0; f < kStages - 1; ++f) fifo[f] = fifo[f + 1];
+    fifo[kStages - 1] = __builtin_amdgcn_readfirstlane(entry_at(e + kStages));
+    const int j = static_cast<int>(ent & 0xffffu);
     const unsigned char* kbuf = smem + (e % kStages) * kStageBytes;
     const unsigned char* vbuf = kbuf + kTileBytes;
     if constexpr (DENSE) {
       if (rw >= s.S_q || j * kBS > lim1) continue;   // neither token sees block j
-      dense_block(dn, kbuf, vbuf, j, sl2, j * kBS + kBS - 1 > lim0, lane);
+      dense_block(dn, dnl, kbuf, vbuf, j, sl2, j * kBS + kBS - 1 > lim0, lane >> 5);
     } else {
-      const uint32_t wm = __builtin_amdgcn_readfirstlane((bmask[j] >> (wave * T)) & 3u);
-      const int hl = lane & 15, gq = lane >> 4;
-      if (wm == 3u) sparse_block<3>(sp, kbuf, vbuf, j, sl2, hl, gq);
-      else if (wm == 1u) sparse_block<1>(sp, kbuf, vbuf, j, sl2, hl, gq);
-      else if (wm == 2u) sparse_block<2>(sp, kbuf, vbuf, j, sl2, hl, gq);
+      const uint32_t wm = (ent >> (16 + wave * T)) & 3u;
+      const int gq = lane >> 4;
+      if (wm == 3u) sparse_block<3>(sp, spl, kbuf, vbuf, j, sl2, gq);
+      else if (wm == 1u) sparse_block<1>(sp, spl, kbuf, vbuf, j, sl2, gq);
+      else if (wm == 2u) sparse_block<2>(sp, spl, kbuf, vbuf, j, sl2, gq);
     }
   }
 
