@@ -38,14 +38,17 @@
 
 namespace infv2 {
 
-constexpr int kWaves = 8;
-constexpr int kTokPerWave = 2;
-constexpr int kWin = kWaves * kTokPerWave;        // tokens per workgroup
+// Sparse: 16 waves x 1 token (4 waves per SIMD: every member token is an
+// independent instruction stream).  Dense: 8 waves x 2 tokens (the 32 MFMA
+// columns).  Both cover a window of kWin = 16 tokens.
+template <bool DENSE> struct Cfg;
+template <> struct Cfg<false> { static constexpr int kWaves = 16, kTok = 1; };
+template <> struct Cfg<true> { static constexpr int kWaves = 8, kTok = 2; };
+constexpr int kWin = 16;                          // tokens per workgroup
 constexpr int kRowBytes = kD * 2;                 // one K or V row in LDS
 constexpr int kTileBytes = kBS * kRowBytes;       // one 64-key block of K (or V)
 constexpr int kStageBytes = 2 * kTileBytes;       // K + V of one block
 constexpr int kStages = 4;                        // LDS ring: 3 blocks in flight
-constexpr int kDmaPerBlock = 4;                   // direct-to-LDS loads per wave per block
 constexpr int kXcds = 8;                          // workgroups are dealt round-robin to 8 XCDs
 constexpr int kXcdGroup = 32;                     // windows kept together on one XCD (one per CU)
 constexpr float kRescaleSlack = 8.f;              // log2 units the running max may lag behind
@@ -54,12 +57,15 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-// Slot of 16-byte chunk c in LDS row r: c ^ swz(r), swz = 4-bit bit reversal
-// of r.  16 aligned rows get 16 distinct slots (16-lane K reads), 8 aligned
-// rows distinct 32-byte pairs and 4 aligned rows distinct 64-byte quads
-// (transposing V reads of the 16x16 and 32x32 layouts).
+// Slot of 16-byte chunk c in LDS row r: c ^ swz(r), with swz a linear map of
+// the row's low 4 bits (bit0 = r0, bit1 = r1, bit2 = r0^r2, bit3 = r0^r1^r3).
+// It is chosen so that every fragment read below is free of bank conflicts
+// whether the LDS serves 8 or 16 lanes of a 16-byte read, or 16 or 32 lanes
+// of an 8-byte transposing read, per cycle: any 8 aligned rows have distinct
+// low 3 slot bits, any 4 aligned rows distinct slot bits 1-2 and 2-3, and
+// any 8 aligned rows distinct slot bits 1-3.
 __device__ __forceinline__ int swz(int r) {
-  return ((r & 1) << 3) | ((r & 2) << 1) | ((r & 4) >> 1) | ((r & 8) >> 3);
+  return (r & 3) | (((r ^ (r >> 2)) & 1) << 2) | (((r ^ (r >> 1) ^ (r >> 3)) & 1) << 3);
 }
 
 __device__ __forceinline__ bf16x4 lds_read_tr(const unsigned char* p) {
@@ -104,52 +110,66 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
                :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(base) : "memory", "m0");
 }
 
-// Wait until at most `in_flight` later blocks' loads of this wave are pending.
+// Wait until at most `in_flight` later blocks' loads of this wave are
+// pending; each block is `per_block` loads per wave.
+template <int per_block>
 __device__ __forceinline__ void wait_dma(int in_flight) {
-  if (in_flight >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else if (in_flight == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  static_assert(per_block == 2 || per_block == 4, "vmcnt immediates below");
+  if (in_flight >= 2) {
+    if constexpr (per_block == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  } else if (in_flight == 1) {
+    if constexpr (per_block == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
 }
-static_assert(kDmaPerBlock * (kStages - 2) == 8, "wait_dma counts assume 4 loads per block, 2 ahead");
 
-// Per-lane byte offsets, within a 64-key block, of the two 16-byte chunks
-// this lane moves (each wave moves 2 K and 2 V chunks of 4 rows: 1 KB = 64
-// lanes x 16 B per load).  A full block needs no clamping; in a partial
-// last block, rows past S_k - 1 re-read row S_k - 1 (finite data, masked).
+// Per-lane byte offsets, within a 64-key block, of the 16-byte chunks this
+// lane moves.  A tile (K or V of one block) is 16 chunks of 4 rows (1 KB =
+// 64 lanes x 16 B per load); each of the WAVES waves moves 16 / WAVES of
+// them for K and as many for V.  A full block needs no clamping; in a
+// partial last block, rows past S_k - 1 re-read row S_k - 1 (finite, masked).
+template <int WAVES>
 struct DmaLane {
-  uint32_t off[2];
+  static constexpr int kChunks = 16 / WAVES;
+  uint32_t off[kChunks];
 };
-__device__ __forceinline__ DmaLane dma_lane(int wave, int lane) {
-  DmaLane d;
+template <int WAVES>
+__device__ __forceinline__ DmaLane<WAVES> dma_lane(int wave, int lane) {
+  DmaLane<WAVES> d;
   const int sub = lane >> 4, slot = lane & 15;
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int row = (wave * 2 + n) * 4 + sub;
+  for (int n = 0; n < DmaLane<WAVES>::kChunks; ++n) {
+    const int row = (wave * DmaLane<WAVES>::kChunks + n) * 4 + sub;
     d.off[n] = static_cast<uint32_t>(row * kRowBytes + ((slot ^ swz(row)) << 4));
   }
   return d;
 }
 
 // Issue the loads of key block j into one stage of the ring.
+template <int WAVES>
 __device__ __forceinline__ void stage_block(uint32_t stage_lds, const uint16_t* kg, const uint16_t* vg, int j,
-                                            int S_k, const DmaLane& d, int wave, int lane) {
+                                            int S_k, const DmaLane<WAVES>& d, int wave, int lane) {
+  constexpr int C = DmaLane<WAVES>::kChunks;
   const char* kb = reinterpret_cast<const char*>(kg) + static_cast<size_t>(j) * kTileBytes;
   const char* vb = reinterpret_cast<const char*>(vg) + static_cast<size_t>(j) * kTileBytes;
   if (j * kBS + kBS <= S_k) {
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const uint32_t lds = stage_lds + (wave * 2 + n) * 1024;
+    for (int n = 0; n < C; ++n) {
+      const uint32_t lds = stage_lds + (wave * C + n) * 1024;
       dma16(kb, d.off[n], lds);
       dma16(vb, d.off[n], lds + kTileBytes);
     }
   } else {
     const int sub = lane >> 4, slot = lane & 15;
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int row = (wave * 2 + n) * 4 + sub;
+    for (int n = 0; n < C; ++n) {
+      const int row = (wave * C + n) * 4 + sub;
       const int crow = min(row, S_k - 1 - j * kBS);
       const uint32_t off = static_cast<uint32_t>(crow * kRowBytes + ((slot ^ swz(row)) << 4));
-      const uint32_t lds = stage_lds + (wave * 2 + n) * 1024;
+      const uint32_t lds = stage_lds + (wave * C + n) * 1024;
       dma16(kb, off, lds);
       dma16(vb, off, lds + kTileBytes);
     }
@@ -188,13 +208,14 @@ __device__ __forceinline__ bf16x8 settle(bf16x8 x) {
 
 // ---------------------------------------------------------------------------
 // Sparse: 16x16x32 MFMAs, one token per 16-column block (lane = head hl,
-// key quad gq).  MASK says which of the wave's two tokens attend block j.
+// key quad gq).  MASK says which of the wave's tokens attend block j.
 // ---------------------------------------------------------------------------
+constexpr int kSparseTok = Cfg<false>::kTok;
 struct SparseState {
-  bf16x8 qf[kTokPerWave][4];     // Q^T B operands, k-steps of 32 dims
-  floatx4 o[kTokPerWave][8];     // O^T accumulators, 8 tiles of 16 dims
-  float m[kTokPerWave], l[kTokPerWave];
-  int lim[kTokPerWave];          // last visible key position of each token
+  bf16x8 qf[kSparseTok][4];      // Q^T B operands, k-steps of 32 dims
+  floatx4 o[kSparseTok][8];      // O^T accumulators, 8 tiles of 16 dims
+  float m[kSparseTok], l[kSparseTok];
+  int lim[kSparseTok];           // last visible key position of each token
 };
 
 // Per-lane LDS byte offsets of the sparse fragment reads within a stage:
@@ -218,7 +239,7 @@ __device__ __forceinline__ SparseLane sparse_lane(int hl, int gq) {
 template <int MASK>
 __device__ __forceinline__ void sparse_block(SparseState& st, const SparseLane& ln, const unsigned char* kbuf,
                                              const unsigned char* vbuf, int j, float sl2, int gq) {
-  constexpr int T = kTokPerWave;
+  constexpr int T = kSparseTok;
   // S^T = K Q^T, one 16-key tile (4 MFMAs over 128 dims) at a time
   floatx4 sacc[T][4];
 #pragma unroll
@@ -398,13 +419,14 @@ __device__ __forceinline__ void dense_block(DenseState& st, const DenseLane& ln,
 }
 
 template <bool DENSE>
-__global__ __launch_bounds__(kWaves * 64, 1) void attn_window_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel(const uint16_t* __restrict__ q,
                                                                      const uint16_t* __restrict__ k,
                                                                      const uint16_t* __restrict__ v,
                                                                      const int32_t* __restrict__ blk_idx,
                                                                      uint16_t* __restrict__ out,
                                                                      float* __restrict__ lse, AttnShape s) {
-  constexpr int T = kTokPerWave;
+  constexpr int kWaves = Cfg<DENSE>::kWaves;
+  constexpr int T = Cfg<DENSE>::kTok;
   constexpr int NT = kWaves * 64;
   extern __shared__ __align__(1024) unsigned char smem[];
   uint32_t* bmask = reinterpret_cast<uint32_t*>(smem + kStages * kStageBytes);  // [NB], sparse only
@@ -514,7 +536,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_window_kernel(const uint1
     else return e < nblk ? static_cast<uint32_t>(blist[e]) : 0u;
   };
 
-  const DmaLane dl = dma_lane(wave, lane);
+  const DmaLane<kWaves> dl = dma_lane<kWaves>(wave, lane);
   // prologue: the first kStages - 1 blocks in flight
 #pragma unroll
   for (int e = 0; e < kStages - 1; ++e)
@@ -534,7 +556,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_window_kernel(const uint1
 
   // ---- stream the blocks -----------------------------------------------------
   for (int e = 0; e < nblk; ++e) {
-    wait_dma(min(kStages - 2, nblk - 1 - e));
+    wait_dma<2 * DmaLane<kWaves>::kChunks>(min(kStages - 2, nblk - 1 - e));
     __syncthreads();  // block e is in LDS; every wave is done with block e - 1
     if (e + kStages - 1 < nblk)
       stage_block(ring + ((e + kStages - 1) % kStages) * kStageBytes, kg, vg, fifo[kStages - 1] & 0xffffu,
@@ -550,11 +572,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_window_kernel(const uint1
       if (rw >= s.S_q || j * kBS > lim1) continue;   // neither token sees block j
       dense_block(dn, dnl, kbuf, vbuf, j, sl2, j * kBS + kBS - 1 > lim0, lane >> 5);
     } else {
-      const uint32_t wm = (ent >> (16 + wave * T)) & 3u;
-      const int gq = lane >> 4;
-      if (wm == 3u) sparse_block<3>(sp, spl, kbuf, vbuf, j, sl2, gq);
-      else if (wm == 1u) sparse_block<1>(sp, spl, kbuf, vbuf, j, sl2, gq);
-      else if (wm == 2u) sparse_block<2>(sp, spl, kbuf, vbuf, j, sl2, gq);
+      static_assert(T == 1, "one token per sparse wave");
+      if ((ent >> (16 + wave)) & 1u) sparse_block<1>(sp, spl, kbuf, vbuf, j, sl2, lane >> 4);
     }
   }
 
@@ -607,7 +626,8 @@ static hipError_t launch_window(const uint16_t* q, const uint16_t* k, const uint
   const int nwin = (s.S_q + kWin - 1) / kWin;
   const dim3 grid(padded_grid(nwin, s.B * s.H_kv));
   const size_t lds = kStages * kStageBytes + (DENSE ? 0 : 2 * sizeof(int) * static_cast<size_t>(s.NB));
-  hipLaunchKernelGGL((attn_window_kernel<DENSE>), grid, dim3(kWaves * 64), lds, stream, q, k, v, blk_idx, out,
+  hipLaunchKernelGGL((attn_window_kernel<DENSE>), grid, dim3(Cfg<DENSE>::kWaves * 64), lds, stream, q, k, v,
+                     blk_idx, out,
                      lse, s);
   return hipGetLastError();
 }
