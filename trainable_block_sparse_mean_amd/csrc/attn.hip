@@ -210,12 +210,12 @@ __device__ __forceinline__ bf16x8 settle(bf16x8 x) {
 // Sparse: 16x16x32 MFMAs, one token per 16-column block (lane = head hl,
 // key quad gq).  MASK says which of the wave's tokens attend block j.
 // ---------------------------------------------------------------------------
-constexpr int kSparseTok = Cfg<false>::kTok;
+static_assert(Cfg<false>::kTok == 1, "one token per sparse wave");
 struct SparseState {
-  bf16x8 qf[kSparseTok][4];      // Q^T B operands, k-steps of 32 dims
-  floatx4 o[kSparseTok][8];      // O^T accumulators, 8 tiles of 16 dims
-  float m[kSparseTok], l[kSparseTok];
-  int lim[kSparseTok];           // last visible key position of each token
+  bf16x8 qf[4];        // Q^T B operands, k-steps of 32 dims
+  floatx4 o[8];        // O^T accumulators, 8 tiles of 16 dims
+  float m, l;
+  int lim;             // last visible key position of the token
 };
 
 // Per-lane LDS byte offsets of the sparse fragment reads within a stage:
@@ -236,85 +236,83 @@ __device__ __forceinline__ SparseLane sparse_lane(int hl, int gq) {
   return o;
 }
 
-template <int MASK>
-__device__ __forceinline__ void sparse_block(SparseState& st, const SparseLane& ln, const unsigned char* kbuf,
-                                             const unsigned char* vbuf, int j, float sl2, int gq) {
-  constexpr int T = kSparseTok;
-  // S^T = K Q^T, one 16-key tile (4 MFMAs over 128 dims) at a time
-  floatx4 sacc[T][4];
+// One online-softmax step of the wave's token over N attended blocks (N * 64
+// keys): S^T = K Q^T for each block, one joint max / rescale, P, then
+// O^T += V^T P^T.  Stage n holds block js[n].
+template <int N>
+__device__ __forceinline__ void sparse_step(SparseState& st, const SparseLane& ln, const unsigned char* const* stg,
+                                            const int* js, float sl2, int gq) {
+  floatx4 sacc[N][4];
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    bf16x8 kf[4];
+  for (int n = 0; n < N; ++n)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kf[ks] = as_bf16x8(load16(kbuf + ln.k[ks] + kt * 16 * kRowBytes));
+    for (int kt = 0; kt < 4; ++kt) {
+      bf16x8 kf[4];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      if (!(MASK >> t & 1)) continue;
-      sacc[t][kt] = mfma_16x16x32(kf[0], st.qf[t][0], floatx4{0.f, 0.f, 0.f, 0.f});
+      for (int ks = 0; ks < 4; ++ks) kf[ks] = as_bf16x8(load16(stg[n] + ln.k[ks] + kt * 16 * kRowBytes));
+      sacc[n][kt] = mfma_16x16x32(kf[0], st.qf[0], floatx4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int ks = 1; ks < 4; ++ks) sacc[t][kt] = mfma_16x16x32(kf[ks], st.qf[t][ks], sacc[t][kt]);
+      for (int ks = 1; ks < 4; ++ks) sacc[n][kt] = mfma_16x16x32(kf[ks], st.qf[ks], sacc[n][kt]);
     }
-  }
-  // softmax; lane (hl, gq) holds keys 16*kt + 4*gq + e2 of head hl
-  bf16x8 pf[T][2];
+  // lane (hl, gq) holds keys 16*kt + 4*gq + e2 of head hl in each block
+  float mx = -INFINITY;
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    if (!(MASK >> t & 1)) continue;
-    if (j * kBS + kBS - 1 > st.lim[t]) {  // wave-uniform: the block reaches past the token
-      const int first = st.lim[t] - j * kBS - 4 * gq;  // keys 16*kt + e2 > first are masked
+  for (int n = 0; n < N; ++n) {
+    if (js[n] * kBS + kBS - 1 > st.lim) {  // wave-uniform: the block reaches past the token
+      const int first = st.lim - js[n] * kBS - 4 * gq;  // keys 16*kt + e2 > first are masked
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2)
-          if (16 * kt + e2 > first) sacc[t][kt][e2] = -INFINITY;
+          if (16 * kt + e2 > first) sacc[n][kt][e2] = -INFINITY;
     }
-    float mx = fmaxf(fmaxf(fmaxf(sacc[t][0][0], sacc[t][0][1]), fmaxf(sacc[t][0][2], sacc[t][0][3])),
-                     fmaxf(fmaxf(sacc[t][1][0], sacc[t][1][1]), fmaxf(sacc[t][1][2], sacc[t][1][3])));
-    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sacc[t][2][0], sacc[t][2][1]), fmaxf(sacc[t][2][2], sacc[t][2][3])),
-                         fmaxf(fmaxf(sacc[t][3][0], sacc[t][3][1]), fmaxf(sacc[t][3][2], sacc[t][3][3]))));
-    mx = max_xor32(max_xor16(mx)) * sl2;
-    const bool grow = mx > st.m[t] + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float mn = grow ? mx : st.m[t];
-      const float alpha = __builtin_amdgcn_exp2f(st.m[t] - mn);  // m = -inf on a row's first block: 0
-      st.l[t] *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) st.o[t][dt] *= alpha;
-      st.m[t] = mn;
-    }
-    const float nm = -st.m[t];
+    for (int kt = 0; kt < 4; ++kt)
+      mx = fmaxf(mx, fmaxf(fmaxf(sacc[n][kt][0], sacc[n][kt][1]), fmaxf(sacc[n][kt][2], sacc[n][kt][3])));
+  }
+  mx = max_xor32(max_xor16(mx)) * sl2;
+  const bool grow = mx > st.m + kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(grow)) {
+    const float mn = grow ? mx : st.m;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - mn);  // m = -inf on a row's first block: 0
+    st.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) st.o[dt] *= alpha;
+    st.m = mn;
+  }
+  const float nm = -st.m;
+  bf16x8 pf[N][2];
+  float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
     uint32_t pw[8];
-    float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int c2 = 0; c2 < 8; ++c2) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[t][c2 >> 1][(c2 & 1) * 2], sl2, nm));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[t][c2 >> 1][(c2 & 1) * 2 + 1], sl2, nm));
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[n][c2 >> 1][(c2 & 1) * 2], sl2, nm));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[n][c2 >> 1][(c2 & 1) * 2 + 1], sl2, nm));
       pw[c2] = pack_bf16x2(p0, p1);
       rs0 += p0;
       rs1 += p1;
     }
-    st.l[t] += rs0 + rs1;
     // k-step s2 of PV takes S^T tiles 2*s2 (slots 0..3) and 2*s2+1 (slots 4..7)
-    pf[t][0] = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
-    pf[t][1] = as_bf16x8(u32x4{pw[4], pw[5], pw[6], pw[7]});
+    pf[n][0] = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
+    pf[n][1] = as_bf16x8(u32x4{pw[4], pw[5], pw[6], pw[7]});
   }
+  st.l += rs0 + rs1;
   // O^T += V^T P^T.  The V^T operand of lane (hl, gq) for k-step s2 is keys
   // 32*s2 + 4*gq + {0..3} and 32*s2 + 16 + 4*gq + {0..3} of dim 16*dt + hl.
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    bf16x8 vf[2];
+  for (int n = 0; n < N; ++n)
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const unsigned char* p = vbuf + ln.v[dt] + s2 * 32 * kRowBytes;
-      vf[s2] = __builtin_shufflevector(lds_read_tr(p), lds_read_tr(p + 16 * kRowBytes), 0, 1, 2, 3, 4, 5, 6, 7);
-    }
+    for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      if (!(MASK >> t & 1)) continue;
-      st.o[t][dt] = mfma_16x16x32(vf[0], pf[t][0], st.o[t][dt]);
-      st.o[t][dt] = mfma_16x16x32(vf[1], pf[t][1], st.o[t][dt]);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const unsigned char* p = stg[n] + kTileBytes + ln.v[dt] + s2 * 32 * kRowBytes;
+        const bf16x8 vf =
+            __builtin_shufflevector(lds_read_tr(p), lds_read_tr(p + 16 * kRowBytes), 0, 1, 2, 3, 4, 5, 6, 7);
+        st.o[dt] = mfma_16x16x32(vf, pf[n][s2], st.o[dt]);
+      }
     }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -471,24 +469,17 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
     dn.lim = s.causal ? min(off + r, s.S_k - 1) : s.S_k - 1;
   } else {
     const int hl = lane & 15, gq = lane >> 4;
+    const bool valid = rw < s.S_q && hl < s.G;
+    const uint16_t* qrow = q + (static_cast<size_t>(b * s.H_q + g * s.G + hl) * s.S_q + rw) * kD + gq * 8;
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const int r = rw + t;
-      const bool valid = r < s.S_q && hl < s.G;
-      const uint16_t* qrow = q + (static_cast<size_t>(b * s.H_q + g * s.G + hl) * s.S_q + r) * kD + gq * 8;
+    for (int ks = 0; ks < 4; ++ks) sp.qf[ks] = valid ? as_bf16x8(load16(qrow + ks * 32)) : bf16x8{};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) sp.qf[t][ks] = valid ? as_bf16x8(load16(qrow + ks * 32)) : bf16x8{};
-    }
+    for (int ks = 0; ks < 4; ++ks) sp.qf[ks] = settle(sp.qf[ks]);
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) sp.qf[t][ks] = settle(sp.qf[t][ks]);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) sp.o[t][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      sp.m[t] = -INFINITY;
-      sp.l[t] = 0.f;
-      sp.lim[t] = min(off + rw + t, s.S_k - 1);
-    }
+    for (int dt = 0; dt < 8; ++dt) sp.o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    sp.m = -INFINITY;
+    sp.l = 0.f;
+    sp.lim = min(off + rw, s.S_k - 1);
   }
 
   // ---- the union of attended blocks ---------------------------------------
@@ -537,43 +528,58 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
   };
 
   const DmaLane<kWaves> dl = dma_lane<kWaves>(wave, lane);
-  // prologue: the first kStages - 1 blocks in flight
-#pragma unroll
-  for (int e = 0; e < kStages - 1; ++e)
-    if (e < nblk) stage_block(ring + e * kStageBytes, kg, vg, entry_at(e) & 0xffffu, s.S_k, dl, wave, lane);
+  constexpr int kDma = 2 * DmaLane<kWaves>::kChunks;  // loads per wave per block
 
-  // dense: this wave's two tokens' visibility limits (a token past the end of
-  // the queries takes its partner's)
-  const int lim0 = s.causal ? min(off + rw, s.S_k - 1) : s.S_k - 1;
-  const int lim1 = rw + 1 < s.S_q ? (s.causal ? min(off + rw + 1, s.S_k - 1) : s.S_k - 1) : lim0;
-  const SparseLane spl = sparse_lane(lane & 15, lane >> 4);
-  const DenseLane dnl = dense_lane(lane);
-
-  // list entries of blocks e .. e + kStages - 1 (scalar FIFO, read ahead)
-  uint32_t fifo[kStages];
+  if constexpr (DENSE) {
+    // prologue: the first kStages - 1 blocks in flight
 #pragma unroll
-  for (int f = 0; f < kStages; ++f) fifo[f] = __builtin_amdgcn_readfirstlane(entry_at(f));
-
-  // ---- stream the blocks -----------------------------------------------------
-  for (int e = 0; e < nblk; ++e) {
-    wait_dma<2 * DmaLane<kWaves>::kChunks>(min(kStages - 2, nblk - 1 - e));
-    __syncthreads();  // block e is in LDS; every wave is done with block e - 1
-    if (e + kStages - 1 < nblk)
-      stage_block(ring + ((e + kStages - 1) % kStages) * kStageBytes, kg, vg, fifo[kStages - 1] & 0xffffu,
-                  s.S_k, dl, wave, lane);
-    const uint32_t ent = fifo[0];
-#pragma unroll
-    for (int f = 0; f < kStages - 1; ++f) fifo[f] = fifo[f + 1];
-    fifo[kStages - 1] = __builtin_amdgcn_readfirstlane(entry_at(e + kStages));
-    const int j = static_cast<int>(ent & 0xffffu);
-    const unsigned char* kbuf = smem + (e % kStages) * kStageBytes;
-    const unsigned char* vbuf = kbuf + kTileBytes;
-    if constexpr (DENSE) {
+    for (int e = 0; e < kStages - 1; ++e)
+      if (e < nblk) stage_block(ring + e * kStageBytes, kg, vg, e, s.S_k, dl, wave, lane);
+    // this wave's two tokens' visibility limits (a token past the end of the
+    // queries takes its partner's)
+    const int lim0 = s.causal ? min(off + rw, s.S_k - 1) : s.S_k - 1;
+    const int lim1 = rw + 1 < s.S_q ? (s.causal ? min(off + rw + 1, s.S_k - 1) : s.S_k - 1) : lim0;
+    const DenseLane dnl = dense_lane(lane);
+    for (int j = 0; j < nblk; ++j) {
+      wait_dma<kDma>(min(kStages - 2, nblk - 1 - j));
+      __syncthreads();  // block j is in LDS; every wave is done with block j - 1
+      if (j + kStages - 1 < nblk)
+        stage_block(ring + ((j + kStages - 1) % kStages) * kStageBytes, kg, vg, j + kStages - 1, s.S_k, dl, wave,
+                    lane);
       if (rw >= s.S_q || j * kBS > lim1) continue;   // neither token sees block j
-      dense_block(dn, dnl, kbuf, vbuf, j, sl2, j * kBS + kBS - 1 > lim0, lane >> 5);
-    } else {
-      static_assert(T == 1, "one token per sparse wave");
-      if ((ent >> (16 + wave)) & 1u) sparse_block<1>(sp, spl, kbuf, vbuf, j, sl2, lane >> 4);
+      const unsigned char* kbuf = smem + (j % kStages) * kStageBytes;
+      dense_block(dn, dnl, kbuf, kbuf + kTileBytes, j, sl2, j * kBS + kBS - 1 > lim0, lane >> 5);
+    }
+  } else {
+    // Pairs of list entries: the ring holds the pair being multiplied (2
+    // stages) and the next pair in flight (the other 2); one barrier per pair.
+    static_assert(kStages == 4, "two pairs of stages");
+    const SparseLane spl = sparse_lane(lane & 15, lane >> 4);
+    const int npair = (nblk + 1) / 2;
+    uint32_t cur0 = __builtin_amdgcn_readfirstlane(entry_at(0)), cur1 = __builtin_amdgcn_readfirstlane(entry_at(1));
+    uint32_t nxt0 = __builtin_amdgcn_readfirstlane(entry_at(2)), nxt1 = __builtin_amdgcn_readfirstlane(entry_at(3));
+    stage_block(ring, kg, vg, cur0 & 0xffffu, s.S_k, dl, wave, lane);
+    if (nblk > 1) stage_block(ring + kStageBytes, kg, vg, cur1 & 0xffffu, s.S_k, dl, wave, lane);
+    const uint32_t bit = 1u << (16 + wave);
+    for (int pi = 0; pi < npair; ++pi) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // pair pi is in LDS; every wave is done with pair pi - 1
+      const int half = (pi & 1) * 2;  // first stage of pair pi
+      if (2 * pi + 2 < nblk) {
+        stage_block(ring + (half ^ 2) * kStageBytes, kg, vg, nxt0 & 0xffffu, s.S_k, dl, wave, lane);
+        if (2 * pi + 3 < nblk)
+          stage_block(ring + ((half ^ 2) + 1) * kStageBytes, kg, vg, nxt1 & 0xffffu, s.S_k, dl, wave, lane);
+      }
+      const unsigned char* stg[2] = {smem + half * kStageBytes, smem + (half + 1) * kStageBytes};
+      const int js[2] = {static_cast<int>(cur0 & 0xffffu), static_cast<int>(cur1 & 0xffffu)};
+      const bool m0 = (cur0 & bit) != 0u, m1 = (cur1 & bit) != 0u;   // cur1 = 0 past the list
+      if (m0 && m1) sparse_step<2>(sp, spl, stg, js, sl2, lane >> 4);
+      else if (m0) sparse_step<1>(sp, spl, stg, js, sl2, lane >> 4);
+      else if (m1) sparse_step<1>(sp, spl, stg + 1, js + 1, sl2, lane >> 4);
+      cur0 = nxt0;
+      cur1 = nxt1;
+      nxt0 = __builtin_amdgcn_readfirstlane(entry_at(2 * pi + 4));
+      nxt1 = __builtin_amdgcn_readfirstlane(entry_at(2 * pi + 5));
     }
   }
 
@@ -599,21 +605,18 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
     }
   } else {
     const int hl = lane & 15, gq = lane >> 4;
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const float l = sum_xor32(sum_xor16(sp.l[t]));
-      const int r = rw + t;
-      if (r >= s.S_q || hl >= s.G) continue;
+    const float l = sum_xor32(sum_xor16(sp.l));
+    if (rw < s.S_q && hl < s.G) {
       const int h = g * s.G + hl;
       const float inv = 1.f / l;
-      uint16_t* orow = out + (static_cast<size_t>(b * s.H_q + h) * s.S_q + r) * kD + 4 * gq;
+      uint16_t* orow = out + (static_cast<size_t>(b * s.H_q + h) * s.S_q + rw) * kD + 4 * gq;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const u32x2 w = {pack_bf16x2(sp.o[t][dt][0] * inv, sp.o[t][dt][1] * inv),
-                         pack_bf16x2(sp.o[t][dt][2] * inv, sp.o[t][dt][3] * inv)};
+        const u32x2 w = {pack_bf16x2(sp.o[dt][0] * inv, sp.o[dt][1] * inv),
+                         pack_bf16x2(sp.o[dt][2] * inv, sp.o[dt][3] * inv)};
         *reinterpret_cast<u32x2*>(orow + 16 * dt) = w;
       }
-      if (lse && gq == 0) lse[static_cast<size_t>(b * s.H_q + h) * s.S_q + r] = (sp.m[t] + log2f(l)) * kLn2;
+      if (lse && gq == 0) lse[static_cast<size_t>(b * s.H_q + h) * s.S_q + rw] = (sp.m + log2f(l)) * kLn2;
     }
   }
 }
