@@ -242,17 +242,19 @@ __device__ __forceinline__ SparseLane sparse_lane(int hl, int gq) {
 template <int N>
 __device__ __forceinline__ void sparse_step(SparseState& st, const SparseLane& ln, const unsigned char* const* stg,
                                             const int* js, float sl2, int gq) {
+  // k-step outer, key tile inner: each step is 4 independent MFMAs whose K
+  // fragments were all requested together
   floatx4 sacc[N][4];
 #pragma unroll
   for (int n = 0; n < N; ++n)
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int ks = 0; ks < 4; ++ks) {
       bf16x8 kf[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kf[ks] = as_bf16x8(load16(stg[n] + ln.k[ks] + kt * 16 * kRowBytes));
-      sacc[n][kt] = mfma_16x16x32(kf[0], st.qf[0], floatx4{0.f, 0.f, 0.f, 0.f});
+      for (int kt = 0; kt < 4; ++kt) kf[kt] = as_bf16x8(load16(stg[n] + ln.k[ks] + kt * 16 * kRowBytes));
 #pragma unroll
-      for (int ks = 1; ks < 4; ++ks) sacc[n][kt] = mfma_16x16x32(kf[ks], st.qf[ks], sacc[n][kt]);
+      for (int kt = 0; kt < 4; ++kt)
+        sacc[n][kt] = mfma_16x16x32(kf[kt], st.qf[ks], ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : sacc[n][kt]);
     }
   // lane (hl, gq) holds keys 16*kt + 4*gq + e2 of head hl in each block
   float mx = -INFINITY;
@@ -301,18 +303,22 @@ __device__ __forceinline__ void sparse_step(SparseState& st, const SparseLane& l
   st.l += rs0 + rs1;
   // O^T += V^T P^T.  The V^T operand of lane (hl, gq) for k-step s2 is keys
   // 32*s2 + 4*gq + {0..3} and 32*s2 + 16 + 4*gq + {0..3} of dim 16*dt + hl.
+  // k-step outer, dim tiles inner in groups of 4: independent MFMAs.
 #pragma unroll
   for (int n = 0; n < N; ++n)
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const unsigned char* p = stg[n] + kTileBytes + ln.v[dt] + s2 * 32 * kRowBytes;
-        const bf16x8 vf =
-            __builtin_shufflevector(lds_read_tr(p), lds_read_tr(p + 16 * kRowBytes), 0, 1, 2, 3, 4, 5, 6, 7);
-        st.o[dt] = mfma_16x16x32(vf, pf[n][s2], st.o[dt]);
+      for (int d0 = 0; d0 < 8; d0 += 4) {
+        bf16x8 vf[4];
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd) {
+          const unsigned char* p = stg[n] + kTileBytes + ln.v[d0 + dd] + s2 * 32 * kRowBytes;
+          vf[dd] = __builtin_shufflevector(lds_read_tr(p), lds_read_tr(p + 16 * kRowBytes), 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd) st.o[d0 + dd] = mfma_16x16x32(vf[dd], pf[n][s2], st.o[d0 + dd]);
       }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -404,15 +410,16 @@ __device__ __forceinline__ void dense_block(DenseState& st, const DenseLane& ln,
   st.l += rs0 + rs1;
   // O^T += V^T P^T; k-step s, slot e of half h2 is key 16*s + 8*(e/4) + 4*h2 + e%4,
   // dim 32*dt + c32: two transposing reads of 4-key x 16-dim tiles
+  // k-step outer, dim tile inner: 4 independent MFMAs per step
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
+  for (int s = 0; s < 4; ++s) {
+    bf16x8 vf[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8 vf = __builtin_shufflevector(lds_read_tr(vbuf + ln.v[dt][0] + s * 16 * kRowBytes),
-                                                lds_read_tr(vbuf + ln.v[dt][1] + s * 16 * kRowBytes), 0, 1, 2,
-                                                3, 4, 5, 6, 7);
-      st.o[dt] = mfma_32x32x16(vf, pf[s], st.o[dt]);
-    }
+    for (int dt = 0; dt < 4; ++dt)
+      vf[dt] = __builtin_shufflevector(lds_read_tr(vbuf + ln.v[dt][0] + s * 16 * kRowBytes),
+                                       lds_read_tr(vbuf + ln.v[dt][1] + s * 16 * kRowBytes), 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) st.o[dt] = mfma_32x32x16(vf[dt], pf[s], st.o[dt]);
   }
 }
 
