@@ -32,8 +32,8 @@
  *    any HIP call; on an error nothing is launched and outputs are untouched.
  *    Supported on the GPU: D = 128, block_size = 64, 1 <= G <= 16,
  *    0 <= topk <= 256; other values give INFV2_ERR_UNSUPPORTED.
- *  - Calls on distinct streams are independent; the library keeps no state
- *    between calls apart from a per-process cache of device properties.
+ *  - The library keeps no state between calls; calls on distinct streams
+ *    with distinct outputs and workspaces are independent.
  */
 #ifndef INFV2_H
 #define INFV2_H
@@ -110,8 +110,11 @@ int infv2_select_blocks(const void* q, const void* k_cmp,
  * Query position i attends keys t <= i of the blocks
  *   {0..n_init-1} U {qb-n_local+1 .. qb} U {selected},  qb = floor(i/block_size).
  * workspace: device memory of at least infv2_sparse_workspace_bytes(...)
- * bytes, 256-byte aligned (holds a block-transposed copy of V and split
- * partials); its contents on entry do not matter.
+ * bytes, 256-byte aligned; its contents on entry do not matter.  Long query
+ * ranges need none (0 bytes).  For few query windows (decode) the block list
+ * of a window is split over several workgroups whose fp32 partial results
+ * (nsplit x B x H_q x S_q rows of 132 floats) are merged by a second kernel;
+ * the split count depends only on B, H_kv, S_q and topk.
  */
 size_t infv2_sparse_workspace_bytes(int B, int H_q, int H_kv, int S_q, int S_k,
                                     int D, int block_size, int topk);

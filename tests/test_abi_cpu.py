@@ -82,9 +82,13 @@ def test_sparse_validation_codes():
 
 def test_workspace_sizes():
     lib = tb.load_library()
-    # prefill attention needs no workspace; the switch carves k_cmp and blk_idx
-    assert lib.infv2_sparse_workspace_bytes(1, 32, 2, 100, 1000, 128, 64, 8) == 0
+    # long queries need no workspace; short ones (decode) hold split-KV
+    # partials: nsplit x B x H_q x S_q rows of 132 floats
+    assert lib.infv2_sparse_workspace_bytes(1, 32, 2, 32768, 32768, 128, 64, 64) == 0
     assert lib.infv2_dense_workspace_bytes(2, 8, 1, 64, 64, 128) == 0
+    dec = lib.infv2_sparse_workspace_bytes(16, 32, 2, 1, 32768, 128, 64, 64)
+    assert dec == 16 * 16 * 32 * 1 * 132 * 4                   # 16 splits
+    assert lib.infv2_sparse_workspace_bytes(1, 32, 2, 1, 1000, 128, 64, 4) == 0   # one split: no partials
     dense = lib.infv2_attn_workspace_bytes(1, 32, 2, 4096, 4096, 128, 64, 16, 4096)
     sparse = lib.infv2_attn_workspace_bytes(1, 32, 2, 4097, 4097, 128, 64, 16, 4096)
     assert dense == lib.infv2_dense_workspace_bytes(1, 32, 2, 4096, 4096, 128)

@@ -60,6 +60,7 @@ AttnShape make_shape(int B, int H_q, int H_kv, int S_q, int S_k, int block_size,
   s.n_local = n_local;
   s.scale_log2 = sl2;
   s.causal = causal;
+  s.nsplit = 1;
   return s;
 }
 

@@ -178,22 +178,26 @@ __device__ __forceinline__ void stage_block(uint32_t stage_lds, const uint16_t* 
 
 // Workgroup -> (KV head, window).  The hardware deals workgroups to the XCDs
 // round-robin; this maps the k-th workgroup of every XCD so that each XCD
-// runs groups of kXcdGroup adjacent windows of one KV head together (they
-// stream the same K/V blocks through that XCD's L2), latest (heaviest)
-// windows first.  Returns false for padding workgroups.
+// runs groups of `gs` (<= kXcdGroup) adjacent windows of one KV head
+// together (they stream the same K/V blocks through that XCD's L2), latest
+// (heaviest) windows first.  Returns false for padding workgroups.
+__host__ __device__ constexpr int xcd_group(int nwin) { return nwin < kXcdGroup ? nwin : kXcdGroup; }
+
 __device__ __forceinline__ bool map_window(int n, int nwin, int nheads, int& head, int& win) {
+  const int gs = xcd_group(nwin);
   const int xcd = n % kXcds, k = n / kXcds;
-  const int rank = (k / kXcdGroup) * kXcds + xcd;  // index of a group of kXcdGroup windows
-  const int ngrp = (nwin + kXcdGroup - 1) / kXcdGroup;
+  const int rank = (k / gs) * kXcds + xcd;  // index of a group of gs windows
+  const int ngrp = (nwin + gs - 1) / gs;
   head = rank % nheads;
   const int grp = ngrp - 1 - rank / nheads;
-  win = grp * kXcdGroup + (k % kXcdGroup);
+  win = grp * gs + (k % gs);
   return grp >= 0 && win < nwin;
 }
 
 __host__ __device__ constexpr int padded_grid(int nwin, int nheads) {
   // ranks needed: ngrp * nheads, rounded up to whole rounds of kXcds
-  return ((((nwin + kXcdGroup - 1) / kXcdGroup) * nheads + kXcds - 1) / kXcds) * kXcds * kXcdGroup;
+  return ((((nwin + xcd_group(nwin) - 1) / xcd_group(nwin)) * nheads + kXcds - 1) / kXcds) * kXcds *
+         xcd_group(nwin);
 }
 
 // Wait for register values produced by global loads here, once, on every
@@ -429,7 +433,8 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
                                                                      const uint16_t* __restrict__ v,
                                                                      const int32_t* __restrict__ blk_idx,
                                                                      uint16_t* __restrict__ out,
-                                                                     float* __restrict__ lse, AttnShape s) {
+                                                                     float* __restrict__ lse,
+                                                                     float* __restrict__ part, AttnShape s) {
   constexpr int kWaves = Cfg<DENSE>::kWaves;
   constexpr int T = Cfg<DENSE>::kTok;
   constexpr int NT = kWaves * 64;
@@ -562,19 +567,25 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
     // stages) and the next pair in flight (the other 2); one barrier per pair.
     static_assert(kStages == 4, "two pairs of stages");
     const SparseLane spl = sparse_lane(lane & 15, lane >> 4);
-    const int npair = (nblk + 1) / 2;
-    uint32_t cur0 = __builtin_amdgcn_readfirstlane(entry_at(0)), cur1 = __builtin_amdgcn_readfirstlane(entry_at(1));
-    uint32_t nxt0 = __builtin_amdgcn_readfirstlane(entry_at(2)), nxt1 = __builtin_amdgcn_readfirstlane(entry_at(3));
-    stage_block(ring, kg, vg, cur0 & 0xffffu, s.S_k, dl, wave, lane);
-    if (nblk > 1) stage_block(ring + kStageBytes, kg, vg, cur1 & 0xffffu, s.S_k, dl, wave, lane);
+    // split-KV: this workgroup takes entries [e_lo, e_hi) of the list
+    const int split = blockIdx.y;
+    const int e_lo = static_cast<int>(static_cast<long long>(split) * nblk / s.nsplit);
+    const int e_hi = static_cast<int>(static_cast<long long>(split + 1) * nblk / s.nsplit);
+    const int nseg = e_hi - e_lo;
+    auto seg_at = [&](int x) -> uint32_t { return x < nseg ? entry_at(e_lo + x) : 0u; };
+    const int npair = (nseg + 1) / 2;
+    uint32_t cur0 = __builtin_amdgcn_readfirstlane(seg_at(0)), cur1 = __builtin_amdgcn_readfirstlane(seg_at(1));
+    uint32_t nxt0 = __builtin_amdgcn_readfirstlane(seg_at(2)), nxt1 = __builtin_amdgcn_readfirstlane(seg_at(3));
+    if (nseg > 0) stage_block(ring, kg, vg, cur0 & 0xffffu, s.S_k, dl, wave, lane);
+    if (nseg > 1) stage_block(ring + kStageBytes, kg, vg, cur1 & 0xffffu, s.S_k, dl, wave, lane);
     const uint32_t bit = 1u << (16 + wave);
     for (int pi = 0; pi < npair; ++pi) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();  // pair pi is in LDS; every wave is done with pair pi - 1
       const int half = (pi & 1) * 2;  // first stage of pair pi
-      if (2 * pi + 2 < nblk) {
+      if (2 * pi + 2 < nseg) {
         stage_block(ring + (half ^ 2) * kStageBytes, kg, vg, nxt0 & 0xffffu, s.S_k, dl, wave, lane);
-        if (2 * pi + 3 < nblk)
+        if (2 * pi + 3 < nseg)
           stage_block(ring + ((half ^ 2) + 1) * kStageBytes, kg, vg, nxt1 & 0xffffu, s.S_k, dl, wave, lane);
       }
       const unsigned char* stg[2] = {smem + half * kStageBytes, smem + (half + 1) * kStageBytes};
@@ -585,8 +596,8 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
       else if (m1) sparse_step<1>(sp, spl, stg + 1, js + 1, sl2, lane >> 4);
       cur0 = nxt0;
       cur1 = nxt1;
-      nxt0 = __builtin_amdgcn_readfirstlane(entry_at(2 * pi + 4));
-      nxt1 = __builtin_amdgcn_readfirstlane(entry_at(2 * pi + 5));
+      nxt0 = __builtin_amdgcn_readfirstlane(seg_at(2 * pi + 4));
+      nxt1 = __builtin_amdgcn_readfirstlane(seg_at(2 * pi + 5));
     }
   }
 
@@ -613,6 +624,20 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
   } else {
     const int hl = lane & 15, gq = lane >> 4;
     const float l = sum_xor32(sum_xor16(sp.l));
+    if (s.nsplit > 1) {
+      // unnormalised partial state of this split, merged by combine_splits_kernel
+      if (rw < s.S_q && hl < s.G) {
+        const int h = g * s.G + hl;
+        float* pr = part + ((static_cast<size_t>(blockIdx.y) * s.B * s.H_q + b * s.H_q + h) * s.S_q + rw) * kPartFloats;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<floatx4*>(pr + 16 * dt + 4 * gq) = sp.o[dt];
+        if (gq == 0) {
+          pr[128] = sp.m;
+          pr[129] = l;
+        }
+      }
+      return;
+    }
     if (rw < s.S_q && hl < s.G) {
       const int h = g * s.G + hl;
       const float inv = 1.f / l;
@@ -628,31 +653,75 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
   }
 }
 
-size_t attn_workspace_bytes(const AttnShape&) { return 0; }
+// Merge the split partials of each query row: m = max_s m_s,
+// l = sum_s l_s 2^(m_s - m), O = sum_s o_s 2^(m_s - m) / l.  One workgroup of
+// 128 threads (one per dim) per row.
+__global__ __launch_bounds__(128) void combine_splits_kernel(const float* __restrict__ part,
+                                                             uint16_t* __restrict__ out, float* __restrict__ lse,
+                                                             int nsplit, size_t rows) {
+  const size_t row = blockIdx.x;
+  const int d = threadIdx.x;
+  const size_t stride = rows * kPartFloats;
+  float m = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp) m = fmaxf(m, part[sp * stride + row * kPartFloats + 128]);
+  float l = 0.f, o = 0.f;
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float* pr = part + sp * stride + row * kPartFloats;
+    const float ms = pr[128];
+    if (ms == -INFINITY) continue;  // a split that saw no block of this row
+    const float w = exp2f(ms - m);
+    l += pr[129] * w;
+    o += pr[d] * w;
+  }
+  out[row * kD + d] = static_cast<uint16_t>(f32_to_bf16_bits(o / l));
+  if (lse && d == 0) lse[row] = (m + log2f(l)) * kLn2;
+}
+
+int sparse_splits(int B, int H_kv, int S_q, int topk) {
+  const long long units = static_cast<long long>(B) * H_kv * ((S_q + kWin - 1) / kWin);
+  if (units >= 128) return 1;
+  const int by_units = static_cast<int>(512 / units);
+  const int by_blocks = max(1, (topk + 3) / 4);  // keep >= ~4 blocks per split
+  return max(1, min(16, min(by_units, by_blocks)));
+}
+
+size_t attn_workspace_bytes(const AttnShape& s) {
+  const int ns = sparse_splits(s.B, s.H_kv, s.S_q, s.topk);
+  if (ns <= 1) return 0;
+  return static_cast<size_t>(ns) * s.B * s.H_q * s.S_q * kPartFloats * sizeof(float);
+}
 
 template <bool DENSE>
 static hipError_t launch_window(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* blk_idx,
-                                uint16_t* out, float* lse, const AttnShape& s, hipStream_t stream) {
+                                uint16_t* out, float* lse, float* part, const AttnShape& s, hipStream_t stream) {
   const int nwin = (s.S_q + kWin - 1) / kWin;
-  const dim3 grid(padded_grid(nwin, s.B * s.H_kv));
+  const dim3 grid(padded_grid(nwin, s.B * s.H_kv), DENSE ? 1 : s.nsplit);
   const size_t lds = kStages * kStageBytes + (DENSE ? 0 : 2 * sizeof(int) * static_cast<size_t>(s.NB));
   hipLaunchKernelGGL((attn_window_kernel<DENSE>), grid, dim3(Cfg<DENSE>::kWaves * 64), lds, stream, q, k, v,
-                     blk_idx, out,
-                     lse, s);
+                     blk_idx, out, lse, part, s);
   return hipGetLastError();
 }
 
 hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               const int32_t* blk_idx, uint16_t* out, float* lse,
-                              const AttnShape& s, void*, hipStream_t stream) {
-  if (s.B == 0 || s.S_q == 0) return hipSuccess;
-  return launch_window<false>(q, k, v, blk_idx, out, lse, s, stream);
+                              const AttnShape& s_in, void* workspace, hipStream_t stream) {
+  if (s_in.B == 0 || s_in.S_q == 0) return hipSuccess;
+  AttnShape s = s_in;
+  s.nsplit = sparse_splits(s.B, s.H_kv, s.S_q, s.topk);
+  float* part = s.nsplit > 1 ? static_cast<float*>(workspace) : nullptr;
+  hipError_t err = launch_window<false>(q, k, v, blk_idx, out, lse, part, s, stream);
+  if (err != hipSuccess || s.nsplit == 1) return err;
+  const size_t rows = static_cast<size_t>(s.B) * s.H_q * s.S_q;
+  hipLaunchKernelGGL(combine_splits_kernel, dim3(rows), dim3(128), 0, stream, part, out, lse, s.nsplit, rows);
+  return hipGetLastError();
 }
 
 hipError_t launch_dense_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                             uint16_t* out, float* lse, const AttnShape& s, void*, hipStream_t stream) {
-  if (s.B == 0 || s.S_q == 0) return hipSuccess;
-  return launch_window<true>(q, k, v, nullptr, out, lse, s, stream);
+                             uint16_t* out, float* lse, const AttnShape& s_in, void*, hipStream_t stream) {
+  if (s_in.B == 0 || s_in.S_q == 0) return hipSuccess;
+  AttnShape s = s_in;
+  s.nsplit = 1;
+  return launch_window<true>(q, k, v, nullptr, out, lse, nullptr, s, stream);
 }
 
 }  // namespace infv2

@@ -14,7 +14,17 @@ struct AttnShape {
   int topk, n_init, n_local;
   float scale_log2;  // softmax scale * log2(e)
   int causal;
+  int nsplit;        // sparse: workgroups sharing one window's block list (1 = no split)
 };
+
+// Split-KV partials of the sparse kernel, in the workspace: for split s and
+// query row (b, h, r), 128 unnormalised fp32 output values relative to the
+// split's running max, then that max (log2 units) and the row sum (two
+// padding floats keep rows 16-byte aligned).
+constexpr int kPartFloats = 132;  // 128 + m + l, padded to 16 bytes
+
+// number of splits the sparse kernel uses for a shape (1 for long queries)
+int sparse_splits(int B, int H_kv, int S_q, int topk);
 
 hipError_t launch_compress_k(const uint16_t* k, uint16_t* k_cmp, int B, int H_kv, int S_k,
                              hipStream_t stream);
