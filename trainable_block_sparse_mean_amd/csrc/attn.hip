@@ -57,17 +57,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-// Slot of 16-byte chunk c in LDS row r: c ^ swz(r), with swz a linear map of
-// the row's low 4 bits (bit0 = r0, bit1 = r1, bit2 = r0^r2, bit3 = r0^r1^r3).
-// It is chosen so that every fragment read below is free of bank conflicts
-// whether the LDS serves 8 or 16 lanes of a 16-byte read, or 16 or 32 lanes
-// of an 8-byte transposing read, per cycle: any 8 aligned rows have distinct
-// low 3 slot bits, any 4 aligned rows distinct slot bits 1-2 and 2-3, and
-// any 8 aligned rows distinct slot bits 1-3.
-__device__ __forceinline__ int swz(int r) {
-  return (r & 3) | (((r ^ (r >> 2)) & 1) << 2) | (((r ^ (r >> 1) ^ (r >> 3)) & 1) << 3);
-}
-
 __device__ __forceinline__ bf16x4 lds_read_tr(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
@@ -76,39 +65,6 @@ __device__ __forceinline__ floatx16 mfma_32x32x16(bf16x8 a, bf16x8 b, floatx16 c
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
-}
-
-// reductions over lanes l, l^16 (the two rows of a row pair) and l, l^32
-// (the two wave halves): v_permlane{16,32}_swap of a value with itself
-// returns both partners' values
-__device__ __forceinline__ float max_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float sum_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// One direct-to-LDS load: 64 lanes x 16 bytes land contiguously at LDS byte
-// address `lds` (M0), read from the scalar base address plus each lane's
-// 32-bit byte offset.  Issued from asm so the compiler does not serialise the
-// later LDS reads behind it; completion is awaited explicitly (wait_dma)
-// before the workgroup barrier that publishes the block.  No output registers.
-__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(base) : "memory", "m0");
-}
 
 // Wait until at most `in_flight` later blocks' loads of this wave are
 // pending; each block is `per_block` loads per wave.
@@ -200,15 +156,6 @@ __host__ __device__ constexpr int padded_grid(int nwin, int nheads) {
          xcd_group(nwin);
 }
 
-// Wait for register values produced by global loads here, once, on every
-// path: afterwards they count as written by this (empty) asm, so no later
-// instruction inherits a wait on those loads -- which would also wait on the
-// block prefetches issued after them.
-__device__ __forceinline__ bf16x8 settle(bf16x8 x) {
-  u32x4 w = as_u32x4(x);
-  asm volatile("" : "+v"(w));
-  return as_bf16x8(w);
-}
 
 // ---------------------------------------------------------------------------
 // Sparse: 16x16x32 MFMAs, one token per 16-column block (lane = head hl,

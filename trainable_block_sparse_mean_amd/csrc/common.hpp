@@ -73,4 +73,67 @@ __device__ __forceinline__ int mask_rank(uint64_t mask) {
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// Slot of 16-byte chunk c in LDS row r: c ^ swz(r), with swz a linear map of
+// the row's low 4 bits (bit0 = r0, bit1 = r1, bit2 = r0^r2, bit3 = r0^r1^r3).
+// It is chosen so that every fragment read below is free of bank conflicts
+// whether the LDS serves 8 or 16 lanes of a 16-byte read, or 16 or 32 lanes
+// of an 8-byte transposing read, per cycle: any 8 aligned rows have distinct
+// low 3 slot bits, any 4 aligned rows distinct slot bits 1-2 and 2-3, and
+// any 8 aligned rows distinct slot bits 1-3.
+__device__ __forceinline__ int swz(int r) {
+  return (r & 3) | (((r ^ (r >> 2)) & 1) << 2) | (((r ^ (r >> 1) ^ (r >> 3)) & 1) << 3);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
+}
+
+// reductions over lanes l, l^16 (the two rows of a row pair) and l, l^32
+// (the two wave halves): v_permlane{16,32}_swap of a value with itself
+// returns both partners' values
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One direct-to-LDS load: 64 lanes x 16 bytes land contiguously at LDS byte
+// address `lds` (M0), read from the scalar base address plus each lane's
+// 32-bit byte offset.  Issued from asm so the compiler does not serialise the
+// later LDS reads behind it; completion is awaited explicitly (wait_dma)
+// before the workgroup barrier that publishes the block.  No output registers.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  // the base must be wave-uniform; readfirstlane keeps it in SGPRs.  The
+  // builtin returns int: both halves go through uint32_t so that the low
+  // half is zero-extended, not sign-extended, into the 64-bit address.
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32)));
+  const uint64_t sbase = (static_cast<uint64_t>(hi) << 32) | lo;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+
+// Wait for register values produced by global loads here, once, on every
+// path: afterwards they count as written by this (empty) asm, so no later
+// instruction inherits a wait on those loads -- which would also wait on the
+// block prefetches issued after them.
+__device__ __forceinline__ bf16x8 settle(bf16x8 x) {
+  u32x4 w = as_u32x4(x);
+  asm volatile("" : "+v"(w));
+  return as_bf16x8(w);
+}
+
 }  // namespace infv2

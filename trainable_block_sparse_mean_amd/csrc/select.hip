@@ -7,237 +7,334 @@
 // selected_attention (top-k per query position) at block granularity (news
 // summary, Technical Mechanism).
 //
-// A wave handles kTok consecutive query tokens of one KV head.  For each
-// token the 16 heads of the group are the N dimension of a 16x16x32 bf16
-// MFMA and the compressed keys the M dimension, so a tile of 16 block scores
-// is 4 MFMAs (K = 128).  Each compressed-key fragment is loaded once per wave
-// and applied to all of its tokens.  Pass 1 computes each head's log-sum-exp
-// over the fully visible blocks with an online max; pass 2 recomputes the
-// scores, normalises them and sums the heads with DPP row rotations (the 16
-// lanes of a row hold the 16 heads of one block).  Group scores stay in LDS,
-// never in HBM.  The top-k is an exact radix select on the fp32 bit patterns
-// (non-negative floats order like their bits), then ties are taken lowest
-// index first and the kept indices compacted in ascending order by ballot.
+// One workgroup = 16 consecutive query tokens of one KV head, one token per
+// wave.  The compressed keys stream through a 3-slot LDS ring of CH-block
+// chunks (direct-to-LDS loads, two chunks in flight, one barrier per chunk)
+// that all 16 waves read, so each chunk comes from L2 once per workgroup and
+// pass.  For a token, S = Q k_cmp^T on 16x16x32 bf16 MFMAs puts the 16 heads
+// of the group in the rows and 16 compressed blocks in the columns: lane
+// (column hl, row quad gq) holds heads 4*gq .. 4*gq+3 of block 16*tile + hl.
+//   pass 1: each lane keeps, per head, a running max (moved only when a
+//           score exceeds it by 2^8) and a sum of exp2 over its blocks; the 16
+//           lanes of a row are merged at the end -> per-head log-sum-exp
+//           (log2 units).
+//   pass 2: p = exp2(z - lse) per head, the group score of a block is the sum
+//           over the lane's 4 heads and the 4 row quads (two permlane swaps);
+//           it goes to LDS only, never to HBM.
+// Heads beyond G (G < 16) have zero queries and an infinite log-sum-exp, so
+// they add exactly 0.  The top-k is an exact radix select on the fp32 bit
+// patterns (non-negative floats order like their bits); ties are then taken
+// lowest index first and the kept indices compacted in ascending order by
+// ballot.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace infv2 {
 
-constexpr int kSelWaves = 4;
-constexpr int kSelTok = 4;                          // tokens per wave
-constexpr int kSelWin = kSelWaves * kSelTok;        // tokens per workgroup
-constexpr int kMaxCandIt = 32;                      // NB <= 2048: at most 32 candidates per lane
+constexpr int kSelWaves = 16;           // = tokens per workgroup
+constexpr int kSelSlots = 3;            // LDS ring: the chunk being read + 2 in flight
+constexpr int kSelRowBytes = kD * 2;    // one compressed block
+constexpr size_t kSelLdsMax = 160 * 1024;
+constexpr float kSelSlack = 8.f;         // log2 units a running max may lag
 
-// sum over the 16 lanes of a DPP row (every lane receives the sum)
-__device__ __forceinline__ float row_sum16(float x) {
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false));  // row_ror:8
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xf, 0xf, false));  // row_ror:4
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x122, 0xf, 0xf, false));  // row_ror:2
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x121, 0xf, 0xf, false));  // row_ror:1
-  return x;
+// floats per token row of block scores in LDS
+__host__ __device__ constexpr int sel_stride(int NB) { return (NB + 3) & ~3; }
+
+template <int CH>
+constexpr size_t select_lds(int NB) {
+  return static_cast<size_t>(kSelSlots) * CH * kSelRowBytes + static_cast<size_t>(kSelWaves) * sel_stride(NB) * 4;
 }
 
-// online (max, sum of exp2) of the two lanes l and l ^ off
-__device__ __forceinline__ void lse_merge(float& m, float& l, int off) {
-  const float mo = shfl_xor(m, off), lo = shfl_xor(l, off);
+// (max, sum of exp2 relative to the max) of the lanes l and l ^ mask within
+// a 16-lane DPP row; dpp = row_ror control.  Both partners compute the same
+// commutative expression, so after the four steps all 16 lanes hold
+// bit-identical results.
+template <int DPP>
+__device__ __forceinline__ void lse_merge_row(float& m, float& l) {
+  const float mo = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), DPP, 0xf, 0xf, false));
+  const float lo = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(l), DPP, 0xf, 0xf, false));
   const float mn = fmaxf(m, mo);
   l = (m == -INFINITY ? 0.f : l * exp2f(m - mn)) + (mo == -INFINITY ? 0.f : lo * exp2f(mo - mn));
   m = mn;
 }
 
+// Exact top-kk (kk = topk < nC) of the nC scores cand[0 .. nC), candidate c
+// in slot c / 64 of lane c % 64 (NS >= ceil(nC / 64) slots per lane).  Keys
+// are the fp32 bit patterns with the sign cleared: every key is below 2^31,
+// also for NaN scores (which order above +inf), and non-negative floats order
+// like their keys.  A bitwise radix search finds the kk-th largest key tt;
+// the keys above tt and the first (lowest-index) ties at tt are kept, written
+// to out[0 .. kk) in ascending index order (index = first + c).
+template <int NS>
+__device__ __forceinline__ void topk_row(const float* cand, int nC, int topk, int first, int32_t* out,
+                                         float* out_s, int lane) {
+  const int kk = topk;
+  uint32_t x[NS];
+#pragma unroll
+  for (int t = 0; t < NS; ++t) {
+    const int c = t * 64 + lane;
+    x[t] = c < nC ? __float_as_uint(cand[c]) & 0x7fffffffu : 0u;
+  }
+  // largest tt with #{x >= tt} >= kk (padding keys are 0 and never reach a
+  // candidate value, which has a bit set)
+  uint32_t tt = 0;
+  for (int bit = 30; bit >= 0; --bit) {
+    const uint32_t cv = tt | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int t = 0; t < NS; ++t) cnt += __popcll(__ballot(x[t] >= cv));
+    if (cnt >= kk) tt = cv;
+  }
+  int n_gt = 0;
+#pragma unroll
+  for (int t = 0; t < NS; ++t) n_gt += __popcll(__ballot(x[t] > tt));
+  const int need_eq = kk - n_gt;  // ties at tt, lowest indices first
+
+  int eq_before = 0, n_out = 0;
+#pragma unroll
+  for (int t = 0; t < NS; ++t) {
+    const bool valid = t * 64 + lane < nC;
+    const bool gt = x[t] > tt;
+    const bool eq = valid && x[t] == tt;
+    const uint64_t eqm = __ballot(eq);
+    const bool sel = gt || (eq && eq_before + mask_rank(eqm) < need_eq);
+    eq_before += __popcll(eqm);
+    const uint64_t selm = __ballot(sel);
+    const int pos = n_out + mask_rank(selm);
+    if (sel && pos < kk) {
+      out[pos] = first + t * 64 + lane;
+      if (out_s) out_s[pos] = __uint_as_float(x[t]);
+    }
+    n_out += __popcll(selm);
+  }
+}
+
+template <int CH>
 __global__ __launch_bounds__(kSelWaves * 64) void select_blocks_kernel(const uint16_t* __restrict__ q,
                                                                        const uint16_t* __restrict__ kc,
                                                                        int32_t* __restrict__ blk_idx,
                                                                        float* __restrict__ blk_score,
                                                                        AttnShape s) {
-  extern __shared__ float sig_all[];  // [kSelWin][sig_stride]
-  // per-token stride: NB rounded up to whole 16-block tiles, so the tile
-  // stores below stay inside each token's own row
-  const int sig_stride = (s.NB + 15) & ~15;
-  const int wave = threadIdx.x >> 6;
+  constexpr int kTiles = CH / 16;               // 16-block MFMA tiles per chunk
+  constexpr int kSlotBytes = CH * kSelRowBytes;
+  constexpr int kDmaWaves = CH / 4;             // each moves 4 rows (1 KB) of a chunk
+  extern __shared__ __align__(16) unsigned char sel_smem[];
+  const uint32_t ring = lds_addr(sel_smem);
+  float* sig_all = reinterpret_cast<float*>(sel_smem + kSelSlots * kSlotBytes);
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar) from here on
   const int lane = threadIdx.x & 63;
-  const int hl = lane & 15;   // head within the group (MFMA column)
-  const int gq = lane >> 4;   // k-slot group / row quad
+  const int hl = lane & 15;   // MFMA column: block within the tile
+  const int gq = lane >> 4;   // row quad: heads 4*gq .. 4*gq+3
   const int g = blockIdx.y % s.H_kv;
   const int b = blockIdx.y / s.H_kv;
-  const int r0 = blockIdx.x * kSelWin + wave * kSelTok;  // first token of this wave
+  const int r0 = (gridDim.x - 1 - blockIdx.x) * kSelWaves;  // latest (heaviest) tokens first
+  const int r = r0 + wave;    // this wave's token
   const int off = s.S_k - s.S_q;
+  const bool active = r < s.S_q;
+  const int nv = active ? (off + r + 1) / kBS : 0;  // fully visible blocks
+  const int r_last = min(r0 + kSelWaves, s.S_q) - 1;
+  const int nv_max = (off + r_last + 1) / kBS;      // largest nv of the workgroup
+  const int nch = (nv_max + CH - 1) / CH;
+  float* sig = sig_all + wave * sel_stride(s.NB);
+  const float sl2 = s.scale_log2;
 
-  int nv[kSelTok];
-  int nv_max = 0;
+  // A operands: Q of the token (lane row = head hl, k-slots = dims 8*gq + 32*ks);
+  // rows of heads >= G are zero
+  bf16x8 qa[4];
+  {
+    const bool ok = active && hl < s.G;
+    const uint16_t* qrow = q + (static_cast<size_t>(b * s.H_q + g * s.G + hl) * s.S_q + r) * kD + gq * 8;
+    u32x4 raw[4];
 #pragma unroll
-  for (int t = 0; t < kSelTok; ++t) {
-    const int r = r0 + t;
-    nv[t] = r < s.S_q ? (off + r + 1) / kBS : 0;
-    nv_max = max(nv_max, nv[t]);
+    for (int ks = 0; ks < 4; ++ks) raw[ks] = ok ? load16(qrow + ks * 32) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qa[ks] = settle(as_bf16x8(raw[ks]));
+  }
+  const uint16_t* kg = kc + static_cast<size_t>(b * s.H_kv + g) * s.NB * kD;
+
+  // chunk loads: wave w < kDmaWaves moves rows 4w .. 4w+3 of a chunk; lane
+  // (sub, slot) fetches 16-byte column slot ^ swz(row) of row 4w + sub into
+  // that row's slot (rows past NB - 1 re-read row NB - 1; never used)
+  const int drow = 4 * wave + (lane >> 4);
+  const uint32_t dcol = static_cast<uint32_t>(((lane & 15) ^ swz(drow)) << 4);
+  const int nit = 2 * nch;  // both passes stream the same chunks
+  auto stage = [&](int it) {
+    if (wave < kDmaWaves && it < nit) {
+      const int c = it < nch ? it : it - nch;
+      const int j = min(c * CH + drow, s.NB - 1);
+      dma16(kg, static_cast<uint32_t>(j) * kSelRowBytes + dcol,
+            ring + (it % kSelSlots) * kSlotBytes + wave * 1024);
+    }
+  };
+  // B-operand read offsets (row = block within the tile, k-step ks)
+  uint32_t boff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) boff[ks] = hl * kSelRowBytes + (((4 * ks + gq) ^ swz(hl)) << 4);
+
+  float m[4], l[4], lse2[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+    lse2[i] = INFINITY;
   }
 
-  // ---- group scores -> LDS ------------------------------------------------
-  if (nv_max > 0) {
-    bf16x8 qf[kSelTok][4];
+  // NT tiles of S from `buf` starting at tile t0: acc[t][i] = z(head 4*gq + i, block)
+  auto scores = [&](const unsigned char* buf, int t0, auto nt_c, floatx4* acc) {
+    constexpr int NT = decltype(nt_c)::value;
 #pragma unroll
-    for (int t = 0; t < kSelTok; ++t) {
-      const int r = r0 + t;
-      const uint16_t* qrow =
-          q + (static_cast<size_t>(b * s.H_q + g * s.G + hl) * s.S_q + r) * kD + gq * 8;
+    for (int t = 0; t < NT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        qf[t][ks] = (r < s.S_q && hl < s.G) ? as_bf16x8(load16(qrow + ks * 32)) : bf16x8{};
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc[t] = mfma_16x16x32(qa[ks], as_bf16x8(load16(buf + boff[ks] + (t0 + t) * 16 * kSelRowBytes)), acc[t]);
+  };
+  // pass 1 update over NT tiles; masked scores (-inf) add nothing.  The
+  // running max m (log2 units) only moves when a score exceeds it by more
+  // than kSelSlack (decided per wave), so most chunks need no rescaling; the
+  // sum stays below 2^8 per term.
+  auto lse_update = [&](const floatx4* acc, auto nt_c) {
+    constexpr int NT = decltype(nt_c)::value;
+    float mx[4];
+    bool need = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mx[i] = acc[0][i];
+#pragma unroll
+      for (int t = 1; t < NT; ++t) mx[i] = fmaxf(mx[i], acc[t][i]);
+      mx[i] *= sl2;
+      need |= mx[i] > m[i] + kSelSlack;
     }
-    const uint16_t* kbase = kc + static_cast<size_t>(b * s.H_kv + g) * s.NB * kD + gq * 8;
-    const int ntile = (nv_max + 15) / 16;
-
-    // pass 1: per-head log-sum-exp (log2 domain), each lane over its rows
-    float m[kSelTok], l[kSelTok];
+    if (__ballot(need) != 0) {
 #pragma unroll
-    for (int t = 0; t < kSelTok; ++t) {
-      m[t] = -INFINITY;
-      l[t] = 0.f;
-    }
-    for (int jt = 0; jt < ntile; ++jt) {
-      const int jrow = min(jt * 16 + hl, s.NB - 1);
-      bf16x8 kf[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kf[ks] = as_bf16x8(load16(kbase + static_cast<size_t>(jrow) * kD + ks * 32));
-#pragma unroll
-      for (int t = 0; t < kSelTok; ++t) {
-        floatx4 acc = mfma_16x16x32(kf[0], qf[t][0], floatx4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int ks = 1; ks < 4; ++ks) acc = mfma_16x16x32(kf[ks], qf[t][ks], acc);
-        float zmax = -INFINITY;
-        float z[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = jt * 16 + gq * 4 + e;
-          z[e] = j < nv[t] ? acc[e] * s.scale_log2 : -INFINITY;
-          zmax = fmaxf(zmax, z[e]);
-        }
-        if (zmax > -INFINITY) {
-          const float mn = fmaxf(m[t], zmax);
-          float add = 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) add += exp2f(z[e] - mn);
-          l[t] = l[t] * exp2f(m[t] - mn) + add;
-          m[t] = mn;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const float mn = fmaxf(m[i], mx[i]);
+        l[i] = mn == -INFINITY ? 0.f : l[i] * __builtin_amdgcn_exp2f(m[i] - mn);
+        m[i] = mn;
       }
     }
-    float lse2[kSelTok];
 #pragma unroll
-    for (int t = 0; t < kSelTok; ++t) {
-      lse_merge(m[t], l[t], 16);
-      lse_merge(m[t], l[t], 32);
-      lse2[t] = m[t] + log2f(l[t]);
+    for (int i = 0; i < 4; ++i) {
+      const float mref = m[i] == -INFINITY ? 0.f : m[i];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) l[i] += __builtin_amdgcn_exp2f(fmaf(acc[t][i], sl2, -mref));
     }
+  };
+  // pass 2: group score of this lane's block in a tile (all 64 lanes get the
+  // column sum)
+  auto group_score = [&](const floatx4& acc) {
+    float p = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p += __builtin_amdgcn_exp2f(fmaf(acc[i], sl2, -lse2[i]));
+    return sum_xor32(sum_xor16(p));
+  };
+  using AllTiles = std::integral_constant<int, kTiles>;
+  using OneTile = std::integral_constant<int, 1>;
 
-    // pass 2: normalised scores, summed over the heads of the group
-    for (int jt = 0; jt < ntile; ++jt) {
-      const int jrow = min(jt * 16 + hl, s.NB - 1);
-      bf16x8 kf[4];
+  stage(0);
+  stage(1);
+  for (int it = 0; it < nit; ++it) {  // chunk it % nch: pass 1, then pass 2
+    if (it + 1 < nit) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // chunk `it` is in LDS; every wave is done with chunk it - 1
+    stage(it + 2);    // into the slot chunk it - 1 used
+    if (it == nch) {
+      // end of pass 1: merge the 16 lanes of each row (one head per register i)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kf[ks] = as_bf16x8(load16(kbase + static_cast<size_t>(jrow) * kD + ks * 32));
+      for (int i = 0; i < 4; ++i) {
+        lse_merge_row<0x128>(m[i], l[i]);
+        lse_merge_row<0x124>(m[i], l[i]);
+        lse_merge_row<0x122>(m[i], l[i]);
+        lse_merge_row<0x121>(m[i], l[i]);
+        lse2[i] = 4 * gq + i < s.G ? m[i] + log2f(l[i]) : INFINITY;
+      }
+    }
+    const int c = it < nch ? it : it - nch;
+    const int jc = c * CH;  // first block of the chunk
+    if (!active || jc >= nv) continue;
+    const unsigned char* buf = sel_smem + (it % kSelSlots) * kSlotBytes;
+    const bool full = jc + CH <= nv;
+    if (it < nch) {
+      if (full) {
+        floatx4 acc[kTiles];
+        scores(buf, 0, AllTiles{}, acc);
+        lse_update(acc, AllTiles{});
+      } else {
+        for (int t = 0; t < kTiles && jc + 16 * t < nv; ++t) {
+          floatx4 acc[1];
+          scores(buf, t, OneTile{}, acc);
+          const bool vis = jc + 16 * t + hl < nv;
 #pragma unroll
-      for (int t = 0; t < kSelTok; ++t) {
-        if (jt * 16 >= nv[t]) continue;
-        floatx4 acc = mfma_16x16x32(kf[0], qf[t][0], floatx4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int ks = 1; ks < 4; ++ks) acc = mfma_16x16x32(kf[ks], qf[t][ks], acc);
-        floatx4 p;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = jt * 16 + gq * 4 + e;
-          p[e] = row_sum16((j < nv[t] && hl < s.G) ? exp2f(acc[e] * s.scale_log2 - lse2[t]) : 0.f);
+          for (int i = 0; i < 4; ++i) acc[0][i] = vis ? acc[0][i] : -INFINITY;
+          lse_update(acc, OneTile{});
         }
-        // lane (hl = 0, gq) stores the 4 group scores of blocks 16*jt + 4*gq + e
-        if (hl == 0) *reinterpret_cast<floatx4*>(sig_all + (wave * kSelTok + t) * sig_stride + jt * 16 + gq * 4) = p;
+      }
+    } else {
+      if (full) {
+        floatx4 acc[kTiles];
+        scores(buf, 0, AllTiles{}, acc);
+        // row quad gq stores tile gq % kTiles (quads with the same tile store
+        // the same value to the same address)
+        float mine = 0.f;
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+          const float p = group_score(acc[t]);
+          mine = (gq % kTiles) == t ? p : mine;
+        }
+        sig[jc + 16 * (gq % kTiles) + hl] = mine;
+      } else {
+        for (int t = 0; t < kTiles && jc + 16 * t < nv; ++t) {
+          floatx4 acc[1];
+          scores(buf, t, OneTile{}, acc);
+          const float p = group_score(acc[0]);
+          const int j = jc + 16 * t + hl;
+          if (gq == 0 && j < nv) sig[j] = p;
+        }
       }
     }
   }
-  __syncthreads();  // (each wave reads only its own tokens' scores; kept for clarity)
 
-  if (s.topk == 0) return;
+  if (!active || s.topk == 0) return;  // no barriers below
 
-  // ---- top-k over the candidates n_init .. qb - n_local, one token at a time -
-  for (int t = 0; t < kSelTok; ++t) {
-    const int r = r0 + t;
-    if (r >= s.S_q) break;
-    const float* sig = sig_all + (wave * kSelTok + t) * sig_stride;
-    const int qb = (off + r) / kBS;
-    const int lo = s.n_init;
-    const int hi = qb - s.n_local;
-    const int nC = hi >= lo ? hi - lo + 1 : 0;
-    const int kk = min(s.topk, nC);
-    int32_t* out = blk_idx + (static_cast<size_t>(b * s.H_kv + g) * s.S_q + r) * s.topk;
-    float* out_s = blk_score ? blk_score + (static_cast<size_t>(b * s.H_kv + g) * s.S_q + r) * s.topk : nullptr;
+  // ---- top-k over the candidates n_init .. qb - n_local ---------------------
+  const int qb = (off + r) / kBS;
+  const int lo = s.n_init;
+  const int hi = qb - s.n_local;
+  const int nC = hi >= lo ? hi - lo + 1 : 0;
+  int32_t* out = blk_idx + (static_cast<size_t>(b * s.H_kv + g) * s.S_q + r) * s.topk;
+  float* out_s = blk_score ? blk_score + (static_cast<size_t>(b * s.H_kv + g) * s.S_q + r) * s.topk : nullptr;
 
-    if (nC <= s.topk) {  // every candidate is kept
-      for (int e = lane; e < s.topk; e += 64) {
-        out[e] = e < nC ? lo + e : -1;
-        if (out_s) out_s[e] = e < nC ? sig[lo + e] : 0.f;
-      }
-      continue;
+  if (nC <= s.topk) {  // every candidate is kept
+    for (int e = lane; e < s.topk; e += 64) {
+      out[e] = e < nC ? lo + e : -1;
+      if (out_s) out_s[e] = e < nC ? sig[lo + e] : 0.f;
     }
-
-    const int nIt = (nC + 63) / 64;
-    uint32_t x[kMaxCandIt];
-#pragma unroll
-    for (int it = 0; it < kMaxCandIt; ++it) {
-      const int c = it * 64 + lane;
-      x[it] = (it < nIt && c < nC) ? __float_as_uint(sig[lo + c]) : 0u;
-    }
-    // validity of slot `it` of this lane: it * 64 + lane < nC
-    auto valid = [&](int it) { return it * 64 + lane < nC; };
-
-    // largest tt with #{x >= tt} >= kk is the kk-th largest value (bits 30..0;
-    // the sign bit is clear for non-negative scores)
-    uint32_t tt = 0;
-    for (int bit = 30; bit >= 0; --bit) {
-      const uint32_t cand = tt | (1u << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int it = 0; it < kMaxCandIt; ++it)
-        if (it < nIt) cnt += __popcll(__ballot(valid(it) && x[it] >= cand));
-      if (cnt >= kk) tt = cand;
-    }
-    int n_gt = 0;
-#pragma unroll
-    for (int it = 0; it < kMaxCandIt; ++it)
-      if (it < nIt) n_gt += __popcll(__ballot(valid(it) && x[it] > tt));
-    const int need_eq = kk - n_gt;  // ties at tt, lowest indices first
-
-    int eq_before = 0, n_out = 0;
-#pragma unroll
-    for (int it = 0; it < kMaxCandIt; ++it) {
-      if (it < nIt) {
-        const bool v = valid(it);
-        const bool gt = v && x[it] > tt;
-        const bool eq = v && x[it] == tt;
-        const uint64_t eqm = __ballot(eq);
-        const bool sel = gt || (eq && eq_before + mask_rank(eqm) < need_eq);
-        eq_before += __popcll(eqm);
-        const uint64_t selm = __ballot(sel);
-        if (sel) {
-          const int pos = n_out + mask_rank(selm);
-          out[pos] = lo + it * 64 + lane;
-          if (out_s) out_s[pos] = __uint_as_float(x[it]);
-        }
-        n_out += __popcll(selm);
-      }
-    }
-    for (int e = kk + lane; e < s.topk; e += 64) {
-      out[e] = -1;
-      if (out_s) out_s[e] = 0.f;
-    }
+    return;
   }
+  const int nIt = (nC + 63) / 64;  // candidate slots per lane (<= 32)
+  if (nIt <= 1) topk_row<1>(sig + lo, nC, s.topk, lo, out, out_s, lane);
+  else if (nIt <= 2) topk_row<2>(sig + lo, nC, s.topk, lo, out, out_s, lane);
+  else if (nIt <= 4) topk_row<4>(sig + lo, nC, s.topk, lo, out, out_s, lane);
+  else if (nIt <= 8) topk_row<8>(sig + lo, nC, s.topk, lo, out, out_s, lane);
+  else if (nIt <= 16) topk_row<16>(sig + lo, nC, s.topk, lo, out, out_s, lane);
+  else topk_row<32>(sig + lo, nC, s.topk, lo, out, out_s, lane);
 }
 
 hipError_t launch_select_blocks(const uint16_t* q, const uint16_t* k_cmp, int32_t* blk_idx,
                                 float* blk_score, const AttnShape& s, hipStream_t stream) {
   if (s.B == 0 || s.S_q == 0) return hipSuccess;
-  dim3 grid((s.S_q + kSelWin - 1) / kSelWin, s.B * s.H_kv);
-  const size_t lds = static_cast<size_t>(kSelWin) * ((s.NB + 15) & ~15) * sizeof(float);
-  hipLaunchKernelGGL(select_blocks_kernel, grid, dim3(64 * kSelWaves), lds, stream, q, k_cmp, blk_idx,
-                     blk_score, s);
+  dim3 grid((s.S_q + kSelWaves - 1) / kSelWaves, s.B * s.H_kv);
+  // 64-block chunks where the LDS holds them, else 32 (NB <= 2048 fits)
+  if (select_lds<64>(s.NB) <= kSelLdsMax)
+    hipLaunchKernelGGL(select_blocks_kernel<64>, grid, dim3(64 * kSelWaves), select_lds<64>(s.NB), stream, q, k_cmp,
+                       blk_idx, blk_score, s);
+  else
+    hipLaunchKernelGGL(select_blocks_kernel<32>, grid, dim3(64 * kSelWaves), select_lds<32>(s.NB), stream, q, k_cmp,
+                       blk_idx, blk_score, s);
   return hipGetLastError();
 }
 
