@@ -42,7 +42,7 @@ namespace infv2 {
 // independent instruction stream).  Dense: 8 waves x 2 tokens (the 32 MFMA
 // columns).  Both cover a window of kWin = 16 tokens.
 template <bool DENSE> struct Cfg;
-template <> struct Cfg<false> { static constexpr int kWaves = 16, kTok = 1; };
+template <> struct Cfg<false> { static constexpr int kTok = 1, kWaves = 16; };
 template <> struct Cfg<true> { static constexpr int kWaves = 8, kTok = 2; };
 constexpr int kWin = 16;                          // tokens per workgroup
 constexpr int kRowBytes = kD * 2;                 // one K or V row in LDS
@@ -161,7 +161,6 @@ __host__ __device__ constexpr int padded_grid(int nwin, int nheads) {
 // Sparse: 16x16x32 MFMAs, one token per 16-column block (lane = head hl,
 // key quad gq).  MASK says which of the wave's tokens attend block j.
 // ---------------------------------------------------------------------------
-static_assert(Cfg<false>::kTok == 1, "one token per sparse wave");
 struct SparseState {
   bf16x8 qf[4];        // Q^T B operands, k-steps of 32 dims
   floatx4 o[8];        // O^T accumulators, 8 tiles of 16 dims
@@ -172,18 +171,19 @@ struct SparseState {
 // Per-lane LDS byte offsets of the sparse fragment reads within a stage:
 // K (A operand of S^T = K Q^T) for k-step ks at row hl (+16 rows per key
 // tile), and V (transposing reads, A operand of O^T += V^T P^T) for dim tile
-// dt at row 4*gq + hl/4 (+16 rows per half, +32 per k-step).
+// dt at row 4*gq + hl/4 (+16 rows per half, +32 per k-step).  The swizzle
+// is an XOR, so the offsets for k-step ks (dim tile dt) are the ks = 0
+// (dt = 0) offset XOR ks << 6 (dt << 5): one register each.
 struct SparseLane {
-  uint32_t k[4], v[8];
+  uint32_t k0, v0;
+  __device__ __forceinline__ uint32_t k(int ks) const { return k0 ^ static_cast<uint32_t>(ks << 6); }
+  __device__ __forceinline__ uint32_t v(int dt) const { return v0 ^ static_cast<uint32_t>(dt << 5); }
 };
 __device__ __forceinline__ SparseLane sparse_lane(int hl, int gq) {
   SparseLane o;
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) o.k[ks] = hl * kRowBytes + (((4 * ks + gq) ^ swz(hl)) << 4);
+  o.k0 = hl * kRowBytes + ((gq ^ swz(hl)) << 4);
   const int vr = 4 * gq + (hl >> 2);
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
-    o.v[dt] = vr * kRowBytes + (((2 * dt + ((hl & 3) >> 1)) ^ swz(vr)) << 4) + ((hl & 1) << 3);
+  o.v0 = vr * kRowBytes + ((((hl & 3) >> 1) ^ swz(vr)) << 4) + ((hl & 1) << 3);
   return o;
 }
 
@@ -202,7 +202,7 @@ __device__ __forceinline__ void sparse_step(SparseState& st, const SparseLane& l
     for (int ks = 0; ks < 4; ++ks) {
       bf16x8 kf[4];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) kf[kt] = as_bf16x8(load16(stg[n] + ln.k[ks] + kt * 16 * kRowBytes));
+      for (int kt = 0; kt < 4; ++kt) kf[kt] = as_bf16x8(load16(stg[n] + ln.k(ks) + kt * 16 * kRowBytes));
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
         sacc[n][kt] = mfma_16x16x32(kf[kt], st.qf[ks], ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : sacc[n][kt]);
@@ -264,7 +264,7 @@ __device__ __forceinline__ void sparse_step(SparseState& st, const SparseLane& l
         bf16x8 vf[4];
 #pragma unroll
         for (int dd = 0; dd < 4; ++dd) {
-          const unsigned char* p = stg[n] + kTileBytes + ln.v[d0 + dd] + s2 * 32 * kRowBytes;
+          const unsigned char* p = stg[n] + kTileBytes + ln.v(d0 + dd) + s2 * 32 * kRowBytes;
           vf[dd] = __builtin_shufflevector(lds_read_tr(p), lds_read_tr(p + 16 * kRowBytes), 0, 1, 2, 3, 4, 5, 6, 7);
         }
 #pragma unroll
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
   const float sl2 = s.scale_log2;
 
   // ---- per-token queries (the compiler waits for them once, in settle) -----
-  SparseState sp;
+  SparseState sp[T];  // sparse: one state per token of the wave
   DenseState dn;
   if constexpr (DENSE) {
     const int c32 = lane & 31, h2 = lane >> 5;
@@ -428,17 +428,24 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
     dn.lim = s.causal ? min(off + r, s.S_k - 1) : s.S_k - 1;
   } else {
     const int hl = lane & 15, gq = lane >> 4;
-    const bool valid = rw < s.S_q && hl < s.G;
-    const uint16_t* qrow = q + (static_cast<size_t>(b * s.H_q + g * s.G + hl) * s.S_q + rw) * kD + gq * 8;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) sp.qf[ks] = valid ? as_bf16x8(load16(qrow + ks * 32)) : bf16x8{};
+    for (int t = 0; t < T; ++t) {
+      const int r = rw + t;
+      const bool valid = r < s.S_q && hl < s.G;
+      const uint16_t* qrow = q + (static_cast<size_t>(b * s.H_q + g * s.G + hl) * s.S_q + r) * kD + gq * 8;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) sp.qf[ks] = settle(sp.qf[ks]);
+      for (int ks = 0; ks < 4; ++ks) sp[t].qf[ks] = valid ? as_bf16x8(load16(qrow + ks * 32)) : bf16x8{};
+    }
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) sp.o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    sp.m = -INFINITY;
-    sp.l = 0.f;
-    sp.lim = min(off + rw, s.S_k - 1);
+    for (int t = 0; t < T; ++t) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) sp[t].qf[ks] = settle(sp[t].qf[ks]);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) sp[t].o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      sp[t].m = -INFINITY;
+      sp[t].l = 0.f;
+      sp[t].lim = min(off + rw + t, s.S_k - 1);
+    }
   }
 
   // ---- the union of attended blocks ---------------------------------------
@@ -525,7 +532,6 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
     uint32_t nxt0 = __builtin_amdgcn_readfirstlane(seg_at(2)), nxt1 = __builtin_amdgcn_readfirstlane(seg_at(3));
     if (nseg > 0) stage_block(ring, kg, vg, cur0 & 0xffffu, s.S_k, dl, wave, lane);
     if (nseg > 1) stage_block(ring + kStageBytes, kg, vg, cur1 & 0xffffu, s.S_k, dl, wave, lane);
-    const uint32_t bit = 1u << (16 + wave);
     for (int pi = 0; pi < npair; ++pi) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();  // pair pi is in LDS; every wave is done with pair pi - 1
@@ -537,10 +543,14 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
       }
       const unsigned char* stg[2] = {smem + half * kStageBytes, smem + (half + 1) * kStageBytes};
       const int js[2] = {static_cast<int>(cur0 & 0xffffu), static_cast<int>(cur1 & 0xffffu)};
-      const bool m0 = (cur0 & bit) != 0u, m1 = (cur1 & bit) != 0u;   // cur1 = 0 past the list
-      if (m0 && m1) sparse_step<2>(sp, spl, stg, js, sl2, lane >> 4);
-      else if (m0) sparse_step<1>(sp, spl, stg, js, sl2, lane >> 4);
-      else if (m1) sparse_step<1>(sp, spl, stg + 1, js + 1, sl2, lane >> 4);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const uint32_t bit = 1u << (16 + wave * T + t);
+        const bool m0 = (cur0 & bit) != 0u, m1 = (cur1 & bit) != 0u;   // cur1 = 0 past the list
+        if (m0 && m1) sparse_step<2>(sp[t], spl, stg, js, sl2, lane >> 4);
+        else if (m0) sparse_step<1>(sp[t], spl, stg, js, sl2, lane >> 4);
+        else if (m1) sparse_step<1>(sp[t], spl, stg + 1, js + 1, sl2, lane >> 4);
+      }
       cur0 = nxt0;
       cur1 = nxt1;
       nxt0 = __builtin_amdgcn_readfirstlane(seg_at(2 * pi + 4));
@@ -570,32 +580,32 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
     }
   } else {
     const int hl = lane & 15, gq = lane >> 4;
-    const float l = sum_xor32(sum_xor16(sp.l));
-    if (s.nsplit > 1) {
-      // unnormalised partial state of this split, merged by combine_splits_kernel
-      if (rw < s.S_q && hl < s.G) {
-        const int h = g * s.G + hl;
-        float* pr = part + ((static_cast<size_t>(blockIdx.y) * s.B * s.H_q + b * s.H_q + h) * s.S_q + rw) * kPartFloats;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<floatx4*>(pr + 16 * dt + 4 * gq) = sp.o[dt];
+    for (int t = 0; t < T; ++t) {
+      const int r = rw + t;
+      const float l = sum_xor32(sum_xor16(sp[t].l));
+      if (r >= s.S_q || hl >= s.G) continue;
+      const int h = g * s.G + hl;
+      if (s.nsplit > 1) {
+        // unnormalised partial state of this split, merged by combine_splits_kernel
+        float* pr = part + ((static_cast<size_t>(blockIdx.y) * s.B * s.H_q + b * s.H_q + h) * s.S_q + r) * kPartFloats;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<floatx4*>(pr + 16 * dt + 4 * gq) = sp[t].o[dt];
         if (gq == 0) {
-          pr[128] = sp.m;
+          pr[128] = sp[t].m;
           pr[129] = l;
         }
+        continue;
       }
-      return;
-    }
-    if (rw < s.S_q && hl < s.G) {
-      const int h = g * s.G + hl;
       const float inv = 1.f / l;
-      uint16_t* orow = out + (static_cast<size_t>(b * s.H_q + h) * s.S_q + rw) * kD + 4 * gq;
+      uint16_t* orow = out + (static_cast<size_t>(b * s.H_q + h) * s.S_q + r) * kD + 4 * gq;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const u32x2 w = {pack_bf16x2(sp.o[dt][0] * inv, sp.o[dt][1] * inv),
-                         pack_bf16x2(sp.o[dt][2] * inv, sp.o[dt][3] * inv)};
+        const u32x2 w = {pack_bf16x2(sp[t].o[dt][0] * inv, sp[t].o[dt][1] * inv),
+                         pack_bf16x2(sp[t].o[dt][2] * inv, sp[t].o[dt][3] * inv)};
         *reinterpret_cast<u32x2*>(orow + 16 * dt) = w;
       }
-      if (lse && gq == 0) lse[static_cast<size_t>(b * s.H_q + h) * s.S_q + rw] = (sp.m + log2f(l)) * kLn2;
+      if (lse && gq == 0) lse[static_cast<size_t>(b * s.H_q + h) * s.S_q + r] = (sp[t].m + log2f(l)) * kLn2;
     }
   }
 }
