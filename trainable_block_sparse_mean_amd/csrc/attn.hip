@@ -8,17 +8,19 @@
 // of values).
 //
 // Work unit: one workgroup = one KV head of one batch entry x a window of
-// W = 16 consecutive query tokens; 8 waves (two per SIMD, so one wave's
-// matrix instructions overlap the other's softmax), each owning 2 tokens.
-// The G <= 16 query heads of the KV head share every K/V byte.
-//   * The workgroup builds the union of the blocks its tokens attend (a
-//     per-block bitmask of member tokens in LDS, compacted to an ascending
-//     list) and streams each block of the union once through LDS.
+// W = 16 consecutive query tokens.  Sparse: 16 waves of one token each (four
+// per SIMD, every member token an independent instruction stream).  Dense:
+// 8 waves of two tokens each.  The G <= 16 query heads of the KV head share
+// every K/V byte.
+//   * The sparse workgroup builds the union of the blocks its tokens attend
+//     (a per-block bitmask of member tokens in LDS, compacted to an ascending
+//     list) and streams each block of the union once through LDS, two blocks
+//     per barrier; few query windows (decode) split the list over several
+//     workgroups whose partial results a second kernel merges.
 //   * K and V blocks go global -> LDS with asynchronous direct-to-LDS loads
-//     (global_load_lds_dwordx4) into a 4-stage ring, three blocks ahead of
-//     the one being multiplied.  LDS rows are 256 bytes whose 16-byte chunks
-//     are permuted by a 4-bit bit reversal of the row, which keeps every
-//     fragment read pattern below free of bank conflicts.
+//     (global_load_lds_dwordx4) into a 4-stage ring.  LDS rows are 256 bytes
+//     whose 16-byte chunks are permuted by a linear swizzle of the row, which
+//     keeps every fragment read pattern below free of bank conflicts.
 //   * Scores are computed transposed, S^T = K Q^T (keys x heads): each lane
 //     then owns one head and a few keys, the row max needs only cross-lane
 //     swaps (v_permlane{16,32}_swap), and the softmax output is already the
@@ -30,7 +32,8 @@
 //   * Sparse: one token per MFMA column block (16x16x32 bf16, N = 16 heads),
 //     so a token that does not attend a block costs nothing.  Dense: every
 //     token attends every earlier block, so the two tokens of a wave share a
-//     32x32x16 bf16 MFMA (N = 2 tokens x 16 heads), the full-rate shape.
+//     32x32x16 bf16 MFMA (N = 2 tokens x 16 heads) and every K/V fragment
+//     read from LDS serves both.
 //   * Online softmax in log2 units; the running max only moves when a block
 //     max exceeds it by more than 2^8, so the O rescale is rare.
 #include "common.hpp"
