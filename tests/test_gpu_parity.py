@@ -87,6 +87,44 @@ def test_select_matches_oracle(name, w, rows):
     assert counts["near_tie"] <= 0.02 * sum(counts.values())
 
 
+def test_select_nonfinite_query_rows_stay_valid():
+    """NaN or Inf in a query makes that token's group scores NaN.  Its row must
+    still be a valid selection (the top-k keys clear the sign bit, so no row
+    can overflow), and every other row must be untouched.  The oracle has no
+    defined result for non-finite inputs, so poisoned rows are checked for
+    validity only."""
+    w = workloads.TINY.with_(H_q=32, H_kv=2, S_q=2048, S_k=2048, topk=12)
+    log("select non-finite", w)
+    x = gpu_inputs(w)
+    q_clean = x["q"].clone()
+    nan_rows, inf_rows = [100, 777, 1500, 2047], [300, 1800]
+    q = x["q"]
+    q[0, 3, nan_rows, 5] = float("nan")    # a head of KV group 0
+    q[0, 20, inf_rows, 0] = float("inf")   # a head of KV group 1
+    kc = tb.compress_k(x["k"])
+    idx = tb.select_blocks(q, kc, w.S_k, w.topk, w.n_init, w.n_local).cpu().numpy()
+    for r, g in [(r, 0) for r in nan_rows] + [(r, 1) for r in inf_rows]:
+        qb = (w.S_k - w.S_q + r) // 64
+        cand = set(range(w.n_init, qb - w.n_local + 1))
+        k = min(w.topk, len(cand))
+        row = list(idx[0, g, r])
+        assert all(j in cand for j in row[:k]) and row[:k] == sorted(set(row[:k])), (r, g, row)
+        assert row[k:] == [-1] * (w.topk - k), (r, g, row)
+    poisoned = set(nan_rows + inf_rows)
+    rows = np.array([r for r in range(0, w.S_q, 3) if r not in poisoned])
+    ref, scores = O.select_blocks(sparse_rows_q(q_clean, rows), np64(kc), w.S_k, w.topk, w.n_init, w.n_local, 64,
+                                  1 / math.sqrt(w.D), rows=rows, return_scores=True)
+    counts = check_selection(idx[:, :, rows], ref, scores, rows, w.S_q, w.S_k, w.topk, w.n_init, w.n_local)
+    log("  clean rows:", counts)
+    # the other KV group of a poisoned token is untouched too
+    for r, g_other in [(r, 1) for r in nan_rows] + [(r, 0) for r in inf_rows]:
+        one = np.array([r])
+        ref1, sc1 = O.select_blocks(sparse_rows_q(q_clean, one), np64(kc), w.S_k, w.topk, w.n_init, w.n_local, 64,
+                                    1 / math.sqrt(w.D), rows=one, return_scores=True)
+        check_selection(idx[:, g_other:g_other + 1, one], ref1[:, g_other:g_other + 1], {(0, 0, r): sc1[(0, g_other, r)]},
+                        one, w.S_q, w.S_k, w.topk, w.n_init, w.n_local)
+
+
 def test_select_all_ties_is_bit_exact():
     w = workloads.TINY.with_(H_q=32, H_kv=2, S_q=2048, S_k=2048, topk=12, values="constant_k")
     log("select ties", w)

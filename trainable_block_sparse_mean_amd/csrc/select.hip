@@ -64,8 +64,9 @@ __device__ __forceinline__ void lse_merge_row(float& m, float& l) {
 // in slot c / 64 of lane c % 64 (NS >= ceil(nC / 64) slots per lane).  Keys
 // are the fp32 bit patterns with the sign cleared: every key is below 2^31,
 // also for NaN scores (which order above +inf), and non-negative floats order
-// like their keys.  A bitwise radix search finds the kk-th largest key tt;
-// the keys above tt and the first (lowest-index) ties at tt are kept, written
+// like their keys.  A bitwise radix search finds a threshold tt: the kk-th
+// largest key, or any prefix of it at or below which exactly kk keys lie.
+// The keys above tt and the first (lowest-index) ties at tt are kept, written
 // to out[0 .. kk) in ascending index order (index = first + c).
 template <int NS>
 __device__ __forceinline__ void topk_row(const float* cand, int nC, int topk, int first, int32_t* out,
@@ -78,14 +79,19 @@ __device__ __forceinline__ void topk_row(const float* cand, int nC, int topk, in
     x[t] = c < nC ? __float_as_uint(cand[c]) & 0x7fffffffu : 0u;
   }
   // largest tt with #{x >= tt} >= kk (padding keys are 0 and never reach a
-  // candidate value, which has a bit set)
+  // candidate value, which has a bit set).  The search may stop as soon as
+  // exactly kk keys are >= the prefix found so far: those kk keys are then
+  // the selection, and the pass below keeps exactly them.
   uint32_t tt = 0;
   for (int bit = 30; bit >= 0; --bit) {
     const uint32_t cv = tt | (1u << bit);
     int cnt = 0;
 #pragma unroll
     for (int t = 0; t < NS; ++t) cnt += __popcll(__ballot(x[t] >= cv));
-    if (cnt >= kk) tt = cv;
+    if (cnt >= kk) {
+      tt = cv;
+      if (cnt == kk) break;
+    }
   }
   int n_gt = 0;
 #pragma unroll
