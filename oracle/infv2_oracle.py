@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for InfLLM-V2 dense-sparse switchable attention (forward).
+"""fp64 CPU oracle for InfLLM-V2 dense-sparse switchable attention (forward and
+the block-sparse attention backward).
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 execute this module: only the test suite, the smoke check and the benchmark's
@@ -10,7 +11,8 @@ pages, named in its docstring as  [page title, section].  The pages are:
   * "Infllm V2 Dense Sparse Switchable Attention" (skill page), with the
     sections Architecture Overview; Step 1: Dense Attention Layer Foundation;
     Step 2: Sparse Pattern Selection Module; Step 3: Switchable Attention with
-    Pattern Router; Practical Guidance (When NOT to Use, Common Pitfalls).
+    Pattern Router; Step 5: Training and Fine-tuning Procedure; Practical
+    Guidance (When NOT to Use, Common Pitfalls).
   * "InfLLM-V2: Dense-Sparse Switchable Attention for Seamless Short-to-Long
     Adaptation" (paper page), Abstract.
   * The InfLLM-V2 news summary (reportify), sections Model Advantages and
@@ -329,3 +331,66 @@ def attention(q, k, v, block_size: int, topk: int, n_init: int, n_local: int,
     idx = select_blocks(q, kc, S_k, topk, n_init, n_local, block_size, scale, rows=rows)
     o, l = sparse_attn(q, k, v, idx, block_size, n_init, n_local, scale, rows=rows)
     return dict(out=o, lse=l, path="sparse", blk_idx=idx, k_cmp_bits=bits)
+
+
+# ---------------------------------------------------------------------------
+# Backward of the block-sparse attention (next row: training)
+# ---------------------------------------------------------------------------
+
+
+def _softmax_attend_grad(qh: np.ndarray, kk: np.ndarray, vv: np.ndarray, do: np.ndarray,
+                         scale: float):
+    """Gradients of o = softmax(scale * q k^T) v for one token's head group.
+
+    [skill page, Step 5: Training and Fine-tuning Procedure]: the attention
+    is trained by back-propagating a loss through it; this is the chain rule
+    through the forward of [skill page, Step 1].  With p the softmax weights,
+    dp = dO v^T, and the softmax Jacobian dz = p * (dp - <dO, o>):
+    dq = scale * dz k,  dk = scale * dz^T q,  dv = p^T dO.
+    qh, do [G, D]; kk, vv [T, D].  Returns (dq [G, D], dk [T, D], dv [T, D]).
+    """
+    z = scale * (qh @ kk.T)                                   # [G, T]
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    o = p @ vv                                                # [G, D]
+    dp = do @ vv.T                                            # [G, T]
+    dz = p * (dp - (do * o).sum(axis=1, keepdims=True))
+    return scale * (dz @ kk), scale * (dz.T @ qh), p.T @ do
+
+
+def sparse_attn_bwd(q, k, v, dout, blk_idx, block_size: int, n_init: int, n_local: int,
+                    scale: float):
+    """Gradients of the block-sparse attention with respect to q, k and v.
+
+    [skill page, Step 5: Training and Fine-tuning Procedure] applied to the
+    attention of ``sparse_attn``: the attended key set of each query is the
+    same (forced blocks, selected blocks, causal inside a block), and the
+    selection itself is a discrete choice with no gradient, so gradients flow
+    only through the attention over that set.  The key and value gradients
+    of a KV head sum over every query token and every head of its group that
+    attends the key.
+
+    q, dout [B,H_q,S_q,D]; k, v [B,H_kv,S_k,D]; blk_idx int [B,H_kv,S_q,topk].
+    Returns (dq [B,H_q,S_q,D], dk [B,H_kv,S_k,D], dv [B,H_kv,S_k,D]).
+    """
+    B, H_q, S_q, D = q.shape
+    H_kv, S_k = k.shape[1], k.shape[2]
+    G = H_q // H_kv
+    off = S_k - S_q
+    dq = np.zeros_like(q, dtype=np.float64)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for b in range(B):
+        for g in range(H_kv):
+            hs = slice(g * G, (g + 1) * G)
+            for r in range(S_q):
+                i = off + r
+                sel = [int(j) for j in blk_idx[b, g, r] if j >= 0]
+                t = attend_keys(i, forced_blocks(i, block_size, n_init, n_local) + sel, block_size, S_k)
+                gq, gk, gv = _softmax_attend_grad(q[b, hs, r, :], k[b, g, t, :], v[b, g, t, :],
+                                                  dout[b, hs, r, :], scale)
+                dq[b, hs, r, :] = gq
+                dk[b, g, t, :] += gk
+                dv[b, g, t, :] += gv
+    return dq, dk, dv
+

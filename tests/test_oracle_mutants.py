@@ -74,6 +74,25 @@ def _softmax_attend_no_max_in_lse(qh, kk, vv, scale):
     return (w / l) @ vv, np.log(l)[:, 0]
 
 
+def _grad_no_rowsum_term(qh, kk, vv, do, scale):
+    z = scale * (qh @ kk.T)
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    dz = p * (do @ vv.T)                                   # softmax Jacobian without -<dO, o>
+    return scale * (dz @ kk), scale * (dz.T @ qh), p.T @ do
+
+
+def _grad_dk_unscaled(qh, kk, vv, do, scale):
+    dq, dk, dv = impl.__dict__["_real_grad"](qh, kk, vv, do, scale)
+    return dq, dk / scale, dv
+
+
+def _grad_dv_unnormalised(qh, kk, vv, do, scale):
+    dq, dk, _ = impl.__dict__["_real_grad"](qh, kk, vv, do, scale)
+    z = scale * (qh @ kk.T)
+    return dq, dk, np.exp(z - z.max(axis=1, keepdims=True)).T @ do
+
+
 MUTANTS = [
     ("group_scores", _scores_no_normalisation, [pins.test_scores_sum_to_group_size_and_nonnegative,
                                                 pins.test_scores_hand_derived_golden]),
@@ -85,11 +104,18 @@ MUTANTS = [
     ("compress_k", _compress_divide_by_count, [pins.test_compress_tail_zero_padded_divides_by_block_size]),
     ("f64_to_bf16", _bf16_truncate, [pins.test_bf16_rounding_hand_cases]),
     ("_softmax_attend", _softmax_attend_no_max_in_lse, [pins.test_dense_matches_torch_sdpa_fp64]),
+    ("_softmax_attend_grad", _grad_no_rowsum_term, [pins.test_backward_sum_invariants,
+                                                    pins.test_backward_dense_case_matches_torch_autograd_fp64]),
+    ("_softmax_attend_grad", _grad_dk_unscaled, [pins.test_backward_matches_finite_differences_of_the_forward,
+                                                 pins.test_backward_dense_case_matches_torch_autograd_fp64]),
+    ("_softmax_attend_grad", _grad_dv_unnormalised, [pins.test_backward_sum_invariants,
+                                                     pins.test_backward_dense_case_matches_torch_autograd_fp64]),
 ]
 
 
 @pytest.mark.parametrize("name,mutant,catchers", MUTANTS, ids=[m[0] + ":" + m[1].__name__ for m in MUTANTS])
 def test_pin_catches_mutant(monkeypatch, name, mutant, catchers):
+    monkeypatch.setattr(impl, "_real_grad", impl._softmax_attend_grad, raising=False)
     monkeypatch.setattr(impl, name, mutant)
     for pin in catchers:
         with pytest.raises(AssertionError):

@@ -456,3 +456,74 @@ def test_scores_group_uses_its_consecutive_heads_only():
         q3 = q.copy()
         q3[0, g * G] = rnd_bf16(rng, 1, D)
         assert not np.array_equal(O.group_scores(q3, kc, 0, g, i, 0, G, 0.7, 64), a)
+
+
+# --------------------------------------------------- backward (training) ----
+
+def _bwd_case(rng, B=1, G=2, H_kv=2, S=150, D=8, topk=1):
+    q = rnd_bf16(rng, B, G * H_kv, S, D)
+    k = rnd_bf16(rng, B, H_kv, S, D)
+    v = rnd_bf16(rng, B, H_kv, S, D)
+    do = rng.standard_normal((B, G * H_kv, S, D))
+    # arbitrary selections (duplicates, forced blocks and -1 gaps allowed)
+    idx = rng.integers(-1, (S + 63) // 64, size=(B, H_kv, S, topk))
+    return q, k, v, do, idx
+
+
+def test_backward_matches_finite_differences_of_the_forward():
+    """Central differences of L = <dO, sparse_attn(q, k, v)>, entry by entry."""
+    rng = np.random.default_rng(31)
+    q, k, v, do, idx = _bwd_case(rng)
+    scale = 0.3
+    dq, dk, dv = O.sparse_attn_bwd(q, k, v, do, idx, 64, 1, 2, scale)
+
+    def loss(q_, k_, v_):
+        out, _ = O.sparse_attn(q_, k_, v_, idx, 64, 1, 2, scale)
+        return float((out * do).sum())
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(12):
+            pos = tuple(int(rng.integers(0, n)) for n in x.shape)
+            xp, xm = x.copy(), x.copy()
+            xp[pos] += h
+            xm[pos] -= h
+            args_p = dict(q=q, k=k, v=v); args_p[name] = xp
+            args_m = dict(q=q, k=k, v=v); args_m[name] = xm
+            num = (loss(args_p["q"], args_p["k"], args_p["v"]) - loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * h)
+            assert abs(num - g[pos]) <= 1e-6 * max(1.0, abs(num)), (name, pos, num, g[pos])
+
+
+def test_backward_dense_case_matches_torch_autograd_fp64():
+    """topk covering every candidate makes the sparse attention dense and
+    causal; its gradients then equal torch autograd through SDPA in fp64."""
+    rng = np.random.default_rng(32)
+    G, H_kv, S, D = 2, 2, 200, 16
+    q, k, v, do, _ = _bwd_case(rng, G=G, H_kv=H_kv, S=S, D=D)
+    nb = (S + 63) // 64
+    idx = np.tile(np.arange(nb), (1, H_kv, S, 1))
+    dq, dk, dv = O.sparse_attn_bwd(q, k, v, do, idx, 64, 1, 2, 0.25)
+    tq = torch.from_numpy(q).requires_grad_()
+    tk = torch.from_numpy(k).requires_grad_()
+    tv = torch.from_numpy(v).requires_grad_()
+    out = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk.repeat_interleave(G, dim=1), tv.repeat_interleave(G, dim=1),
+        attn_mask=torch.ones(S, S, dtype=torch.bool).tril(), scale=0.25)
+    out.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_backward_sum_invariants():
+    """Softmax weights sum to one: the key gradients of a KV head sum to zero
+    over keys, and its value gradients sum to the output gradients of its
+    heads summed over tokens."""
+    rng = np.random.default_rng(33)
+    G, H_kv = 4, 2
+    q, k, v, do, idx = _bwd_case(rng, G=G, H_kv=H_kv, S=300, D=8, topk=2)
+    _, dk, dv = O.sparse_attn_bwd(q, k, v, do, idx, 64, 1, 2, 0.3)
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-11)
+    want = do.reshape(1, H_kv, G, 300, 8).sum(axis=(2, 3))
+    np.testing.assert_allclose(dv.sum(axis=2), want, rtol=1e-11, atol=1e-11)
+
