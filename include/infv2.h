@@ -31,7 +31,9 @@
  *  - Return value: INFV2_OK or an error code.  All argument checks run before
  *    any HIP call; on an error nothing is launched and outputs are untouched.
  *    Supported on the GPU: D = 128, block_size = 64, 1 <= G <= 16,
- *    0 <= topk <= 256; other values give INFV2_ERR_UNSUPPORTED.
+ *    0 <= topk <= 256, and at most 4096 key blocks (S_k <= 262144) for the
+ *    sparse forward and backward (2048 for the block selection); other
+ *    values give INFV2_ERR_UNSUPPORTED.
  *  - The library keeps no state between calls; calls on distinct streams
  *    with distinct outputs and workspaces are independent.
  */
@@ -120,6 +122,41 @@ size_t infv2_sparse_workspace_bytes(int B, int H_q, int H_kv, int S_q, int S_k,
                                     int D, int block_size, int topk);
 int infv2_sparse_attn_fwd(const void* q, const void* k, const void* v,
                           const int32_t* blk_idx, void* out, float* lse,
+                          int B, int H_q, int H_kv, int S_q, int S_k, int D,
+                          int block_size, int topk, int n_init, int n_local,
+                          float softmax_scale,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Block-sparse attention backward (skill page, Step 5: Training and
+ * Fine-tuning Procedure: the attention is trained by back-propagation).
+ * Gradients of the attention of infv2_sparse_attn_fwd with respect to q, k
+ * and v, over the same attended key sets; the block selection carries no
+ * gradient.
+ *   q, out, dout  bf16 [B][H_q][S_q][D]    (forward input, forward output,
+ *                                           gradient of the output)
+ *   k, v          bf16 [B][H_kv][S_k][D]
+ *   lse           fp32 [B][H_q][S_q]       (required: the forward's natural-log
+ *                                           log-sum-exp)
+ *   blk_idx       int32 [B][H_kv][S_q][topk] (as for the forward)
+ *   dq            bf16 [B][H_q][S_q][D]    (output)
+ *   dk, dv        bf16 [B][H_kv][S_k][D]   (output, overwritten; keys no query
+ *                                           attends get 0)
+ * With P the softmax weights, D = <dout, out> per (token, head) and
+ * dS = P * (dout v^T - D):  dq = scale dS k,  dk = scale sum dS^T q,
+ * dv = sum P^T dout, the sums over every (token, head of the group) that
+ * attends the key.  Accumulation is fp32, each output rounded once to bf16;
+ * the result does not depend on scheduling (no atomics on gradients).
+ * workspace: at least infv2_sparse_bwd_workspace_bytes(...) bytes, 256-byte
+ * aligned, contents on entry irrelevant (4 bytes per query row and head, plus
+ * one bit per KV head, block and query token).  S_q = 0 needs none and writes
+ * zero dk, dv.
+ */
+size_t infv2_sparse_bwd_workspace_bytes(int B, int H_q, int H_kv, int S_q, int S_k,
+                                        int D, int block_size, int topk);
+int infv2_sparse_attn_bwd(const void* q, const void* k, const void* v,
+                          const void* out, const float* lse, const void* dout,
+                          const int32_t* blk_idx, void* dq, void* dk, void* dv,
                           int B, int H_q, int H_kv, int S_q, int S_k, int D,
                           int block_size, int topk, int n_init, int n_local,
                           float softmax_scale,

@@ -339,7 +339,7 @@ def attention(q, k, v, block_size: int, topk: int, n_init: int, n_local: int,
 
 
 def _softmax_attend_grad(qh: np.ndarray, kk: np.ndarray, vv: np.ndarray, do: np.ndarray,
-                         scale: float):
+                         scale: float, magnitudes: bool = False):
     """Gradients of o = softmax(scale * q k^T) v for one token's head group.
 
     [skill page, Step 5: Training and Fine-tuning Procedure]: the attention
@@ -348,18 +348,26 @@ def _softmax_attend_grad(qh: np.ndarray, kk: np.ndarray, vv: np.ndarray, do: np.
     dp = dO v^T, and the softmax Jacobian dz = p * (dp - <dO, o>):
     dq = scale * dz k,  dk = scale * dz^T q,  dv = p^T dO.
     qh, do [G, D]; kk, vv [T, D].  Returns (dq [G, D], dk [T, D], dv [T, D]).
+    With ``magnitudes`` it also returns the same sums taken over absolute
+    values, with |dz| replaced by p * (|dp| + |<dO, o>|): the size of the
+    terms a rounded computation adds up (a scale for its rounding error).
     """
     z = scale * (qh @ kk.T)                                   # [G, T]
     p = np.exp(z - z.max(axis=1, keepdims=True))
     p /= p.sum(axis=1, keepdims=True)
     o = p @ vv                                                # [G, D]
     dp = do @ vv.T                                            # [G, T]
-    dz = p * (dp - (do * o).sum(axis=1, keepdims=True))
-    return scale * (dz @ kk), scale * (dz.T @ qh), p.T @ do
+    d = (do * o).sum(axis=1, keepdims=True)
+    dz = p * (dp - d)
+    grads = (scale * (dz @ kk), scale * (dz.T @ qh), p.T @ do)
+    if not magnitudes:
+        return grads
+    mz = p * (np.abs(dp) + np.abs(d))
+    return grads + (scale * (mz @ np.abs(kk)), scale * (mz.T @ np.abs(qh)), p.T @ np.abs(do))
 
 
 def sparse_attn_bwd(q, k, v, dout, blk_idx, block_size: int, n_init: int, n_local: int,
-                    scale: float):
+                    scale: float, magnitudes: bool = False):
     """Gradients of the block-sparse attention with respect to q, k and v.
 
     [skill page, Step 5: Training and Fine-tuning Procedure] applied to the
@@ -371,15 +379,17 @@ def sparse_attn_bwd(q, k, v, dout, blk_idx, block_size: int, n_init: int, n_loca
     attends the key.
 
     q, dout [B,H_q,S_q,D]; k, v [B,H_kv,S_k,D]; blk_idx int [B,H_kv,S_q,topk].
-    Returns (dq [B,H_q,S_q,D], dk [B,H_kv,S_k,D], dv [B,H_kv,S_k,D]).
+    Returns (dq [B,H_q,S_q,D], dk [B,H_kv,S_k,D], dv [B,H_kv,S_k,D]), and with
+    ``magnitudes`` also the absolute-value sums of _softmax_attend_grad in
+    the same shapes.
     """
     B, H_q, S_q, D = q.shape
     H_kv, S_k = k.shape[1], k.shape[2]
     G = H_q // H_kv
     off = S_k - S_q
-    dq = np.zeros_like(q, dtype=np.float64)
-    dk = np.zeros(k.shape)
-    dv = np.zeros(v.shape)
+    res = [np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)]
+    if magnitudes:
+        res += [np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)]
     for b in range(B):
         for g in range(H_kv):
             hs = slice(g * G, (g + 1) * G)
@@ -387,10 +397,11 @@ def sparse_attn_bwd(q, k, v, dout, blk_idx, block_size: int, n_init: int, n_loca
                 i = off + r
                 sel = [int(j) for j in blk_idx[b, g, r] if j >= 0]
                 t = attend_keys(i, forced_blocks(i, block_size, n_init, n_local) + sel, block_size, S_k)
-                gq, gk, gv = _softmax_attend_grad(q[b, hs, r, :], k[b, g, t, :], v[b, g, t, :],
-                                                  dout[b, hs, r, :], scale)
-                dq[b, hs, r, :] = gq
-                dk[b, g, t, :] += gk
-                dv[b, g, t, :] += gv
-    return dq, dk, dv
+                parts = _softmax_attend_grad(q[b, hs, r, :], k[b, g, t, :], v[b, g, t, :],
+                                             dout[b, hs, r, :], scale, magnitudes)
+                for n in range(0, len(res), 3):
+                    res[n][b, hs, r, :] = parts[n]
+                    res[n + 1][b, g, t, :] += parts[n + 1]
+                    res[n + 2][b, g, t, :] += parts[n + 2]
+    return tuple(res)
 

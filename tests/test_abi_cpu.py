@@ -32,7 +32,7 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ["infv2_compress_k", "infv2_select_blocks", "infv2_sparse_attn_fwd", "infv2_dense_attn_fwd",
-              "infv2_attn_fwd", "infv2_status_string"]:
+              "infv2_attn_fwd", "infv2_sparse_attn_bwd", "infv2_status_string"]:
         assert n in names
 
 
@@ -137,3 +137,49 @@ def test_binding_raises_when_library_missing(tmp_path, monkeypatch):
     monkeypatch.setattr(tb, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         tb.load_library(str(tmp_path / "nope.so"))
+
+
+def _bwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, dout=FAKE, idx=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1,
+             H_q=32, H_kv=2, S_q=128, S_k=128, D=128, bs=64, topk=4, n_init=1, n_local=2, scale=0.0, ws=FAKE,
+             wsb=0, stream=None)
+    a.update(kw)
+    return lib.infv2_sparse_attn_bwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["dout"], a["idx"], a["dq"],
+                                     a["dk"], a["dv"], a["B"], a["H_q"], a["H_kv"], a["S_q"], a["S_k"], a["D"],
+                                     a["bs"], a["topk"], a["n_init"], a["n_local"], a["scale"], a["ws"], a["wsb"],
+                                     a["stream"])
+
+
+@no_gpu
+def test_backward_validation_codes():
+    lib = tb.load_library()
+    assert _bwd(lib, H_q=31) == tb.ERR_INVALID                 # H_q % H_kv
+    assert _bwd(lib, S_q=129) == tb.ERR_INVALID                # S_q > S_k
+    assert _bwd(lib, n_local=0) == tb.ERR_INVALID
+    assert _bwd(lib, lse=None) == tb.ERR_INVALID               # the forward's lse is required
+    assert _bwd(lib, dout=FAKE_MIS) == tb.ERR_INVALID
+    assert _bwd(lib, dk=None) == tb.ERR_INVALID
+    assert _bwd(lib, D=64) == tb.ERR_UNSUPPORTED
+    assert _bwd(lib, H_q=64, H_kv=2) == tb.ERR_UNSUPPORTED      # G = 32 > 16
+    assert _bwd(lib, S_q=10, S_k=4096 * 64 + 1) == tb.ERR_UNSUPPORTED   # more key blocks than LDS holds
+    assert _bwd(lib, ws=None) == tb.ERR_WORKSPACE
+    assert _bwd(lib, wsb=1024) == tb.ERR_WORKSPACE
+    assert _bwd(lib, B=0) == tb.OK                             # nothing to write
+
+
+def test_backward_workspace_sizes():
+    lib = tb.load_library()
+    # D (4 bytes per row and head, rounded to 256) + one bit per (KV head, block, token)
+    # (rounded to 256) + fp32 dk/dv partials of 4 token pieces per block from 3 * 4096 queries on
+    assert lib.infv2_sparse_bwd_workspace_bytes(1, 32, 2, 32768, 32768, 128, 64, 64) == \
+        32 * 32768 * 4 + 2 * 512 * 1024 * 4 + 2 * 512 * 4 * (2 * 64 * 128 * 4)
+    assert lib.infv2_sparse_bwd_workspace_bytes(2, 6, 3, 37, 1000, 128, 64, 5) == \
+        ((2 * 6 * 37 * 4 + 255) // 256) * 256 + 2 * 3 * 16 * 2 * 4
+    assert lib.infv2_sparse_bwd_workspace_bytes(1, 32, 2, 10, 10, 64, 64, 4) == 0   # unsupported D
+
+
+@no_gpu
+def test_sparse_block_limit_is_what_lds_holds():
+    lib = tb.load_library()
+    assert _sparse(lib, S_q=10, S_k=4096 * 64 + 1) == tb.ERR_UNSUPPORTED
+

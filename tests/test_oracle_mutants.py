@@ -74,7 +74,7 @@ def _softmax_attend_no_max_in_lse(qh, kk, vv, scale):
     return (w / l) @ vv, np.log(l)[:, 0]
 
 
-def _grad_no_rowsum_term(qh, kk, vv, do, scale):
+def _grad_no_rowsum_term(qh, kk, vv, do, scale, magnitudes=False):
     z = scale * (qh @ kk.T)
     p = np.exp(z - z.max(axis=1, keepdims=True))
     p /= p.sum(axis=1, keepdims=True)
@@ -82,12 +82,12 @@ def _grad_no_rowsum_term(qh, kk, vv, do, scale):
     return scale * (dz @ kk), scale * (dz.T @ qh), p.T @ do
 
 
-def _grad_dk_unscaled(qh, kk, vv, do, scale):
+def _grad_dk_unscaled(qh, kk, vv, do, scale, magnitudes=False):
     dq, dk, dv = impl.__dict__["_real_grad"](qh, kk, vv, do, scale)
     return dq, dk / scale, dv
 
 
-def _grad_dv_unnormalised(qh, kk, vv, do, scale):
+def _grad_dv_unnormalised(qh, kk, vv, do, scale, magnitudes=False):
     dq, dk, _ = impl.__dict__["_real_grad"](qh, kk, vv, do, scale)
     z = scale * (qh @ kk.T)
     return dq, dk, np.exp(z - z.max(axis=1, keepdims=True)).T @ do

@@ -33,6 +33,8 @@ SIGNATURES = {
     "infv2_select_blocks": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 10 + [_c_float, _vp]),
     "infv2_sparse_workspace_bytes": (_c_size, [_c_int] * 8),
     "infv2_sparse_attn_fwd": (_c_int, [_vp] * 6 + [_c_int] * 10 + [_c_float, _vp, _c_size, _vp]),
+    "infv2_sparse_bwd_workspace_bytes": (_c_size, [_c_int] * 8),
+    "infv2_sparse_attn_bwd": (_c_int, [_vp] * 10 + [_c_int] * 10 + [_c_float, _vp, _c_size, _vp]),
     "infv2_dense_workspace_bytes": (_c_size, [_c_int] * 6),
     "infv2_dense_attn_fwd": (_c_int, [_vp] * 5 + [_c_int] * 6 + [_c_float, _c_int, _vp, _c_size, _vp]),
     "infv2_attn_workspace_bytes": (_c_size, [_c_int] * 9),
@@ -141,6 +143,29 @@ def sparse_attn_fwd(q, k, v, blk_idx, n_init: int = 1, n_local: int = 2, softmax
           B, H_q, H_kv, S_q, S_k, D, block_size, topk, n_init, n_local, _scale(softmax_scale),
           _ptr(ws), ws.numel(), _stream())
     return out, lse
+
+
+def sparse_attn_bwd(q, k, v, out, lse, dout, blk_idx, n_init: int = 1, n_local: int = 2, softmax_scale=None,
+                    block_size: int = 64):
+    """Gradients of sparse_attn_fwd with respect to q, k, v, given the forward's
+    output and log-sum-exp and the gradient of the output.
+    Returns (dq bf16 [B,H_q,S_q,D], dk, dv bf16 [B,H_kv,S_k,D])."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _need(t, n, torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    _need(blk_idx, "blk_idx", torch.int32, 4)
+    B, H_q, S_q, D = q.shape
+    H_kv, S_k = k.shape[1], k.shape[2]
+    topk = blk_idx.shape[3]
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    nbytes = load_library().infv2_sparse_bwd_workspace_bytes(B, H_q, H_kv, S_q, S_k, D, block_size, topk)
+    ws = _workspace(nbytes, q.device)
+    _call("infv2_sparse_attn_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(blk_idx),
+          _ptr(dq), _ptr(dk), _ptr(dv), B, H_q, H_kv, S_q, S_k, D, block_size, topk, n_init, n_local,
+          _scale(softmax_scale), _ptr(ws), ws.numel(), _stream())
+    return dq, dk, dv
 
 
 def dense_attn_fwd(q, k, v, causal: bool = True, softmax_scale=None, return_lse: bool = True):

@@ -14,7 +14,9 @@ namespace {
 constexpr int kAbiVersion = 1;
 constexpr int kMaxTopk = 256;
 constexpr int kMaxSelectBlocks = 2048;  // select keeps each token's scores in LDS
-constexpr int kMaxSparseBlocks = 8192;  // sparse keeps a per-block member mask in LDS
+// the sparse kernels keep a member mask and a list entry (8 bytes) per key
+// block in LDS beside the 128 KB K/V ring: 160 KB holds 4096 of them
+constexpr int kMaxSparseBlocks = 4096;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -144,6 +146,44 @@ int infv2_sparse_attn_fwd(const void* q, const void* k, const void* v, const int
   return hip_status(infv2::launch_sparse_attn(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
       blk_idx, static_cast<uint16_t*>(out), lse, s, workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t infv2_sparse_bwd_workspace_bytes(int B, int H_q, int H_kv, int S_q, int S_k, int D, int block_size,
+                                        int topk) {
+  if (check_shape(B, H_q, H_kv, S_q, S_k, D) != INFV2_OK) return 0;
+  if (check_sparse_params(block_size, topk, 0, 1) != INFV2_OK) return 0;
+  const AttnShape s = make_shape(B, H_q, H_kv, S_q, S_k, block_size, topk, 0, 1, 1.f, 1);
+  return round_up(infv2::attn_bwd_workspace_bytes(s), 256);
+}
+
+int infv2_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                          const void* dout, const int32_t* blk_idx, void* dq, void* dk, void* dv, int B, int H_q,
+                          int H_kv, int S_q, int S_k, int D, int block_size, int topk, int n_init, int n_local,
+                          float softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(B, H_q, H_kv, S_q, S_k, D);
+  if (st != INFV2_OK) return st;
+  st = check_sparse_params(block_size, topk, n_init, n_local);
+  if (st != INFV2_OK) return st;
+  if (num_blocks(S_k, block_size) > kMaxSparseBlocks) return INFV2_ERR_UNSUPPORTED;
+  if (B == 0 || S_k == 0) return INFV2_OK;  // no key: nothing to write
+  if (!tensor_ok(dk) || !tensor_ok(dv)) return INFV2_ERR_INVALID;
+  if (S_q > 0) {
+    if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(out) || !tensor_ok(dout) ||
+        !tensor_ok(dq) || !tensor_ok(lse))
+      return INFV2_ERR_INVALID;
+    if (topk > 0 && !tensor_ok(blk_idx)) return INFV2_ERR_INVALID;
+    const size_t need = infv2_sparse_bwd_workspace_bytes(B, H_q, H_kv, S_q, S_k, D, block_size, topk);
+    if (workspace == nullptr || workspace_bytes < need) return INFV2_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return INFV2_ERR_INVALID;
+  }
+  const float sc = softmax_scale > 0.f ? softmax_scale : 1.f / sqrtf(static_cast<float>(D));
+  const AttnShape s = make_shape(B, H_q, H_kv, S_q, S_k, block_size, topk, n_init, n_local,
+                                 sc * infv2::kLog2e, 1);
+  return hip_status(infv2::launch_sparse_attn_bwd(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+      static_cast<const uint16_t*>(out), lse, static_cast<const uint16_t*>(dout), blk_idx,
+      static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), s, sc, workspace,
+      static_cast<hipStream_t>(stream)));
 }
 
 size_t infv2_dense_workspace_bytes(int B, int H_q, int H_kv, int S_q, int S_k, int D) {

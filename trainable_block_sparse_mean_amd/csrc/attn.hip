@@ -36,8 +36,7 @@
 //     read from LDS serves both.
 //   * Online softmax in log2 units; the running max only moves when a block
 //     max exceeds it by more than 2^8, so the O rescale is rare.
-#include "common.hpp"
-#include "kernels.hpp"
+#include "attn_common.hpp"
 
 namespace infv2 {
 
@@ -47,117 +46,8 @@ namespace infv2 {
 template <bool DENSE> struct Cfg;
 template <> struct Cfg<false> { static constexpr int kTok = 1, kWaves = 16; };
 template <> struct Cfg<true> { static constexpr int kWaves = 8, kTok = 2; };
-constexpr int kWin = 16;                          // tokens per workgroup
-constexpr int kRowBytes = kD * 2;                 // one K or V row in LDS
-constexpr int kTileBytes = kBS * kRowBytes;       // one 64-key block of K (or V)
-constexpr int kStageBytes = 2 * kTileBytes;       // K + V of one block
-constexpr int kStages = 4;                        // LDS ring: 3 blocks in flight
-constexpr int kXcds = 8;                          // workgroups are dealt round-robin to 8 XCDs
-constexpr int kXcdGroup = 32;                     // windows kept together on one XCD (one per CU)
 constexpr float kRescaleSlack = 8.f;              // log2 units the running max may lag behind
 
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-
-__device__ __forceinline__ bf16x4 lds_read_tr(const unsigned char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
-}
-
-__device__ __forceinline__ floatx16 mfma_32x32x16(bf16x8 a, bf16x8 b, floatx16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-
-// Wait until at most `in_flight` later blocks' loads of this wave are
-// pending; each block is `per_block` loads per wave.
-template <int per_block>
-__device__ __forceinline__ void wait_dma(int in_flight) {
-  static_assert(per_block == 2 || per_block == 4, "vmcnt immediates below");
-  if (in_flight >= 2) {
-    if constexpr (per_block == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  } else if (in_flight == 1) {
-    if constexpr (per_block == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-}
-
-// Per-lane byte offsets, within a 64-key block, of the 16-byte chunks this
-// lane moves.  A tile (K or V of one block) is 16 chunks of 4 rows (1 KB =
-// 64 lanes x 16 B per load); each of the WAVES waves moves 16 / WAVES of
-// them for K and as many for V.  A full block needs no clamping; in a
-// partial last block, rows past S_k - 1 re-read row S_k - 1 (finite, masked).
-template <int WAVES>
-struct DmaLane {
-  static constexpr int kChunks = 16 / WAVES;
-  uint32_t off[kChunks];
-};
-template <int WAVES>
-__device__ __forceinline__ DmaLane<WAVES> dma_lane(int wave, int lane) {
-  DmaLane<WAVES> d;
-  const int sub = lane >> 4, slot = lane & 15;
-#pragma unroll
-  for (int n = 0; n < DmaLane<WAVES>::kChunks; ++n) {
-    const int row = (wave * DmaLane<WAVES>::kChunks + n) * 4 + sub;
-    d.off[n] = static_cast<uint32_t>(row * kRowBytes + ((slot ^ swz(row)) << 4));
-  }
-  return d;
-}
-
-// Issue the loads of key block j into one stage of the ring.
-template <int WAVES>
-__device__ __forceinline__ void stage_block(uint32_t stage_lds, const uint16_t* kg, const uint16_t* vg, int j,
-                                            int S_k, const DmaLane<WAVES>& d, int wave, int lane) {
-  constexpr int C = DmaLane<WAVES>::kChunks;
-  const char* kb = reinterpret_cast<const char*>(kg) + static_cast<size_t>(j) * kTileBytes;
-  const char* vb = reinterpret_cast<const char*>(vg) + static_cast<size_t>(j) * kTileBytes;
-  if (j * kBS + kBS <= S_k) {
-#pragma unroll
-    for (int n = 0; n < C; ++n) {
-      const uint32_t lds = stage_lds + (wave * C + n) * 1024;
-      dma16(kb, d.off[n], lds);
-      dma16(vb, d.off[n], lds + kTileBytes);
-    }
-  } else {
-    const int sub = lane >> 4, slot = lane & 15;
-#pragma unroll
-    for (int n = 0; n < C; ++n) {
-      const int row = (wave * C + n) * 4 + sub;
-      const int crow = min(row, S_k - 1 - j * kBS);
-      const uint32_t off = static_cast<uint32_t>(crow * kRowBytes + ((slot ^ swz(row)) << 4));
-      const uint32_t lds = stage_lds + (wave * C + n) * 1024;
-      dma16(kb, off, lds);
-      dma16(vb, off, lds + kTileBytes);
-    }
-  }
-}
-
-// Workgroup -> (KV head, window).  The hardware deals workgroups to the XCDs
-// round-robin; this maps the k-th workgroup of every XCD so that each XCD
-// runs groups of `gs` (<= kXcdGroup) adjacent windows of one KV head
-// together (they stream the same K/V blocks through that XCD's L2), latest
-// (heaviest) windows first.  Returns false for padding workgroups.
-__host__ __device__ constexpr int xcd_group(int nwin) { return nwin < kXcdGroup ? nwin : kXcdGroup; }
-
-__device__ __forceinline__ bool map_window(int n, int nwin, int nheads, int& head, int& win) {
-  const int gs = xcd_group(nwin);
-  const int xcd = n % kXcds, k = n / kXcds;
-  const int rank = (k / gs) * kXcds + xcd;  // index of a group of gs windows
-  const int ngrp = (nwin + gs - 1) / gs;
-  head = rank % nheads;
-  const int grp = ngrp - 1 - rank / nheads;
-  win = grp * gs + (k % gs);
-  return grp >= 0 && win < nwin;
-}
-
-__host__ __device__ constexpr int padded_grid(int nwin, int nheads) {
-  // ranks needed: ngrp * nheads, rounded up to whole rounds of kXcds
-  return ((((nwin + xcd_group(nwin) - 1) / xcd_group(nwin)) * nheads + kXcds - 1) / kXcds) * kXcds *
-         xcd_group(nwin);
-}
 
 
 // ---------------------------------------------------------------------------
@@ -170,25 +60,6 @@ struct SparseState {
   float m, l;
   int lim;             // last visible key position of the token
 };
-
-// Per-lane LDS byte offsets of the sparse fragment reads within a stage:
-// K (A operand of S^T = K Q^T) for k-step ks at row hl (+16 rows per key
-// tile), and V (transposing reads, A operand of O^T += V^T P^T) for dim tile
-// dt at row 4*gq + hl/4 (+16 rows per half, +32 per k-step).  The swizzle
-// is an XOR, so the offsets for k-step ks (dim tile dt) are the ks = 0
-// (dt = 0) offset XOR ks << 6 (dt << 5): one register each.
-struct SparseLane {
-  uint32_t k0, v0;
-  __device__ __forceinline__ uint32_t k(int ks) const { return k0 ^ static_cast<uint32_t>(ks << 6); }
-  __device__ __forceinline__ uint32_t v(int dt) const { return v0 ^ static_cast<uint32_t>(dt << 5); }
-};
-__device__ __forceinline__ SparseLane sparse_lane(int hl, int gq) {
-  SparseLane o;
-  o.k0 = hl * kRowBytes + ((gq ^ swz(hl)) << 4);
-  const int vr = 4 * gq + (hl >> 2);
-  o.v0 = vr * kRowBytes + ((((hl & 3) >> 1) ^ swz(vr)) << 4) + ((hl & 1) << 3);
-  return o;
-}
 
 // One online-softmax step of the wave's token over N attended blocks (N * 64
 // keys): S^T = K Q^T for each block, one joint max / rescale, P, then
@@ -458,37 +329,7 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
   if constexpr (DENSE) {
     nblk = s.causal ? qb_last + 1 : s.NB;
   } else {
-    for (int j = threadIdx.x; j <= qb_last; j += NT) bmask[j] = 0u;
-    __syncthreads();
-    const int per = s.topk + s.n_init + s.n_local;
-    for (int e = threadIdx.x; e < kWin * per; e += NT) {
-      const int tok = e / per, slot = e - tok * per;
-      const int r = r0 + tok;
-      if (r >= s.S_q) continue;
-      const int i = off + r, qb = i / kBS;
-      int j;
-      if (slot < s.topk) {
-        j = blk_idx[(bg * s.S_q + r) * s.topk + slot];
-      } else {
-        const int f = slot - s.topk;
-        j = f < s.n_init ? f : qb - (f - s.n_init);
-      }
-      if (j >= 0 && j <= qb) atomicOr(&bmask[j], 1u << tok);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      int cnt = 0;
-      for (int base = 0; base <= qb_last; base += 64) {
-        const int j = base + lane;
-        const uint32_t mk = j <= qb_last ? bmask[j] : 0u;
-        const uint64_t bal = __ballot(mk != 0u);
-        if (mk) blist[cnt + mask_rank(bal)] = static_cast<int>(static_cast<uint32_t>(j) | (mk << 16));
-        cnt += __popcll(bal);
-      }
-      if (lane == 0) n_list = cnt;
-    }
-    __syncthreads();
-    nblk = n_list;
+    nblk = build_union_list<NT>(bmask, blist, &n_list, blk_idx, bg, r0, off, qb_last, s, wave, lane);
   }
   // entry e of the list (dense: every block in order)
   auto entry_at = [&](int e) -> uint32_t {
@@ -520,32 +361,14 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
       dense_block(dn, dnl, kbuf, kbuf + kTileBytes, j, sl2, j * kBS + kBS - 1 > lim0, lane >> 5);
     }
   } else {
-    // Pairs of list entries: the ring holds the pair being multiplied (2
-    // stages) and the next pair in flight (the other 2); one barrier per pair.
-    static_assert(kStages == 4, "two pairs of stages");
+    // Pairs of list entries, one barrier per pair (stream_pairs).
     const SparseLane spl = sparse_lane(lane & 15, lane >> 4);
     // split-KV: this workgroup takes entries [e_lo, e_hi) of the list
     const int split = blockIdx.y;
     const int e_lo = static_cast<int>(static_cast<long long>(split) * nblk / s.nsplit);
     const int e_hi = static_cast<int>(static_cast<long long>(split + 1) * nblk / s.nsplit);
-    const int nseg = e_hi - e_lo;
-    auto seg_at = [&](int x) -> uint32_t { return x < nseg ? entry_at(e_lo + x) : 0u; };
-    const int npair = (nseg + 1) / 2;
-    uint32_t cur0 = __builtin_amdgcn_readfirstlane(seg_at(0)), cur1 = __builtin_amdgcn_readfirstlane(seg_at(1));
-    uint32_t nxt0 = __builtin_amdgcn_readfirstlane(seg_at(2)), nxt1 = __builtin_amdgcn_readfirstlane(seg_at(3));
-    if (nseg > 0) stage_block(ring, kg, vg, cur0 & 0xffffu, s.S_k, dl, wave, lane);
-    if (nseg > 1) stage_block(ring + kStageBytes, kg, vg, cur1 & 0xffffu, s.S_k, dl, wave, lane);
-    for (int pi = 0; pi < npair; ++pi) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();  // pair pi is in LDS; every wave is done with pair pi - 1
-      const int half = (pi & 1) * 2;  // first stage of pair pi
-      if (2 * pi + 2 < nseg) {
-        stage_block(ring + (half ^ 2) * kStageBytes, kg, vg, nxt0 & 0xffffu, s.S_k, dl, wave, lane);
-        if (2 * pi + 3 < nseg)
-          stage_block(ring + ((half ^ 2) + 1) * kStageBytes, kg, vg, nxt1 & 0xffffu, s.S_k, dl, wave, lane);
-      }
-      const unsigned char* stg[2] = {smem + half * kStageBytes, smem + (half + 1) * kStageBytes};
-      const int js[2] = {static_cast<int>(cur0 & 0xffffu), static_cast<int>(cur1 & 0xffffu)};
+    stream_pairs<kWaves>(smem, kg, vg, s.S_k, e_lo, e_hi, entry_at, wave, lane,
+                         [&](const unsigned char* const* stg, const int* js, uint32_t cur0, uint32_t cur1) {
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         const uint32_t bit = 1u << (16 + wave * T + t);
@@ -554,11 +377,7 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
         else if (m0) sparse_step<1>(sp[t], spl, stg, js, sl2, lane >> 4);
         else if (m1) sparse_step<1>(sp[t], spl, stg + 1, js + 1, sl2, lane >> 4);
       }
-      cur0 = nxt0;
-      cur1 = nxt1;
-      nxt0 = __builtin_amdgcn_readfirstlane(seg_at(2 * pi + 4));
-      nxt1 = __builtin_amdgcn_readfirstlane(seg_at(2 * pi + 5));
-    }
+    });
   }
 
   // ---- epilogue ---------------------------------------------------------------

@@ -126,10 +126,32 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
                :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sbase) : "memory", "m0");
 }
 
+// One direct-to-LDS load of 4 bytes per active lane (lane l writes LDS byte
+// address lds + 4 l).  Same contract as dma16.
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32)));
+  const uint64_t sbase = (static_cast<uint64_t>(hi) << 32) | lo;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
 // Wait for register values produced by global loads here, once, on every
 // path: afterwards they count as written by this (empty) asm, so no later
 // instruction inherits a wait on those loads -- which would also wait on the
 // block prefetches issued after them.
+__device__ __forceinline__ float settle_f(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 __device__ __forceinline__ bf16x8 settle(bf16x8 x) {
   u32x4 w = as_u32x4(x);
   asm volatile("" : "+v"(w));

@@ -43,4 +43,13 @@ hipError_t launch_dense_attn(const uint16_t* q, const uint16_t* k, const uint16_
                              uint16_t* out, float* lse, const AttnShape& s, void* workspace,
                              hipStream_t stream);
 
+// workspace of the sparse backward: D = <dO, O> per (token, head), then the
+// selected-entry bitmap (one bit per KV head, block and query token)
+size_t attn_bwd_workspace_bytes(const AttnShape& s);
+
+hipError_t launch_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* out,
+                                  const float* lse, const uint16_t* dout, const int32_t* blk_idx, uint16_t* dq,
+                                  uint16_t* dk, uint16_t* dv, const AttnShape& s, float scale, void* workspace,
+                                  hipStream_t stream);
+
 }  // namespace infv2
