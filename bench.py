@@ -31,7 +31,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_fwd_long_prefill_32k_traffic.json")
 ATTN_SOURCES = [os.path.join(ROOT, "trainable_block_sparse_mean_amd", "csrc", f)
-                for f in ("attn.hip", "common.hpp", "kernels.hpp")]
+                for f in ("attn.hip", "attn_common.hpp", "common.hpp", "kernels.hpp")]
 
 
 def attended_keys(S_q, S_k, bs, topk, n_init, n_local):
@@ -120,6 +120,13 @@ def cpu_baseline(w, x, target_s=15.0):
                 step_s_estimate=step_s)
 
 
+def seeded_dout(q, torch):
+    """A seeded gradient of the attention output (bf16, N(0,1))."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(17)
+    return torch.randn(*q.shape, generator=g).to(torch.bfloat16).to(q.device)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +137,9 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--profile-attn", type=int, default=0,
                     help="only launch the sparse attention kernel this many times (for counter runs)")
+    ap.add_argument("--profile-bwd", type=int, default=0,
+                    help="only run the sparse attention backward this many times (for profiler runs)")
+    ap.add_argument("--no-bwd", action="store_true", help="skip timing the sparse attention backward")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -160,6 +170,15 @@ def main():
             tb.sparse_attn_fwd(q, k, v, idx, wl.n_init, wl.n_local)
         torch.cuda.synchronize()
         print(json.dumps({"profile_attn_launches": args.profile_attn, "copy_bytes": 2 * a.numel()}))
+        return
+    if args.profile_bwd:
+        idx = tb.select_blocks(q, tb.compress_k(k), wl.S_k, wl.topk, wl.n_init, wl.n_local)
+        o, lse = tb.sparse_attn_fwd(q, k, v, idx, wl.n_init, wl.n_local)
+        dout = seeded_dout(q, torch)
+        for _ in range(args.profile_bwd):
+            tb.sparse_attn_bwd(q, k, v, o, lse, dout, idx, wl.n_init, wl.n_local)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_bwd_runs": args.profile_bwd}))
         return
 
     plan = tb.AttnPlan(wl.B, wl.H_q, wl.H_kv, wl.S_q, wl.S_k, wl.D, wl.block_size, wl.topk, wl.n_init,
@@ -210,6 +229,24 @@ def main():
         torch.cuda.synchronize()
         dense_ms = d0.elapsed_time(d1) / dreps
 
+    # ---- the backward of the sparse attention (training), same shape ------------
+    bwd_ms = None
+    if not args.no_bwd:
+        idx = tb.select_blocks(q, tb.compress_k(k), wl.S_k, wl.topk, wl.n_init, wl.n_local)
+        o, lse = tb.sparse_attn_fwd(q, k, v, idx, wl.n_init, wl.n_local)
+        dout = seeded_dout(q, torch)
+        tb.sparse_attn_bwd(q, k, v, o, lse, dout, idx, wl.n_init, wl.n_local)
+        torch.cuda.synchronize()
+        breps = 3
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record()
+        for _ in range(breps):
+            tb.sparse_attn_bwd(q, k, v, o, lse, dout, idx, wl.n_init, wl.n_local)
+        b1.record()
+        torch.cuda.synchronize()
+        bwd_ms = b0.elapsed_time(b1) / breps
+        del o, lse, dout
+
     attn_tflops = sparse_flops / (stages["sparse_attn"] * 1e-3) / 1e12
     value = sparse_flops / (ms_step * 1e-3) / 1e12
     traffic = stored_traffic()
@@ -247,7 +284,10 @@ def main():
         "dense_attn_ms": None if dense_ms is None else round(dense_ms, 4),
         "dense_attn_tflops": None if dense_ms is None else round(dense_flops / (dense_ms * 1e-3) / 1e12, 2),
         "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms_step, 3),
-        "algorithmic_flops": {"sparse_attn": sparse_flops, "dense_attn": dense_flops, "select": select_flops},
+        "sparse_attn_bwd_ms": None if bwd_ms is None else round(bwd_ms, 4),
+        "sparse_attn_bwd_tflops": None if bwd_ms is None else round(2 * sparse_flops / (bwd_ms * 1e-3) / 1e12, 2),
+        "algorithmic_flops": {"sparse_attn": sparse_flops, "dense_attn": dense_flops, "select": select_flops,
+                              "sparse_attn_bwd": 2 * sparse_flops},
         "wall_ms_per_step": round(wall_ms, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
