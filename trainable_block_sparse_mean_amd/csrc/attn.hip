@@ -61,89 +61,136 @@ struct SparseState {
   int lim;             // last visible key position of the token
 };
 
-// One online-softmax step of the wave's token over N attended blocks (N * 64
-// keys): S^T = K Q^T for each block, one joint max / rescale, P, then
-// O^T += V^T P^T.  Stage n holds block js[n].
-template <int N>
-__device__ __forceinline__ void sparse_step(SparseState& st, const SparseLane& ln, const unsigned char* const* stg,
-                                            const int* js, float sl2, int gq) {
-  // k-step outer, key tile inner: each step is 4 independent MFMAs whose K
-  // fragments were all requested together
-  floatx4 sacc[N][4];
+// Half-block pipeline: the same online softmax taken over 32-key halves of
+// the attended blocks (half i = keys 32*(i%2) .. 32*(i%2)+31 of block i/2:
+// S^T tiles 2*(i%2) and 2*(i%2)+1, and exactly k-step i%2 of O^T += V^T P^T).
+// Each half's exp work is issued between the MFMAs of the next half's
+// scores, and the next half's max between the MFMAs of this half's P V, so
+// one wave keeps its matrix core busy during its own softmax.  The rescale
+// decision stays per half (exact: a half's P is formed only after every
+// earlier half has been accumulated at the running max it was scaled by).
+__device__ __forceinline__ void qk_half(floatx4 (&sc)[2], const SparseState& st, const SparseLane& ln,
+                                        const unsigned char* kbuf, int h) {
 #pragma unroll
-  for (int n = 0; n < N; ++n)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 kf[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) kf[kt] = as_bf16x8(load16(stg[n] + ln.k(ks) + kt * 16 * kRowBytes));
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        sacc[n][kt] = mfma_16x16x32(kf[kt], st.qf[ks], ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : sacc[n][kt]);
-    }
-  // lane (hl, gq) holds keys 16*kt + 4*gq + e2 of head hl in each block
-  float mx = -INFINITY;
-#pragma unroll
-  for (int n = 0; n < N; ++n) {
-    if (js[n] * kBS + kBS - 1 > st.lim) {  // wave-uniform: the block reaches past the token
-      const int first = st.lim - js[n] * kBS - 4 * gq;  // keys 16*kt + e2 > first are masked
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2)
-          if (16 * kt + e2 > first) sacc[n][kt][e2] = -INFINITY;
-    }
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-      mx = fmaxf(mx, fmaxf(fmaxf(sacc[n][kt][0], sacc[n][kt][1]), fmaxf(sacc[n][kt][2], sacc[n][kt][3])));
+  for (int ks = 0; ks < 4; ++ks) {
+    const bf16x8 k0 = as_bf16x8(load16(kbuf + ln.k(ks) + (2 * h) * 16 * kRowBytes));
+    const bf16x8 k1 = as_bf16x8(load16(kbuf + ln.k(ks) + (2 * h + 1) * 16 * kRowBytes));
+    sc[0] = mfma_16x16x32(k0, st.qf[ks], ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : sc[0]);
+    sc[1] = mfma_16x16x32(k1, st.qf[ks], ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : sc[1]);
   }
-  mx = max_xor32(max_xor16(mx)) * sl2;
+}
+
+// keys past the token (only in the block holding its position) get -inf;
+// lane (hl, gq) holds keys 16*kt + 4*gq + e2 of the block, kt = 2h + t
+__device__ __forceinline__ void mask_half(floatx4 (&sc)[2], int first, int h) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2)
+      if (16 * (2 * h + t) + e2 > first) sc[t][e2] = -INFINITY;
+}
+
+// Maxima for the online softmax: IEEE maximum (v_maximum3_f32), which needs
+// no quieting of MFMA results first (fmaxf adds a v_max of each input with
+// itself); NaN scores (only from NaN inputs) propagate.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+__device__ __forceinline__ float max_half(const floatx4 (&sc)[2]) {
+  return vmax(vmax(vmax(sc[0][0], sc[0][1]), vmax(sc[0][2], sc[0][3])),
+              vmax(vmax(sc[1][0], sc[1][1]), vmax(sc[1][2], sc[1][3])));
+}
+
+// maximum over lanes l, l^16 and l^32 (the 4 lanes holding a head's keys)
+__device__ __forceinline__ float vmax_lanes(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return vmax(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+
+// running max update when the half's max (log2 units) passes it by the slack
+__device__ __forceinline__ void rescale_half(SparseState& st, float mx) {
   const bool grow = mx > st.m + kRescaleSlack;
   if (__builtin_amdgcn_ballot_w64(grow)) {
     const float mn = grow ? mx : st.m;
-    const float alpha = __builtin_amdgcn_exp2f(st.m - mn);  // m = -inf on a row's first block: 0
+    const float alpha = __builtin_amdgcn_exp2f(st.m - mn);  // m = -inf on a row's first half: 0
     st.l *= alpha;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) st.o[dt] *= alpha;
     st.m = mn;
   }
+}
+
+// P of a half as the B operand of its P V k-step (slots 0..3: tile 2h,
+// slots 4..7: tile 2h+1), and its row sum
+__device__ __forceinline__ bf16x8 softmax_half(SparseState& st, const floatx4 (&sc)[2], float sl2) {
   const float nm = -st.m;
-  bf16x8 pf[N][2];
-  float rs0 = 0.f, rs1 = 0.f;
+  float p[8];
 #pragma unroll
-  for (int n = 0; n < N; ++n) {
-    uint32_t pw[8];
+  for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sc[e >> 2][e & 3], sl2, nm));
+  st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  return as_bf16x8(u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                         pack_bf16x2(p[6], p[7])});
+}
+
+// O^T += V^T P^T for k-step h (keys 32h .. 32h+31): the V^T operand of lane
+// (hl, gq) is keys 32h + 4*gq + {0..3} and 32h + 16 + 4*gq + {0..3} of dim 16*dt + hl
+template <int VF = 2>
+__device__ __forceinline__ void pv_half(SparseState& st, const SparseLane& ln, const unsigned char* vbuf, bf16x8 pf,
+                                        int h) {
 #pragma unroll
-    for (int c2 = 0; c2 < 8; ++c2) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[n][c2 >> 1][(c2 & 1) * 2], sl2, nm));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[n][c2 >> 1][(c2 & 1) * 2 + 1], sl2, nm));
-      pw[c2] = pack_bf16x2(p0, p1);
-      rs0 += p0;
-      rs1 += p1;
+  for (int d0 = 0; d0 < 8; d0 += VF) {
+    bf16x8 vf[VF];
+#pragma unroll
+    for (int dd = 0; dd < VF; ++dd) {
+      const unsigned char* p = vbuf + ln.v(d0 + dd) + h * 32 * kRowBytes;
+      vf[dd] = __builtin_shufflevector(lds_read_tr(p), lds_read_tr(p + 16 * kRowBytes), 0, 1, 2, 3, 4, 5, 6, 7);
     }
-    // k-step s2 of PV takes S^T tiles 2*s2 (slots 0..3) and 2*s2+1 (slots 4..7)
-    pf[n][0] = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
-    pf[n][1] = as_bf16x8(u32x4{pw[4], pw[5], pw[6], pw[7]});
+#pragma unroll
+    for (int dd = 0; dd < VF; ++dd) st.o[d0 + dd] = mfma_16x16x32(vf[dd], pf, st.o[d0 + dd]);
   }
-  st.l += rs0 + rs1;
-  // O^T += V^T P^T.  The V^T operand of lane (hl, gq) for k-step s2 is keys
-  // 32*s2 + 4*gq + {0..3} and 32*s2 + 16 + 4*gq + {0..3} of dim 16*dt + hl.
-  // k-step outer, dim tiles inner in groups of 4: independent MFMAs.
-#pragma unroll
-  for (int n = 0; n < N; ++n)
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int d0 = 0; d0 < 8; d0 += 4) {
-        bf16x8 vf[4];
-#pragma unroll
-        for (int dd = 0; dd < 4; ++dd) {
-          const unsigned char* p = stg[n] + kTileBytes + ln.v(d0 + dd) + s2 * 32 * kRowBytes;
-          vf[dd] = __builtin_shufflevector(lds_read_tr(p), lds_read_tr(p + 16 * kRowBytes), 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-#pragma unroll
-        for (int dd = 0; dd < 4; ++dd) st.o[d0 + dd] = mfma_16x16x32(vf[dd], pf[n][s2], st.o[d0 + dd]);
-      }
+}
+
+// One pipeline step: the next half's scores (nxt, keys 32*hn.. of stage kn)
+// under the exp work of the current half (cur), then the current half's P V
+// (stage kc, k-step hc) under the next half's max.  MASK: the next half's
+// block may hold keys past the token (mask_n, wave-uniform; first_n: see
+// mask_half).
+template <bool MASK>
+__device__ __forceinline__ void half_step(SparseState& st, const SparseLane& ln, const floatx4 (&cur)[2],
+                                          floatx4 (&nxt)[2], const unsigned char* kc, int hc,
+                                          const unsigned char* kn, int hn, bool mask_n, int first_n, float sl2) {
+  qk_half(nxt, st, ln, kn, hn);
+  const bf16x8 pf = softmax_half(st, cur, sl2);
+  pv_half(st, ln, kc + kTileBytes, pf, hc);
+  if constexpr (MASK) {
+    if (mask_n) mask_half(nxt, first_n, hn);
+  }
+  rescale_half(st, vmax_lanes(max_half(nxt)) * sl2);
+}
+
+// The wave's token over one or two attended blocks (stages ka, then kb if
+// two), as one half-block pipeline.  MASK: a block may hold keys past the
+// token (only its own block does): ma / mb (wave-uniform) say which, fa / fb
+// are their mask offsets.
+template <bool MASK>
+__device__ __forceinline__ void sparse_blocks(SparseState& st, const SparseLane& ln, const unsigned char* ka,
+                                              const unsigned char* kb, bool two, bool ma, bool mb, int fa, int fb,
+                                              float sl2) {
+  floatx4 a[2], b[2];
+  qk_half(a, st, ln, ka, 0);
+  if constexpr (MASK) {
+    if (ma) mask_half(a, fa, 0);
+  }
+  rescale_half(st, vmax_lanes(max_half(a)) * sl2);
+  half_step<MASK>(st, ln, a, b, ka, 0, ka, 1, ma, fa, sl2);
+  const unsigned char* kl = ka;  // block of the last half
+  if (two) {
+    half_step<MASK>(st, ln, b, a, ka, 1, kb, 0, mb, fb, sl2);
+    half_step<MASK>(st, ln, a, b, kb, 0, kb, 1, mb, fb, sl2);
+    kl = kb;
+  }
+  pv_half(st, ln, kl + kTileBytes, softmax_half(st, b, sl2), 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -373,9 +420,18 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
       for (int t = 0; t < T; ++t) {
         const uint32_t bit = 1u << (16 + wave * T + t);
         const bool m0 = (cur0 & bit) != 0u, m1 = (cur1 & bit) != 0u;   // cur1 = 0 past the list
-        if (m0 && m1) sparse_step<2>(sp[t], spl, stg, js, sl2, lane >> 4);
-        else if (m0) sparse_step<1>(sp[t], spl, stg, js, sl2, lane >> 4);
-        else if (m1) sparse_step<1>(sp[t], spl, stg + 1, js + 1, sl2, lane >> 4);
+        // wave-uniform: which blocks the token attends, and whether one holds
+        // keys past the token (its own block)
+        const int lim = __builtin_amdgcn_readfirstlane(sp[t].lim);
+        const bool d0 = js[0] * kBS + kBS - 1 > lim, d1 = js[1] * kBS + kBS - 1 > lim;
+        const int f0 = sp[t].lim - js[0] * kBS - 4 * (lane >> 4), f1 = sp[t].lim - js[1] * kBS - 4 * (lane >> 4);
+        if (m0 || m1) {
+          const unsigned char* ka = m0 ? stg[0] : stg[1];
+          if ((m0 && d0) || (m1 && d1))
+            sparse_blocks<true>(sp[t], spl, ka, stg[1], m0 && m1, m0 ? d0 : d1, d1, m0 ? f0 : f1, f1, sl2);
+          else
+            sparse_blocks<false>(sp[t], spl, ka, stg[1], m0 && m1, false, false, 0, 0, sl2);
+        }
       }
     });
   }
