@@ -193,6 +193,63 @@ int infv2_attn_fwd(const void* q, const void* k, const void* v,
                    float softmax_scale, int switch_len,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decode over a paged, variable-length KV cache (news summary, Performance
+ * Evaluation: the method also speeds up decoding).  One new query token per
+ * sequence; sequence b holds seqlens[b] keys and its query is the last of
+ * them (key position seqlens[b] - 1), so the three calls below give, per
+ * sequence, exactly what infv2_compress_k, infv2_select_blocks and
+ * infv2_sparse_attn_fwd give for S_q = 1 on that sequence's contiguous keys.
+ *   k_pages, v_pages  bf16 [num_pages][H_kv][block_size][D]: a page is one
+ *                     key block of every KV head
+ *   block_table       int32 [B][max_blocks]: page of logical block j of
+ *                     sequence b, in [0, num_pages)
+ *   seqlens           int32 [B]: keys of sequence b, in [1, max_blocks *
+ *                     block_size]
+ *   k_cmp             bf16 [B][H_kv][max_blocks][D]: compressed keys of the
+ *                     complete blocks (j < floor(seqlens[b] / block_size);
+ *                     other rows are not read)
+ *   q, out            bf16 [B][H_q][D];  lse fp32 [B][H_q] (optional)
+ *   blk_idx           int32 [B][H_kv][topk]
+ * Lengths, table entries and page ids live in device memory and are not
+ * checked on the host: out-of-range values are clamped into range on the
+ * GPU (no out-of-bounds access), with unspecified results.
+ * A sequence with no more than n_init + n_local + topk blocks attends every
+ * one of its keys, i.e. runs dense: no separate switch is needed.
+ */
+
+/* Compressed keys of the blocks that became complete when each sequence
+ * grew from old_lens[b] to new_lens[b] keys: blocks floor(old/bs) ..
+ * floor(new/bs) - 1, at most max_new_blocks per sequence (1 per generated
+ * token; floor(max_len / bs) to fill a cache from scratch, old_lens = 0).
+ * Other rows of k_cmp are left untouched. */
+int infv2_decode_compress_append(const void* k_pages, const int32_t* block_table,
+                                 const int32_t* old_lens, const int32_t* new_lens,
+                                 void* k_cmp, int B, int H_kv, int D, int block_size,
+                                 int max_blocks, int num_pages, int max_new_blocks,
+                                 void* stream);
+
+/* Block selection of each sequence's query (as infv2_select_blocks). */
+int infv2_decode_select(const void* q, const void* k_cmp, const int32_t* seqlens,
+                        int32_t* blk_idx, float* blk_score,
+                        int B, int H_q, int H_kv, int D, int block_size,
+                        int max_blocks, int topk, int n_init, int n_local,
+                        float softmax_scale, void* stream);
+
+/* Block-sparse attention of each sequence's query over its paged keys (as
+ * infv2_sparse_attn_fwd); workspace of at least
+ * infv2_decode_attn_workspace_bytes(...) bytes, 256-byte aligned, for the
+ * split partials (nsplit x B x H_q rows of 132 floats). */
+size_t infv2_decode_attn_workspace_bytes(int B, int H_q, int H_kv, int D, int block_size,
+                                         int max_blocks, int topk);
+int infv2_decode_attn(const void* q, const void* k_pages, const void* v_pages,
+                      const int32_t* block_table, const int32_t* seqlens,
+                      const int32_t* blk_idx, void* out, float* lse,
+                      int B, int H_q, int H_kv, int D, int block_size,
+                      int max_blocks, int num_pages, int topk, int n_init, int n_local,
+                      float softmax_scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,8 +15,8 @@ pages, named in its docstring as  [page title, section].  The pages are:
     Guidance (When NOT to Use, Common Pitfalls).
   * "InfLLM-V2: Dense-Sparse Switchable Attention for Seamless Short-to-Long
     Adaptation" (paper page), Abstract.
-  * The InfLLM-V2 news summary (reportify), sections Model Advantages and
-    Technical Mechanism.
+  * The InfLLM-V2 news summary (reportify), sections Model Advantages,
+    Technical Mechanism and Performance Evaluation.
 
 Readings where the pages are silent or contradict one another are stated in
 each docstring (they are listed together in the design notes of the repo).
@@ -272,6 +272,61 @@ def sparse_attn(q, k, v, blk_idx, block_size: int, n_init: int, n_local: int,
                 out[b, g * G:(g + 1) * G, n, :] = o
                 lse[b, g * G:(g + 1) * G, n] = m
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# decode over a paged, variable-length cache
+# ---------------------------------------------------------------------------
+
+
+def paged_sequence(pages: np.ndarray, table_row, length: int, block_size: int) -> np.ndarray:
+    """The keys (or values) of one sequence of a paged cache, in order.
+
+    A paged cache stores each sequence's key blocks in pages; logical block j
+    of the sequence is page table_row[j], one block of every KV head.  The
+    sequence is its blocks concatenated in table order and cut to its length.
+
+    pages [num_pages, H, BS, D]; returns [H, length, D].
+    """
+    nb = (length + block_size - 1) // block_size
+    blocks = [pages[int(table_row[j])] for j in range(nb)]
+    return np.concatenate(blocks, axis=1)[:, :length, :]
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seqlens, block_size: int, topk: int,
+                 n_init: int, n_local: int, scale: float):
+    """One decode step over a paged, variable-length cache.
+
+    [news summary, Performance Evaluation]: the method is applied at decode
+    time too.  Each sequence b has seqlens[b] keys; its one new query sits at
+    the last key position (bottom-right alignment).  Per sequence this is
+    exactly compress_k -> select_blocks -> sparse_attn on the sequence's
+    contiguous keys and values (paged_sequence), with S_q = 1.
+
+    q [B, H_q, D]; k_pages, v_pages [num_pages, H_kv, BS, D]; block_table
+    int [B, max_blocks]; seqlens int [B].  Returns (k_cmp per sequence: list
+    of [H_kv, ceil(L/BS), D], blk_idx int32 [B, H_kv, topk], out [B, H_q, D],
+    lse [B, H_q]).
+    """
+    B, H_q, D = q.shape
+    H_kv = k_pages.shape[1]
+    idx = np.full((B, H_kv, topk), -1, dtype=np.int32)
+    out = np.zeros((B, H_q, D))
+    lse = np.zeros((B, H_q))
+    kcs = []
+    for b in range(B):
+        L = int(seqlens[b])
+        kb = paged_sequence(k_pages, block_table[b], L, block_size)[None]
+        vb = paged_sequence(v_pages, block_table[b], L, block_size)[None]
+        qb = q[b][None, :, None, :]
+        _, kc = compress_k(kb, block_size)
+        kcs.append(kc[0])
+        ib = select_blocks(qb, kc, L, topk, n_init, n_local, block_size, scale)
+        idx[b] = ib[0, :, 0, :]
+        ob, lb = sparse_attn(qb, kb, vb, ib, block_size, n_init, n_local, scale)
+        out[b] = ob[0, :, 0, :]
+        lse[b] = lb[0, :, 0]
+    return kcs, idx, out, lse
 
 
 # ---------------------------------------------------------------------------

@@ -32,7 +32,8 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ["infv2_compress_k", "infv2_select_blocks", "infv2_sparse_attn_fwd", "infv2_dense_attn_fwd",
-              "infv2_attn_fwd", "infv2_sparse_attn_bwd", "infv2_status_string"]:
+              "infv2_attn_fwd", "infv2_sparse_attn_bwd", "infv2_status_string", "infv2_decode_compress_append",
+              "infv2_decode_select", "infv2_decode_attn"]:
         assert n in names
 
 
@@ -183,3 +184,53 @@ def test_sparse_block_limit_is_what_lds_holds():
     lib = tb.load_library()
     assert _sparse(lib, S_q=10, S_k=4096 * 64 + 1) == tb.ERR_UNSUPPORTED
 
+
+
+def _dec_attn(lib, **kw):
+    a = dict(q=FAKE, kp=FAKE, vp=FAKE, table=FAKE, lens=FAKE, idx=FAKE, out=FAKE, lse=FAKE, B=16, H_q=32, H_kv=2,
+             D=128, bs=64, max_blocks=512, num_pages=8192, topk=64, n_init=1, n_local=2, scale=0.0, ws=FAKE,
+             wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.infv2_decode_attn(a["q"], a["kp"], a["vp"], a["table"], a["lens"], a["idx"], a["out"], a["lse"],
+                                 a["B"], a["H_q"], a["H_kv"], a["D"], a["bs"], a["max_blocks"], a["num_pages"],
+                                 a["topk"], a["n_init"], a["n_local"], a["scale"], a["ws"], a["wsb"], a["stream"])
+
+
+@no_gpu
+def test_decode_validation_codes():
+    lib = tb.load_library()
+    assert _dec_attn(lib, H_q=31) == tb.ERR_INVALID                # H_q % H_kv
+    assert _dec_attn(lib, max_blocks=0) == tb.ERR_INVALID
+    assert _dec_attn(lib, num_pages=0) == tb.ERR_INVALID
+    assert _dec_attn(lib, table=None) == tb.ERR_INVALID
+    assert _dec_attn(lib, lens=FAKE + 2) == tb.ERR_INVALID         # int32 arrays must be 4-byte aligned
+    assert _dec_attn(lib, kp=FAKE_MIS) == tb.ERR_INVALID
+    assert _dec_attn(lib, n_local=0) == tb.ERR_INVALID
+    assert _dec_attn(lib, D=64) == tb.ERR_UNSUPPORTED
+    assert _dec_attn(lib, bs=32) == tb.ERR_UNSUPPORTED
+    assert _dec_attn(lib, max_blocks=4097) == tb.ERR_UNSUPPORTED   # more blocks than the sparse kernel's LDS holds
+    assert _dec_attn(lib, ws=None) == tb.ERR_WORKSPACE
+    assert _dec_attn(lib, wsb=1024) == tb.ERR_WORKSPACE
+    assert _dec_attn(lib, B=0) == tb.OK
+    sel = lambda **kw: lib.infv2_decode_select(kw.get("q", FAKE), FAKE, kw.get("lens", FAKE), FAKE, None,
+                                               kw.get("B", 16), 32, 2, 128, 64, kw.get("max_blocks", 512),
+                                               kw.get("topk", 64), 1, 2, 0.0, None)
+    assert sel(lens=None) == tb.ERR_INVALID
+    assert sel(max_blocks=2049) == tb.ERR_UNSUPPORTED              # scores of more blocks than LDS holds
+    assert sel(topk=257) == tb.ERR_UNSUPPORTED
+    assert sel(B=0) == tb.OK
+    app = lambda **kw: lib.infv2_decode_compress_append(FAKE, kw.get("table", FAKE), FAKE, FAKE, FAKE, 16, 2, 128,
+                                                        64, 512, kw.get("num_pages", 100), kw.get("max_new", 1),
+                                                        None)
+    assert app(table=None) == tb.ERR_INVALID
+    assert app(num_pages=0) == tb.ERR_INVALID
+    assert app(max_new=513) == tb.ERR_INVALID                      # more new blocks than a sequence holds
+    assert app(max_new=0) == tb.OK
+
+
+def test_decode_workspace_sizes():
+    lib = tb.load_library()
+    # B * H_kv = 32 windows of one query: 16 splits of the block list, each
+    # writing 132 fp32 per (batch, query head)
+    assert lib.infv2_decode_attn_workspace_bytes(16, 32, 2, 128, 64, 512, 64) == 16 * 16 * 32 * 132 * 4
+    assert lib.infv2_decode_attn_workspace_bytes(16, 32, 2, 64, 64, 512, 64) == 0      # unsupported D

@@ -93,6 +93,16 @@ def _grad_dv_unnormalised(qh, kk, vv, do, scale, magnitudes=False):
     return dq, dk, np.exp(z - z.max(axis=1, keepdims=True)).T @ do
 
 
+def _paged_blocks_reversed(pages, table_row, length, block_size):
+    nb = (length + block_size - 1) // block_size
+    blocks = [pages[int(table_row[j])] for j in reversed(range(nb))]
+    return np.concatenate(blocks, axis=1)[:, :length, :]
+
+
+def _paged_drops_last_key(pages, table_row, length, block_size):
+    return impl.__dict__["_real_paged"](pages, table_row, max(length - 1, 1), block_size)
+
+
 MUTANTS = [
     ("group_scores", _scores_no_normalisation, [pins.test_scores_sum_to_group_size_and_nonnegative,
                                                 pins.test_scores_hand_derived_golden]),
@@ -110,12 +120,17 @@ MUTANTS = [
                                                  pins.test_backward_dense_case_matches_torch_autograd_fp64]),
     ("_softmax_attend_grad", _grad_dv_unnormalised, [pins.test_backward_sum_invariants,
                                                      pins.test_backward_dense_case_matches_torch_autograd_fp64]),
+    ("paged_sequence", _paged_blocks_reversed, [pins.test_paged_sequence_inverts_the_page_scatter,
+                                                pins.test_decode_paged_equals_per_sequence_pipeline]),
+    ("paged_sequence", _paged_drops_last_key, [pins.test_paged_sequence_inverts_the_page_scatter,
+                                               pins.test_decode_short_sequence_is_dense_softmax]),
 ]
 
 
 @pytest.mark.parametrize("name,mutant,catchers", MUTANTS, ids=[m[0] + ":" + m[1].__name__ for m in MUTANTS])
 def test_pin_catches_mutant(monkeypatch, name, mutant, catchers):
     monkeypatch.setattr(impl, "_real_grad", impl._softmax_attend_grad, raising=False)
+    monkeypatch.setattr(impl, "_real_paged", impl.paged_sequence, raising=False)
     monkeypatch.setattr(impl, name, mutant)
     for pin in catchers:
         with pytest.raises(AssertionError):

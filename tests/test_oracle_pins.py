@@ -527,3 +527,88 @@ def test_backward_sum_invariants():
     want = do.reshape(1, H_kv, G, 300, 8).sum(axis=(2, 3))
     np.testing.assert_allclose(dv.sum(axis=2), want, rtol=1e-11, atol=1e-11)
 
+
+
+# ---------------------------------------------------------------- decode ----
+# A paged cache is defined by scattering each sequence's key blocks into
+# pages; the oracle's gather must invert that scatter, and its decode step
+# must be the contiguous pipeline run on each sequence with S_q = 1.
+
+def _scatter_into_pages(rng, seqs, bs, extra=3):
+    """seqs: list of [H, L_b, D].  Returns (pages [P, H, bs, D], table int32
+    [B, max_blocks] with unused slots = -1); pages are handed out in a random
+    order and a block's rows past the sequence end stay zero."""
+    H, D = seqs[0].shape[0], seqs[0].shape[2]
+    nbs = [(s.shape[1] + bs - 1) // bs for s in seqs]
+    P = sum(nbs) + extra
+    order = rng.permutation(P)
+    pages = rng.standard_normal((P, H, bs, D))  # unused pages hold noise
+    table = np.full((len(seqs), max(nbs) + 2), -1, dtype=np.int32)
+    c = 0
+    for b, s in enumerate(seqs):
+        for j in range(nbs[b]):
+            p = int(order[c])
+            c += 1
+            table[b, j] = p
+            rows = s[:, j * bs:(j + 1) * bs, :]
+            pages[p] = 0.0
+            pages[p, :, :rows.shape[1], :] = rows
+    return pages, table
+
+
+def test_paged_sequence_inverts_the_page_scatter():
+    rng = np.random.default_rng(31)
+    bs = 8
+    lens = [1, 7, 8, 9, 40, 23]
+    seqs = [rng.standard_normal((2, L, 4)) for L in lens]
+    pages, table = _scatter_into_pages(rng, seqs, bs)
+    for b, s in enumerate(seqs):
+        np.testing.assert_array_equal(O.paged_sequence(pages, table[b], lens[b], bs), s)
+
+
+def test_decode_paged_equals_per_sequence_pipeline():
+    rng = np.random.default_rng(32)
+    bs, H_kv, G, D, topk = 64, 2, 2, 8, 3
+    lens = [1, 64, 65, 300, 900, 640]
+    ks = [rng.standard_normal((H_kv, L, D)) for L in lens]
+    vs = [rng.standard_normal((H_kv, L, D)) for L in lens]
+    kp, table = _scatter_into_pages(rng, ks, bs)
+    vp = np.zeros_like(kp)
+    for b, v in enumerate(vs):  # the values take the same pages as the keys
+        for j in range((lens[b] + bs - 1) // bs):
+            rows = v[:, j * bs:(j + 1) * bs, :]
+            vp[table[b, j], :, :rows.shape[1], :] = rows
+    q = rng.standard_normal((len(lens), H_kv * G, D))
+    kcs, idx, out, lse = O.decode_paged(q, kp, vp, table, np.array(lens), bs, topk, 1, 2, 0.4)
+    for b, L in enumerate(lens):
+        qb = q[b][None, :, None, :]
+        _, kc = O.compress_k(ks[b][None], bs)
+        np.testing.assert_array_equal(kcs[b], kc[0])
+        ib = O.select_blocks(qb, kc, L, topk, 1, 2, bs, 0.4)
+        np.testing.assert_array_equal(idx[b], ib[0, :, 0])
+        ob, lb = O.sparse_attn(qb, ks[b][None], vs[b][None], ib, bs, 1, 2, 0.4)
+        np.testing.assert_array_equal(out[b], ob[0, :, 0])
+        np.testing.assert_array_equal(lse[b], lb[0, :, 0])
+
+
+def test_decode_short_sequence_is_dense_softmax():
+    """A sequence with no more than n_init + n_local + topk blocks attends all
+    of its keys: the output is the plain softmax over them."""
+    rng = np.random.default_rng(33)
+    bs, H_kv, G, D, topk = 64, 1, 4, 8, 2
+    lens = [5, 64, 200, 320]  # at most 1 + 2 + 2 = 5 blocks
+    ks = [rng.standard_normal((H_kv, L, D)) for L in lens]
+    vs = [rng.standard_normal((H_kv, L, D)) for L in lens]
+    kp, table = _scatter_into_pages(rng, ks, bs)
+    vp = np.zeros_like(kp)
+    for b, v in enumerate(vs):
+        for j in range((lens[b] + bs - 1) // bs):
+            rows = v[:, j * bs:(j + 1) * bs, :]
+            vp[table[b, j], :, :rows.shape[1], :] = rows
+    q = rng.standard_normal((len(lens), H_kv * G, D))
+    _, _, out, lse = O.decode_paged(q, kp, vp, table, np.array(lens), bs, topk, 1, 2, 0.3)
+    for b in range(len(lens)):
+        for h in range(H_kv * G):
+            z = 0.3 * ks[b][h // G] @ q[b, h]
+            np.testing.assert_allclose(out[b, h], scipy.special.softmax(z) @ vs[b][h // G], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(lse[b, h], scipy.special.logsumexp(z), rtol=1e-12)

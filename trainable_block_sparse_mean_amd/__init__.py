@@ -39,6 +39,10 @@ SIGNATURES = {
     "infv2_dense_attn_fwd": (_c_int, [_vp] * 5 + [_c_int] * 6 + [_c_float, _c_int, _vp, _c_size, _vp]),
     "infv2_attn_workspace_bytes": (_c_size, [_c_int] * 9),
     "infv2_attn_fwd": (_c_int, [_vp] * 6 + [_c_int] * 10 + [_c_float, _c_int, _vp, _c_size, _vp]),
+    "infv2_decode_compress_append": (_c_int, [_vp] * 5 + [_c_int] * 7 + [_vp]),
+    "infv2_decode_select": (_c_int, [_vp] * 5 + [_c_int] * 9 + [_c_float, _vp]),
+    "infv2_decode_attn_workspace_bytes": (_c_size, [_c_int] * 7),
+    "infv2_decode_attn": (_c_int, [_vp] * 8 + [_c_int] * 10 + [_c_float, _vp, _c_size, _vp]),
 }
 
 _lib = None
@@ -179,6 +183,68 @@ def dense_attn_fwd(q, k, v, causal: bool = True, softmax_scale=None, return_lse:
     ws = _workspace(load_library().infv2_dense_workspace_bytes(B, H_q, H_kv, S_q, S_k, D), q.device)
     _call("infv2_dense_attn_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H_q, H_kv, S_q, S_k, D,
           _scale(softmax_scale), int(bool(causal)), _ptr(ws), ws.numel(), _stream())
+    return out, lse
+
+
+def decode_compress_append(k_pages, block_table, old_lens, new_lens, k_cmp, max_new_blocks: int,
+                           block_size: int = 64):
+    """Fill k_cmp (bf16 [B,H_kv,max_blocks,D], in place) with the compressed keys
+    of the blocks of a paged cache that became complete when sequence b grew
+    from old_lens[b] to new_lens[b] keys (at most max_new_blocks per sequence).
+    k_pages bf16 [num_pages,H_kv,block_size,D]; block_table int32
+    [B,max_blocks]; old_lens, new_lens int32 [B]."""
+    _need(k_pages, "k_pages", torch.bfloat16, 4)
+    _need(k_cmp, "k_cmp", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    for t, n in ((old_lens, "old_lens"), (new_lens, "new_lens")):
+        _need(t, n, torch.int32, 1)
+    num_pages, H_kv, _, D = k_pages.shape
+    B, max_blocks = block_table.shape
+    _call("infv2_decode_compress_append", _ptr(k_pages), _ptr(block_table), _ptr(old_lens), _ptr(new_lens),
+          _ptr(k_cmp), B, H_kv, D, block_size, max_blocks, num_pages, max_new_blocks, _stream())
+    return k_cmp
+
+
+def decode_select(q, k_cmp, seqlens, topk: int, n_init: int = 1, n_local: int = 2, softmax_scale=None,
+                  block_size: int = 64, return_scores: bool = False):
+    """Block selection for one query per sequence (the last of its seqlens[b]
+    keys).  q bf16 [B,H_q,D]; k_cmp bf16 [B,H_kv,max_blocks,D]; seqlens int32
+    [B].  Returns blk_idx int32 [B,H_kv,topk] (and the group scores)."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cmp, "k_cmp", torch.bfloat16, 4)
+    _need(seqlens, "seqlens", torch.int32, 1)
+    B, H_q, D = q.shape
+    H_kv, max_blocks = k_cmp.shape[1], k_cmp.shape[2]
+    idx = torch.empty(B, H_kv, topk, dtype=torch.int32, device=q.device)
+    score = torch.empty(B, H_kv, topk, dtype=torch.float32, device=q.device) if return_scores else None
+    _call("infv2_decode_select", _ptr(q), _ptr(k_cmp), _ptr(seqlens), _ptr(idx), _ptr(score), B, H_q, H_kv, D,
+          block_size, max_blocks, topk, n_init, n_local, _scale(softmax_scale), _stream())
+    return (idx, score) if return_scores else idx
+
+
+def decode_attn(q, k_pages, v_pages, block_table, seqlens, blk_idx, n_init: int = 1, n_local: int = 2,
+                softmax_scale=None, block_size: int = 64, return_lse: bool = True):
+    """Block-sparse attention of one query per sequence over its paged keys.
+    q bf16 [B,H_q,D]; k_pages, v_pages bf16 [num_pages,H_kv,block_size,D];
+    block_table int32 [B,max_blocks]; seqlens int32 [B]; blk_idx int32
+    [B,H_kv,topk].  Returns (out bf16 [B,H_q,D], lse fp32 [B,H_q] or None)."""
+    _need(q, "q", torch.bfloat16, 3)
+    for t, n in ((k_pages, "k_pages"), (v_pages, "v_pages")):
+        _need(t, n, torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seqlens, "seqlens", torch.int32, 1)
+    _need(blk_idx, "blk_idx", torch.int32, 3)
+    B, H_q, D = q.shape
+    num_pages, H_kv = k_pages.shape[0], k_pages.shape[1]
+    max_blocks = block_table.shape[1]
+    topk = blk_idx.shape[2]
+    out = torch.empty_like(q)
+    lse = torch.empty(B, H_q, dtype=torch.float32, device=q.device) if return_lse else None
+    nbytes = load_library().infv2_decode_attn_workspace_bytes(B, H_q, H_kv, D, block_size, max_blocks, topk)
+    ws = _workspace(nbytes, q.device)
+    _call("infv2_decode_attn", _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seqlens),
+          _ptr(blk_idx), _ptr(out), _ptr(lse), B, H_q, H_kv, D, block_size, max_blocks, num_pages, topk, n_init,
+          n_local, _scale(softmax_scale), _ptr(ws), ws.numel(), _stream())
     return out, lse
 
 

@@ -63,10 +63,36 @@ AttnShape make_shape(int B, int H_q, int H_kv, int S_q, int S_k, int block_size,
   s.scale_log2 = sl2;
   s.causal = causal;
   s.nsplit = 1;
+  s.seqlens = nullptr;
+  s.block_table = nullptr;
+  s.num_pages = 0;
   return s;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? INFV2_OK : INFV2_ERR_HIP; }
+
+// ---- decode over a paged, variable-length cache -----------------------------
+int check_decode(int B, int H_q, int H_kv, int D, int block_size, int max_blocks) {
+  if (B < 0 || H_q < 1 || H_kv < 1 || D < 1 || block_size < 1 || max_blocks < 1) return INFV2_ERR_INVALID;
+  if (H_q % H_kv != 0) return INFV2_ERR_INVALID;
+  if (D != infv2::kD || block_size != infv2::kBS) return INFV2_ERR_UNSUPPORTED;
+  if (H_q / H_kv > infv2::kMaxG) return INFV2_ERR_UNSUPPORTED;
+  if (static_cast<long long>(max_blocks) * block_size * D >= (1LL << 31)) return INFV2_ERR_UNSUPPORTED;
+  return INFV2_OK;
+}
+
+bool ints_ok(const void* p) { return p != nullptr && aligned(p, 4); }
+
+// one query per sequence (S_q = 1) at key seqlens[b] - 1 of a cache of
+// max_blocks blocks per sequence
+AttnShape decode_shape(int B, int H_q, int H_kv, int max_blocks, int topk, int n_init, int n_local, float sl2,
+                       const int32_t* seqlens, const int32_t* block_table, int num_pages) {
+  AttnShape s = make_shape(B, H_q, H_kv, 1, max_blocks * infv2::kBS, infv2::kBS, topk, n_init, n_local, sl2, 1);
+  s.seqlens = seqlens;
+  s.block_table = block_table;
+  s.num_pages = num_pages;
+  return s;
+}
 
 size_t sparse_ws(int B, int H_q, int H_kv, int S_q, int S_k, int block_size, int topk) {
   const AttnShape s = make_shape(B, H_q, H_kv, S_q, S_k, block_size, topk, 0, 1, 1.f, 1);
@@ -256,6 +282,73 @@ int infv2_attn_fwd(const void* q, const void* k, const void* v, void* out, float
   }
   return infv2_sparse_attn_fwd(q, k, v, idx, out, lse, B, H_q, H_kv, S_q, S_k, D, block_size, topk, n_init,
                                n_local, softmax_scale, rest, rest_bytes, stream);
+}
+
+int infv2_decode_compress_append(const void* k_pages, const int32_t* block_table, const int32_t* old_lens,
+                                 const int32_t* new_lens, void* k_cmp, int B, int H_kv, int D, int block_size,
+                                 int max_blocks, int num_pages, int max_new_blocks, void* stream) {
+  int st = check_decode(B, H_kv, H_kv, D, block_size, max_blocks);
+  if (st != INFV2_OK) return st;
+  if (num_pages < 1 || max_new_blocks < 0 || max_new_blocks > max_blocks) return INFV2_ERR_INVALID;
+  if (B == 0 || max_new_blocks == 0) return INFV2_OK;
+  if (!tensor_ok(k_pages) || !tensor_ok(k_cmp) || !ints_ok(block_table) || !ints_ok(old_lens) ||
+      !ints_ok(new_lens))
+    return INFV2_ERR_INVALID;
+  const AttnShape s = decode_shape(B, H_kv, H_kv, max_blocks, 0, 0, 1, 1.f, new_lens, block_table, num_pages);
+  return hip_status(infv2::launch_compress_append(static_cast<const uint16_t*>(k_pages), s, old_lens,
+                                                  static_cast<uint16_t*>(k_cmp), max_new_blocks,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+int infv2_decode_select(const void* q, const void* k_cmp, const int32_t* seqlens, int32_t* blk_idx,
+                        float* blk_score, int B, int H_q, int H_kv, int D, int block_size, int max_blocks,
+                        int topk, int n_init, int n_local, float softmax_scale, void* stream) {
+  int st = check_decode(B, H_q, H_kv, D, block_size, max_blocks);
+  if (st != INFV2_OK) return st;
+  st = check_sparse_params(block_size, topk, n_init, n_local);
+  if (st != INFV2_OK) return st;
+  if (max_blocks > kMaxSelectBlocks) return INFV2_ERR_UNSUPPORTED;
+  if (B == 0 || topk == 0) return INFV2_OK;
+  if (!tensor_ok(q) || !tensor_ok(k_cmp) || !tensor_ok(blk_idx) || !ints_ok(seqlens)) return INFV2_ERR_INVALID;
+  if (blk_score && !aligned(blk_score, 16)) return INFV2_ERR_INVALID;
+  const AttnShape s = decode_shape(B, H_q, H_kv, max_blocks, topk, n_init, n_local, scale_log2(softmax_scale, D),
+                                   seqlens, nullptr, 0);
+  return hip_status(infv2::launch_select_blocks(static_cast<const uint16_t*>(q),
+                                                static_cast<const uint16_t*>(k_cmp), blk_idx, blk_score, s,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+size_t infv2_decode_attn_workspace_bytes(int B, int H_q, int H_kv, int D, int block_size, int max_blocks,
+                                         int topk) {
+  if (check_decode(B, H_q, H_kv, D, block_size, max_blocks) != INFV2_OK || topk < 0) return 0;
+  const AttnShape s = decode_shape(B, H_q, H_kv, max_blocks, topk, 0, 1, 1.f, nullptr, nullptr, 0);
+  return round_up(infv2::attn_workspace_bytes(s), 256);
+}
+
+int infv2_decode_attn(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                      const int32_t* seqlens, const int32_t* blk_idx, void* out, float* lse, int B, int H_q,
+                      int H_kv, int D, int block_size, int max_blocks, int num_pages, int topk, int n_init,
+                      int n_local, float softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_decode(B, H_q, H_kv, D, block_size, max_blocks);
+  if (st != INFV2_OK) return st;
+  st = check_sparse_params(block_size, topk, n_init, n_local);
+  if (st != INFV2_OK) return st;
+  if (max_blocks > kMaxSparseBlocks) return INFV2_ERR_UNSUPPORTED;
+  if (num_pages < 1) return INFV2_ERR_INVALID;
+  if (B == 0) return INFV2_OK;
+  if (!tensor_ok(q) || !tensor_ok(k_pages) || !tensor_ok(v_pages) || !tensor_ok(out) || !ints_ok(block_table) ||
+      !ints_ok(seqlens))
+    return INFV2_ERR_INVALID;
+  if (topk > 0 && !tensor_ok(blk_idx)) return INFV2_ERR_INVALID;
+  if (lse && !aligned(lse, 16)) return INFV2_ERR_INVALID;
+  const size_t need = infv2_decode_attn_workspace_bytes(B, H_q, H_kv, D, block_size, max_blocks, topk);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return INFV2_ERR_WORKSPACE;
+  if (workspace && !aligned(workspace, 256)) return INFV2_ERR_INVALID;
+  const AttnShape s = decode_shape(B, H_q, H_kv, max_blocks, topk, n_init, n_local, scale_log2(softmax_scale, D),
+                                   seqlens, block_table, num_pages);
+  return hip_status(infv2::launch_sparse_attn(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pages), static_cast<const uint16_t*>(v_pages),
+      blk_idx, static_cast<uint16_t*>(out), lse, s, workspace, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -321,11 +321,14 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
   const size_t bg = static_cast<size_t>(bg_i);
   const int r0 = win * kWin;
   const int rw = r0 + wave * T;              // first token of this wave
-  const int off = s.S_k - s.S_q;
+  const int S_k = seq_keys(s, b);            // keys of this sequence
+  const int off = S_k - s.S_q;
   const int i_last = off + min(r0 + kWin, s.S_q) - 1;
   const int qb_last = i_last / kBS;
-  const uint16_t* kg = k + bg * s.S_k * kD;
+  const uint16_t* kg = k + bg * s.S_k * kD;  // contiguous K/V (dense, and sparse without pages)
   const uint16_t* vg = v + bg * s.S_k * kD;
+  const BlockSrc src{s.block_table ? k : kg, s.block_table ? v : vg, s.block_table, s.NB, s.num_pages, s.H_kv, b, g,
+                     S_k};
   const uint32_t ring = lds_addr(smem);
   const float sl2 = s.scale_log2;
 
@@ -346,7 +349,7 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
     for (int dt = 0; dt < 4; ++dt) dn.o[dt] = floatx16{};
     dn.m = -INFINITY;
     dn.l = 0.f;
-    dn.lim = s.causal ? min(off + r, s.S_k - 1) : s.S_k - 1;
+    dn.lim = s.causal ? min(off + r, S_k - 1) : S_k - 1;
   } else {
     const int hl = lane & 15, gq = lane >> 4;
 #pragma unroll
@@ -365,7 +368,7 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
       for (int dt = 0; dt < 8; ++dt) sp[t].o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
       sp[t].m = -INFINITY;
       sp[t].l = 0.f;
-      sp[t].lim = min(off + rw + t, s.S_k - 1);
+      sp[t].lim = min(off + rw + t, S_k - 1);
     }
   }
 
@@ -391,18 +394,17 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
     // prologue: the first kStages - 1 blocks in flight
 #pragma unroll
     for (int e = 0; e < kStages - 1; ++e)
-      if (e < nblk) stage_block(ring + e * kStageBytes, kg, vg, e, s.S_k, dl, wave, lane);
+      if (e < nblk) stage_src(ring + e * kStageBytes, src, e, dl, wave, lane);
     // this wave's two tokens' visibility limits (a token past the end of the
     // queries takes its partner's)
-    const int lim0 = s.causal ? min(off + rw, s.S_k - 1) : s.S_k - 1;
-    const int lim1 = rw + 1 < s.S_q ? (s.causal ? min(off + rw + 1, s.S_k - 1) : s.S_k - 1) : lim0;
+    const int lim0 = s.causal ? min(off + rw, S_k - 1) : S_k - 1;
+    const int lim1 = rw + 1 < s.S_q ? (s.causal ? min(off + rw + 1, S_k - 1) : S_k - 1) : lim0;
     const DenseLane dnl = dense_lane(lane);
     for (int j = 0; j < nblk; ++j) {
       wait_dma<kDma>(min(kStages - 2, nblk - 1 - j));
       __syncthreads();  // block j is in LDS; every wave is done with block j - 1
       if (j + kStages - 1 < nblk)
-        stage_block(ring + ((j + kStages - 1) % kStages) * kStageBytes, kg, vg, j + kStages - 1, s.S_k, dl, wave,
-                    lane);
+        stage_src(ring + ((j + kStages - 1) % kStages) * kStageBytes, src, j + kStages - 1, dl, wave, lane);
       if (rw >= s.S_q || j * kBS > lim1) continue;   // neither token sees block j
       const unsigned char* kbuf = smem + (j % kStages) * kStageBytes;
       dense_block(dn, dnl, kbuf, kbuf + kTileBytes, j, sl2, j * kBS + kBS - 1 > lim0, lane >> 5);
@@ -414,7 +416,7 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
     const int split = blockIdx.y;
     const int e_lo = static_cast<int>(static_cast<long long>(split) * nblk / s.nsplit);
     const int e_hi = static_cast<int>(static_cast<long long>(split + 1) * nblk / s.nsplit);
-    stream_pairs<kWaves>(smem, kg, vg, s.S_k, e_lo, e_hi, entry_at, wave, lane,
+    stream_pairs<kWaves>(smem, src, e_lo, e_hi, entry_at, wave, lane,
                          [&](const unsigned char* const* stg, const int* js, uint32_t cur0, uint32_t cur1) {
 #pragma unroll
       for (int t = 0; t < T; ++t) {

@@ -68,14 +68,16 @@ __device__ __forceinline__ DmaLane<WAVES> dma_lane(int wave, int lane) {
   return d;
 }
 
-// Issue the loads of key block j into one stage of the ring.
+// Issue the loads of one key block into one stage of the ring: kb and vb
+// point at the block's first K and V rows, nrows (1..64) of which hold
+// keys.  Rows past the last key re-read that key's row (finite, masked).
 template <int WAVES>
-__device__ __forceinline__ void stage_block(uint32_t stage_lds, const uint16_t* kg, const uint16_t* vg, int j,
-                                            int S_k, const DmaLane<WAVES>& d, int wave, int lane) {
+__device__ __forceinline__ void stage_block(uint32_t stage_lds, const uint16_t* kb16, const uint16_t* vb16, int nrows,
+                                            const DmaLane<WAVES>& d, int wave, int lane) {
   constexpr int C = DmaLane<WAVES>::kChunks;
-  const char* kb = reinterpret_cast<const char*>(kg) + static_cast<size_t>(j) * kTileBytes;
-  const char* vb = reinterpret_cast<const char*>(vg) + static_cast<size_t>(j) * kTileBytes;
-  if (j * kBS + kBS <= S_k) {
+  const char* kb = reinterpret_cast<const char*>(kb16);
+  const char* vb = reinterpret_cast<const char*>(vb16);
+  if (nrows >= kBS) {
 #pragma unroll
     for (int n = 0; n < C; ++n) {
       const uint32_t lds = stage_lds + (wave * C + n) * 1024;
@@ -87,13 +89,38 @@ __device__ __forceinline__ void stage_block(uint32_t stage_lds, const uint16_t* 
 #pragma unroll
     for (int n = 0; n < C; ++n) {
       const int row = (wave * C + n) * 4 + sub;
-      const int crow = min(row, S_k - 1 - j * kBS);
+      const int crow = min(row, nrows - 1);
       const uint32_t off = static_cast<uint32_t>(crow * kRowBytes + ((slot ^ swz(row)) << 4));
       const uint32_t lds = stage_lds + (wave * C + n) * 1024;
       dma16(kb, off, lds);
       dma16(vb, off, lds + kTileBytes);
     }
   }
+}
+
+// Where a KV head's blocks live: the contiguous [S_k][D] rows of one
+// (batch, KV head) at k / v, or, with a block table, pages of a paged cache
+// based at k / v (see block_rows).  krows(j) / vrows(j) give block j's first
+// row, keys(j) how many of its rows hold keys.
+struct BlockSrc {
+  const uint16_t* k;
+  const uint16_t* v;
+  const int* table;  // null: contiguous
+  int nb, num_pages, H_kv, b, g, S_k;
+  __device__ __forceinline__ size_t rows(int j) const {
+    if (!table) return static_cast<size_t>(j) * kBS * kD;
+    const int page = min(max(table[static_cast<size_t>(b) * nb + j], 0), num_pages - 1);
+    return (static_cast<size_t>(page) * H_kv + g) * kBS * kD;
+  }
+  __device__ __forceinline__ const uint16_t* krows(int j) const { return k + rows(j); }
+  __device__ __forceinline__ const uint16_t* vrows(int j) const { return v + rows(j); }
+  __device__ __forceinline__ int keys(int j) const { return min(kBS, S_k - j * kBS); }
+};
+
+template <int WAVES>
+__device__ __forceinline__ void stage_src(uint32_t stage_lds, const BlockSrc& src, int j, const DmaLane<WAVES>& d,
+                                          int wave, int lane) {
+  stage_block<WAVES>(stage_lds, src.krows(j), src.vrows(j), src.keys(j), d, wave, lane);
 }
 
 // Workgroup -> (KV head, window).  The hardware deals workgroups to the XCDs
@@ -192,8 +219,8 @@ __device__ __forceinline__ int build_union_list(uint32_t* bmask, int* blist, int
 // (the other 2); one barrier per pair.  on_pair(stg, js, cur0, cur1) gets the
 // two stages, their blocks and their list entries (cur1 = 0 past the end).
 template <int WAVES, typename Entry, typename F>
-__device__ __forceinline__ void stream_pairs(unsigned char* smem, const uint16_t* kg, const uint16_t* vg, int S_k,
-                                             int e_lo, int e_hi, Entry entry_at, int wave, int lane, F&& on_pair) {
+__device__ __forceinline__ void stream_pairs(unsigned char* smem, const BlockSrc& src, int e_lo, int e_hi,
+                                             Entry entry_at, int wave, int lane, F&& on_pair) {
   static_assert(kStages == 4, "two pairs of stages");
   const uint32_t ring = lds_addr(smem);
   const DmaLane<WAVES> dl = dma_lane<WAVES>(wave, lane);
@@ -202,16 +229,16 @@ __device__ __forceinline__ void stream_pairs(unsigned char* smem, const uint16_t
   const int npair = (nseg + 1) / 2;
   uint32_t cur0 = __builtin_amdgcn_readfirstlane(seg_at(0)), cur1 = __builtin_amdgcn_readfirstlane(seg_at(1));
   uint32_t nxt0 = __builtin_amdgcn_readfirstlane(seg_at(2)), nxt1 = __builtin_amdgcn_readfirstlane(seg_at(3));
-  if (nseg > 0) stage_block(ring, kg, vg, cur0 & 0xffffu, S_k, dl, wave, lane);
-  if (nseg > 1) stage_block(ring + kStageBytes, kg, vg, cur1 & 0xffffu, S_k, dl, wave, lane);
+  if (nseg > 0) stage_src(ring, src, cur0 & 0xffffu, dl, wave, lane);
+  if (nseg > 1) stage_src(ring + kStageBytes, src, cur1 & 0xffffu, dl, wave, lane);
   for (int pi = 0; pi < npair; ++pi) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // pair pi is in LDS; every wave is done with pair pi - 1
     const int half = (pi & 1) * 2;  // first stage of pair pi
     if (2 * pi + 2 < nseg) {
-      stage_block(ring + (half ^ 2) * kStageBytes, kg, vg, nxt0 & 0xffffu, S_k, dl, wave, lane);
+      stage_src(ring + (half ^ 2) * kStageBytes, src, nxt0 & 0xffffu, dl, wave, lane);
       if (2 * pi + 3 < nseg)
-        stage_block(ring + ((half ^ 2) + 1) * kStageBytes, kg, vg, nxt1 & 0xffffu, S_k, dl, wave, lane);
+        stage_src(ring + ((half ^ 2) + 1) * kStageBytes, src, nxt1 & 0xffffu, dl, wave, lane);
     }
     const unsigned char* stg[2] = {smem + half * kStageBytes, smem + (half + 1) * kStageBytes};
     const int js[2] = {static_cast<int>(cur0 & 0xffffu), static_cast<int>(cur1 & 0xffffu)};

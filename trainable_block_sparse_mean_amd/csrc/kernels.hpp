@@ -15,7 +15,32 @@ struct AttnShape {
   float scale_log2;  // softmax scale * log2(e)
   int causal;
   int nsplit;        // sparse: workgroups sharing one window's block list (1 = no split)
+  // A paged, variable-length key cache (decode); both null for one key
+  // length S_k and contiguous [B][H_kv][S_k][D] K/V.
+  //   seqlens[b]: keys of sequence b, 1 .. NB * 64 (its queries end at key
+  //     seqlens[b] - 1); NB is then the per-sequence block capacity, the row
+  //     stride of block_table and of the compressed keys.
+  //   block_table[b * NB + j]: the page holding logical block j of sequence
+  //     b, 0 .. num_pages - 1; a page is one 64-key block of every KV head,
+  //     [H_kv][64][D].
+  const int* seqlens;
+  const int* block_table;
+  int num_pages;
 };
+
+// keys of sequence b (the uniform S_k without a length table), clamped to
+// the block capacity so that a bad length cannot address past the table
+__device__ __forceinline__ int seq_keys(const AttnShape& s, int b) {
+  return s.seqlens ? min(max(s.seqlens[b], 1), s.NB * 64) : s.S_k;
+}
+
+// first row of block j of (batch b, KV head g) in a paged cache of
+// [page][H_kv][64][128] rows (page ids clamped into range, so that a bad
+// table cannot address past the pages)
+__device__ __forceinline__ size_t page_rows(const AttnShape& s, int b, int g, int j) {
+  const int page = min(max(s.block_table[static_cast<size_t>(b) * s.NB + j], 0), s.num_pages - 1);
+  return (static_cast<size_t>(page) * s.H_kv + g) * 64 * 128;
+}
 
 // Split-KV partials of the sparse kernel, in the workspace: for split s and
 // query row (b, h, r), 128 unnormalised fp32 output values relative to the
@@ -28,6 +53,12 @@ int sparse_splits(int B, int H_kv, int S_q, int topk);
 
 hipError_t launch_compress_k(const uint16_t* k, uint16_t* k_cmp, int B, int H_kv, int S_k,
                              hipStream_t stream);
+
+// compressed keys of the blocks of a paged cache that became complete when
+// sequence b grew from old_len[b] to new_len[b] keys (at most max_new per
+// sequence); k_cmp is [B][H_kv][NB][D]
+hipError_t launch_compress_append(const uint16_t* k_pages, const AttnShape& s, const int* old_len,
+                                  uint16_t* k_cmp, int max_new, hipStream_t stream);
 
 hipError_t launch_select_blocks(const uint16_t* q, const uint16_t* k_cmp, int32_t* blk_idx,
                                 float* blk_score, const AttnShape& s, hipStream_t stream);

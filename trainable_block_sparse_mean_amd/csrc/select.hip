@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_blocks_kernel(const uin
   const int b = blockIdx.y / s.H_kv;
   const int r0 = (gridDim.x - 1 - blockIdx.x) * kSelWaves;  // latest (heaviest) tokens first
   const int r = r0 + wave;    // this wave's token
-  const int off = s.S_k - s.S_q;
+  const int off = seq_keys(s, b) - s.S_q;  // query row r sits at key position off + r
   const bool active = r < s.S_q;
   const int nv = active ? (off + r + 1) / kBS : 0;  // fully visible blocks
   const int r_last = min(r0 + kSelWaves, s.S_q) - 1;
