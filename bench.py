@@ -127,6 +127,66 @@ def seeded_dout(q, torch):
     return torch.randn(*q.shape, generator=g).to(torch.bfloat16).to(q.device)
 
 
+def time_decode_paged(torch, tb, workloads, dev, reps=50):
+    """One generation step of the decode workload (16 sequences, 32 q / 2 kv
+    heads, top-64) over a paged cache: append the compressed key of any block
+    the new token completes, select, attend.  The 16 sequences hold 32768 - 37 b
+    keys (ragged) in 64-key pages handed out in a random order.  Returns
+    {paged step ms, its parts, the contiguous path's step at one length}."""
+    wl = workloads.DECODE_32K
+    g = torch.Generator(device="cpu")
+    g.manual_seed(23)
+    B, H_q, H_kv, D = wl.B, wl.H_q, wl.H_kv, wl.D
+    lens = [wl.S_k - 37 * b for b in range(B)]
+    nbs = [(L + 63) // 64 for L in lens]
+    max_blocks = max(nbs) + 1
+    P = sum(nbs) + B
+    order = torch.randperm(P, generator=g)
+    table = torch.zeros(B, max_blocks, dtype=torch.int32)
+    c = 0
+    for b in range(B):  # every sequence owns nbs[b] + 1 pages (room for the next block)
+        table[b, :nbs[b] + 1] = order[c:c + nbs[b] + 1].to(torch.int32)
+        c += nbs[b] + 1
+    kp = torch.randn(P, H_kv, 64, D, generator=g).to(torch.bfloat16).to(dev)
+    vp = torch.randn(P, H_kv, 64, D, generator=g).to(torch.bfloat16).to(dev)
+    q = torch.randn(B, H_q, D, generator=g).to(torch.bfloat16).to(dev)
+    table = table.to(dev)
+    cur = torch.tensor(lens, dtype=torch.int32, device=dev)
+    nxt = cur + 1
+    k_cmp = torch.zeros(B, H_kv, max_blocks, D, dtype=torch.bfloat16, device=dev)
+    tb.decode_compress_append(kp, table, torch.zeros_like(cur), cur, k_cmp, max_blocks)
+
+    def step():
+        tb.decode_compress_append(kp, table, cur, nxt, k_cmp, 1)
+        idx = tb.decode_select(q, k_cmp, nxt, wl.topk, wl.n_init, wl.n_local)
+        return tb.decode_attn(q, kp, vp, table, nxt, idx, wl.n_init, wl.n_local)
+
+    def timed(f, n):
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    res = {"paged_step_ms": timed(step, reps),
+           "append_ms": timed(lambda: tb.decode_compress_append(kp, table, cur, nxt, k_cmp, 1), reps)}
+    idx = tb.decode_select(q, k_cmp, nxt, wl.topk, wl.n_init, wl.n_local)
+    res["select_ms"] = timed(lambda: tb.decode_select(q, k_cmp, nxt, wl.topk, wl.n_init, wl.n_local), reps)
+    res["attn_ms"] = timed(lambda: tb.decode_attn(q, kp, vp, table, nxt, idx, wl.n_init, wl.n_local), reps)
+    # the contiguous path at one length (every sequence 32768 keys): it
+    # compresses the whole cache each step
+    x = workloads.make_inputs(wl)
+    qc, kc, vc = (x[n].to(dev) for n in ("q", "k", "v"))
+    plan = tb.AttnPlan(wl.B, wl.H_q, wl.H_kv, wl.S_q, wl.S_k, wl.D, wl.block_size, wl.topk, wl.n_init,
+                       wl.n_local, 0, None, dev)
+    res["contiguous_step_ms"] = timed(lambda: plan.run(qc, kc, vc), reps)
+    return {k: round(v, 4) for k, v in res.items()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +200,7 @@ def main():
     ap.add_argument("--profile-bwd", type=int, default=0,
                     help="only run the sparse attention backward this many times (for profiler runs)")
     ap.add_argument("--no-bwd", action="store_true", help="skip timing the sparse attention backward")
+    ap.add_argument("--no-decode", action="store_true", help="skip timing the paged decode step")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -250,6 +311,8 @@ def main():
         bwd_ms = b0.elapsed_time(b1) / breps
         del o, lse, dout
 
+    decode = None if args.no_decode else time_decode_paged(torch, tb, workloads, dev)
+
     attn_tflops = sparse_flops / (stages["sparse_attn"] * 1e-3) / 1e12
     value = sparse_flops / (ms_step * 1e-3) / 1e12
     traffic = stored_traffic()
@@ -289,6 +352,7 @@ def main():
         "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms_step, 3),
         "sparse_attn_bwd_ms": None if bwd_ms is None else round(bwd_ms, 4),
         "sparse_attn_bwd_tflops": None if bwd_ms is None else round(2 * sparse_flops / (bwd_ms * 1e-3) / 1e12, 2),
+        "decode_b16_32k_paged": decode,
         "algorithmic_flops": {"sparse_attn": sparse_flops, "dense_attn": dense_flops, "select": select_flops,
                               "sparse_attn_bwd": 2 * sparse_flops},
         "wall_ms_per_step": round(wall_ms, 4),
