@@ -313,6 +313,27 @@ def main():
 
     decode = None if args.no_decode else time_decode_paged(torch, tb, workloads, dev)
 
+    # ---- selection with the strided (approximate) LSE: time and recall ---------
+    strided = {}
+    kc = tb.compress_k(k)
+    exact = tb.select_blocks(q, kc, wl.S_k, wl.topk, wl.n_init, wl.n_local)
+    valid = exact >= 0
+    for stride in (2, 4, 8):
+        run = lambda: tb.select_blocks_strided_lse(q, kc, wl.S_k, wl.topk, stride, wl.n_init, wl.n_local)
+        approx = run()
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(5):
+            run()
+        s1.record()
+        torch.cuda.synchronize()
+        hit = (exact.unsqueeze(-1) == approx.unsqueeze(-2)).any(dim=-1) & valid
+        strided[str(stride)] = {"select_ms": round(s0.elapsed_time(s1) / 5, 4),
+                                "recall": round(float(hit.sum()) / max(float(valid.sum()), 1.0), 4)}
+        del approx, hit
+    del exact, valid
+
     attn_tflops = sparse_flops / (stages["sparse_attn"] * 1e-3) / 1e12
     value = sparse_flops / (ms_step * 1e-3) / 1e12
     traffic = stored_traffic()
@@ -353,6 +374,7 @@ def main():
         "sparse_attn_bwd_ms": None if bwd_ms is None else round(bwd_ms, 4),
         "sparse_attn_bwd_tflops": None if bwd_ms is None else round(2 * sparse_flops / (bwd_ms * 1e-3) / 1e12, 2),
         "decode_b16_32k_paged": decode,
+        "select_strided_lse": strided,
         "algorithmic_flops": {"sparse_attn": sparse_flops, "dense_attn": dense_flops, "select": select_flops,
                               "sparse_attn_bwd": 2 * sparse_flops},
         "wall_ms_per_step": round(wall_ms, 4),

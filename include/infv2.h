@@ -99,6 +99,26 @@ int infv2_select_blocks(const void* q, const void* k_cmp,
                         float softmax_scale, void* stream);
 
 /*
+ * Block selection with an approximate per-head log-sum-exp (skill page,
+ * Architecture Overview: the two-pass selection kernel uses an approximate
+ * LSE; the pages do not define it).  Reading: pass 1 evaluates each head's
+ * softmax normaliser on every lse_stride-th visible compressed block only,
+ * block R*x standing for the R = lse_stride blocks R*x .. R*x+R-1 (the last
+ * group for its visible count):
+ *   LSE_h ~ log sum_x min(R, nv - R*x) exp(scale q_h . k_cmp[R*x]).
+ * Pass 2 and the top-k are those of infv2_select_blocks, so R = 1 gives
+ * exactly its result.  Pass 1 streams 1/R of the compressed keys; the
+ * selection can differ from the exact one (only through the per-head
+ * normalisers: a common factor would not change it).  lse_stride: 1, 2, 4
+ * or 8, else INFV2_ERR_UNSUPPORTED.  Layouts as infv2_select_blocks.
+ */
+int infv2_select_blocks_strided_lse(const void* q, const void* k_cmp,
+                                    int32_t* blk_idx, float* blk_score,
+                                    int B, int H_q, int H_kv, int S_q, int S_k, int D,
+                                    int block_size, int topk, int n_init, int n_local,
+                                    float softmax_scale, int lse_stride, void* stream);
+
+/*
  * Block-sparse attention forward (news summary, Technical Mechanism:
  * attention computed only on the selected key-value blocks; skill page,
  * Step 2, sliding_attention, made causal and block-granular).

@@ -134,6 +134,52 @@ def group_scores(q: np.ndarray, k_cmp: np.ndarray, b: int, g: int, i: int,
     return p.sum(axis=0)
 
 
+def group_scores_strided_lse(q: np.ndarray, k_cmp: np.ndarray, b: int, g: int, i: int, r: int, G: int,
+                             scale: float, block_size: int, stride: int) -> np.ndarray:
+    """group_scores with an approximate per-head log-sum-exp.
+
+    [skill page, Architecture Overview, Hardware Kernel] names an LSE
+    approximation in its first pass without defining it.  Reading: the
+    normaliser of head h is estimated from every stride-th visible compressed
+    block, block R*x (R = stride) standing for the R blocks R*x .. R*x+R-1,
+    the last group for its visible count w_x = min(R, nv - R*x):
+        LSE_h ~ log sum_x w_x exp(z_h,R*x).
+    The scores themselves (pass 2) are exact; stride 1 is group_scores.
+    """
+    nv = visible_blocks(i, block_size)
+    if nv == 0:
+        return np.zeros(0)
+    qh = q[b, g * G:(g + 1) * G, r, :]                  # [G, D]
+    z = scale * (qh @ k_cmp[b, g, :nv, :].T)            # [G, nv]
+    xs = np.arange(0, nv, stride)                       # sampled blocks R*x
+    w = np.minimum(stride, nv - xs).astype(np.float64)  # blocks each one stands for
+    zs = z[:, xs] + np.log(w)[None, :]
+    zmax = zs.max(axis=1, keepdims=True)
+    lse = zmax + np.log(np.exp(zs - zmax).sum(axis=1, keepdims=True))
+    return np.exp(z - lse).sum(axis=0)
+
+
+def select_blocks_strided_lse(q: np.ndarray, k_cmp: np.ndarray, S_k: int, topk: int, n_init: int, n_local: int,
+                              block_size: int, scale: float, stride: int, rows=None, return_scores: bool = False):
+    """select_blocks with the approximate normaliser of group_scores_strided_lse."""
+    B, H_q, S_q, _ = q.shape
+    H_kv = k_cmp.shape[1]
+    G = H_q // H_kv
+    off = S_k - S_q
+    rows = np.arange(S_q) if rows is None else np.asarray(rows)
+    idx = np.full((B, H_kv, rows.size, topk), -1, dtype=np.int32)
+    scores = {}
+    for b in range(B):
+        for g in range(H_kv):
+            for n, r in enumerate(rows):
+                i = off + int(r)
+                sig = group_scores_strided_lse(q, k_cmp, b, g, i, int(r), G, scale, block_size, stride)
+                idx[b, g, n] = select_row(sig, i, block_size, topk, n_init, n_local)
+                if return_scores:
+                    scores[(b, g, int(r))] = sig
+    return (idx, scores) if return_scores else idx
+
+
 # ---------------------------------------------------------------------------
 # a3: top-k block selection
 # ---------------------------------------------------------------------------

@@ -1,0 +1,87 @@
+"""GPU selection with the strided (approximate) log-sum-exp vs the fp64 oracle
+of the same approximation, and against the exact selection (recall).
+
+Stage isolation as in test_gpu_parity: the oracle scores the GPU's own
+compressed keys.  Tolerances are in tests/parity.py.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.infv2_oracle as O
+import trainable_block_sparse_mean_amd as tb
+import workloads
+from tests.parity import check_selection, np64, sparse_rows_q
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+CASES = [
+    ("tiny_2k_g8", workloads.TINY, None),
+    ("switch_4k_g16", workloads.SWITCH_SPARSE.with_(S_q=4096, S_k=4096, switch_len=0), np.arange(0, 4096, 7)),
+    ("ragged_sq37_sk3000", workloads.TINY.with_(H_q=32, H_kv=2, S_q=37, S_k=3000, topk=9), None),
+]
+
+
+@pytest.mark.parametrize("stride", [2, 4, 8])
+@pytest.mark.parametrize("name,w,rows", CASES, ids=[c[0] for c in CASES])
+def test_strided_lse_selection_matches_oracle(name, w, rows, stride):
+    log("strided select", name, "stride", stride)
+    x = workloads.make_inputs(w)
+    q, k = x["q"].to(DEV), x["k"].to(DEV)
+    kc = tb.compress_k(k)
+    idx, score = tb.select_blocks_strided_lse(q, kc, w.S_k, w.topk, stride, w.n_init, w.n_local, return_scores=True)
+    torch.cuda.synchronize()
+    rows = np.arange(w.S_q) if rows is None else rows
+    ref, scores = O.select_blocks_strided_lse(sparse_rows_q(q, rows), np64(kc), w.S_k, w.topk, w.n_init, w.n_local,
+                                              64, 1 / math.sqrt(w.D), stride, rows=rows, return_scores=True)
+    gidx = idx.cpu().numpy()[:, :, rows]
+    counts = check_selection(gidx, ref, scores, rows, w.S_q, w.S_k, w.topk, w.n_init, w.n_local)
+    log("  selection rows:", counts)
+    assert counts["near_tie"] <= 0.02 * sum(counts.values())
+    gs = score.cpu().numpy()[:, :, rows]
+    for (b, g, r), sig in list(scores.items())[:: max(1, len(scores) // 100)]:
+        n = int(np.searchsorted(rows, r))
+        for e, j in enumerate(gidx[b, g, n]):
+            if j >= 0:
+                assert abs(gs[b, g, n, e] - sig[j]) <= 1e-4 * max(sig[j], 1e-3), (b, g, r, j)
+
+
+def test_stride_one_is_the_exact_selection_bitwise():
+    w = workloads.SWITCH_SPARSE.with_(S_q=4096, S_k=4096, switch_len=0)
+    x = workloads.make_inputs(w)
+    q, k = x["q"].to(DEV), x["k"].to(DEV)
+    kc = tb.compress_k(k)
+    a = tb.select_blocks(q, kc, w.S_k, w.topk, w.n_init, w.n_local)
+    b = tb.select_blocks_strided_lse(q, kc, w.S_k, w.topk, 1, w.n_init, w.n_local)
+    assert torch.equal(a, b)
+
+
+def test_strided_lse_recall_at_32k():
+    """Fraction of the exact selection that the approximation keeps, at the
+    benchmark shape (i.i.d. N(0,1) inputs).  Logged for every stride; the
+    bounds are regression floors below the measured values."""
+    w = workloads.LONG_32K
+    x = workloads.make_inputs(w)
+    q, k = x["q"].to(DEV), x["k"].to(DEV)
+    kc = tb.compress_k(k)
+    exact = tb.select_blocks(q, kc, w.S_k, w.topk, w.n_init, w.n_local)
+    valid = exact >= 0
+    floors = {2: 0.98, 4: 0.97, 8: 0.96}
+    for stride in (2, 4, 8):
+        approx = tb.select_blocks_strided_lse(q, kc, w.S_k, w.topk, stride, w.n_init, w.n_local)
+        # both rows are ascending: count the exact entries found in the approximate row
+        hit = (exact.unsqueeze(-1) == approx.unsqueeze(-2)).any(dim=-1) & valid
+        recall = float(hit.sum()) / float(valid.sum())
+        log(f"  stride {stride}: recall {recall:.4f}")
+        assert recall >= floors[stride], (stride, recall)

@@ -103,6 +103,15 @@ def _paged_drops_last_key(pages, table_row, length, block_size):
     return impl.__dict__["_real_paged"](pages, table_row, max(length - 1, 1), block_size)
 
 
+def _strided_unweighted(q, k_cmp, b, g, i, r, G, scale, block_size, stride):
+    nv = impl.visible_blocks(i, block_size)
+    qh = q[b, g * G:(g + 1) * G, r, :]
+    z = scale * (qh @ k_cmp[b, g, :nv, :].T)
+    zs = z[:, ::stride]                                  # samples not weighted by their group size
+    lse = np.log(np.exp(zs).sum(axis=1, keepdims=True))
+    return np.exp(z - lse).sum(axis=0)
+
+
 MUTANTS = [
     ("group_scores", _scores_no_normalisation, [pins.test_scores_sum_to_group_size_and_nonnegative,
                                                 pins.test_scores_hand_derived_golden]),
@@ -120,6 +129,8 @@ MUTANTS = [
                                                  pins.test_backward_dense_case_matches_torch_autograd_fp64]),
     ("_softmax_attend_grad", _grad_dv_unnormalised, [pins.test_backward_sum_invariants,
                                                      pins.test_backward_dense_case_matches_torch_autograd_fp64]),
+    ("group_scores_strided_lse", _strided_unweighted, [pins.test_strided_lse_is_exact_when_each_group_shares_one_key,
+                                                       pins.test_strided_lse_hand_case]),
     ("paged_sequence", _paged_blocks_reversed, [pins.test_paged_sequence_inverts_the_page_scatter,
                                                 pins.test_decode_paged_equals_per_sequence_pipeline]),
     ("paged_sequence", _paged_drops_last_key, [pins.test_paged_sequence_inverts_the_page_scatter,

@@ -612,3 +612,41 @@ def test_decode_short_sequence_is_dense_softmax():
             z = 0.3 * ks[b][h // G] @ q[b, h]
             np.testing.assert_allclose(out[b, h], scipy.special.softmax(z) @ vs[b][h // G], rtol=1e-12, atol=1e-12)
             np.testing.assert_allclose(lse[b, h], scipy.special.logsumexp(z), rtol=1e-12)
+
+
+# ------------------------------------------------------- approximate LSE ----
+
+def test_strided_lse_stride_one_is_the_exact_score():
+    rng = np.random.default_rng(41)
+    q = rng.standard_normal((1, 4, 3, 8))
+    kc = rng.standard_normal((1, 2, 40, 8))
+    for i in (63, 64, 700, 2559):
+        np.testing.assert_allclose(O.group_scores_strided_lse(q, kc, 0, 1, i, 2, 2, 0.7, 64, 1),
+                                   O.group_scores(q, kc, 0, 1, i, 2, 2, 0.7, 64), rtol=1e-13, atol=1e-16)
+
+
+def test_strided_lse_is_exact_when_each_group_shares_one_key():
+    """If the R blocks of every group have the same compressed key, a group's
+    sample times its visible count is its exact sum: the approximate scores
+    equal the exact ones, also for a last group cut short."""
+    rng = np.random.default_rng(42)
+    R = 4
+    base = rng.standard_normal((1, 2, 10, 8))
+    kc = np.repeat(base, R, axis=2)                     # 40 blocks, groups of 4 equal keys
+    q = rng.standard_normal((1, 4, 1, 8))
+    for i in (64 * 37 - 1, 64 * 40 - 1, 64 * 9 + 5):    # nv = 37 (last group 1 of 4), 40, 9
+        np.testing.assert_allclose(O.group_scores_strided_lse(q, kc, 0, 0, i, 0, 2, 0.5, 64, R),
+                                   O.group_scores(q, kc, 0, 0, i, 0, 2, 0.5, 64), rtol=1e-13, atol=1e-15)
+
+
+def test_strided_lse_hand_case():
+    """One head, nv = 5, stride 2: samples are blocks 0, 2, 4 standing for 2,
+    2 and 1 blocks, so LSE = log(2 e^z0 + 2 e^z2 + e^z4)."""
+    q = np.zeros((1, 1, 1, 2))
+    q[0, 0, 0] = [1.0, 0.0]
+    kc = np.zeros((1, 1, 5, 2))
+    kc[0, 0, :, 0] = [0.5, -1.0, 2.0, 0.25, -0.5]       # z_j = scale * k_j0 with scale 1
+    sig = O.group_scores_strided_lse(q, kc, 0, 0, 64 * 5 - 1, 0, 1, 1.0, 64, 2)
+    z = kc[0, 0, :, 0]
+    lse = math.log(2 * math.exp(z[0]) + 2 * math.exp(z[2]) + math.exp(z[4]))
+    np.testing.assert_allclose(sig, np.exp(z - lse), rtol=1e-14)

@@ -31,6 +31,7 @@ SIGNATURES = {
     "infv2_abi_version": (_c_int, []),
     "infv2_compress_k": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
     "infv2_select_blocks": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 10 + [_c_float, _vp]),
+    "infv2_select_blocks_strided_lse": (_c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 10 + [_c_float, _c_int, _vp]),
     "infv2_sparse_workspace_bytes": (_c_size, [_c_int] * 8),
     "infv2_sparse_attn_fwd": (_c_int, [_vp] * 6 + [_c_int] * 10 + [_c_float, _vp, _c_size, _vp]),
     "infv2_sparse_bwd_workspace_bytes": (_c_size, [_c_int] * 8),
@@ -126,6 +127,22 @@ def select_blocks(q: torch.Tensor, k_cmp: torch.Tensor, S_k: int, topk: int, n_i
     score = torch.empty_like(idx, dtype=torch.float32) if return_scores else None
     _call("infv2_select_blocks", _ptr(q), _ptr(k_cmp), _ptr(idx), _ptr(score), B, H_q, H_kv, S_q, S_k, D,
           block_size, topk, n_init, n_local, _scale(softmax_scale), _stream())
+    return (idx, score) if return_scores else idx
+
+
+def select_blocks_strided_lse(q: torch.Tensor, k_cmp: torch.Tensor, S_k: int, topk: int, lse_stride: int,
+                              n_init: int = 1, n_local: int = 2, softmax_scale=None, block_size: int = 64,
+                              return_scores: bool = False):
+    """select_blocks with the approximate per-head log-sum-exp over every
+    lse_stride-th compressed block (1, 2, 4 or 8; 1 is exact)."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k_cmp, "k_cmp", torch.bfloat16, 4)
+    B, H_q, S_q, D = q.shape
+    H_kv = k_cmp.shape[1]
+    idx = torch.empty(B, H_kv, S_q, topk, dtype=torch.int32, device=q.device)
+    score = torch.empty_like(idx, dtype=torch.float32) if return_scores else None
+    _call("infv2_select_blocks_strided_lse", _ptr(q), _ptr(k_cmp), _ptr(idx), _ptr(score), B, H_q, H_kv, S_q, S_k,
+          D, block_size, topk, n_init, n_local, _scale(softmax_scale), lse_stride, _stream())
     return (idx, score) if return_scores else idx
 
 

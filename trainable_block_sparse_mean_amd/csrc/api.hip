@@ -145,6 +145,25 @@ int infv2_select_blocks(const void* q, const void* k_cmp, int32_t* blk_idx, floa
                                                 s, static_cast<hipStream_t>(stream)));
 }
 
+int infv2_select_blocks_strided_lse(const void* q, const void* k_cmp, int32_t* blk_idx, float* blk_score, int B,
+                                    int H_q, int H_kv, int S_q, int S_k, int D, int block_size, int topk,
+                                    int n_init, int n_local, float softmax_scale, int lse_stride, void* stream) {
+  if (lse_stride != 1 && lse_stride != 2 && lse_stride != 4 && lse_stride != 8) return INFV2_ERR_UNSUPPORTED;
+  int st = check_shape(B, H_q, H_kv, S_q, S_k, D);
+  if (st != INFV2_OK) return st;
+  st = check_sparse_params(block_size, topk, n_init, n_local);
+  if (st != INFV2_OK) return st;
+  if (num_blocks(S_k, block_size) > kMaxSelectBlocks) return INFV2_ERR_UNSUPPORTED;
+  if (B == 0 || S_q == 0 || topk == 0) return INFV2_OK;
+  if (!tensor_ok(q) || !tensor_ok(k_cmp) || !tensor_ok(blk_idx)) return INFV2_ERR_INVALID;
+  if (blk_score && !aligned(blk_score, 16)) return INFV2_ERR_INVALID;
+  const AttnShape s = make_shape(B, H_q, H_kv, S_q, S_k, block_size, topk, n_init, n_local,
+                                 scale_log2(softmax_scale, D), 1);
+  return hip_status(infv2::launch_select_blocks(static_cast<const uint16_t*>(q),
+                                                static_cast<const uint16_t*>(k_cmp), blk_idx, blk_score, s,
+                                                static_cast<hipStream_t>(stream), lse_stride));
+}
+
 size_t infv2_sparse_workspace_bytes(int B, int H_q, int H_kv, int S_q, int S_k, int D, int block_size,
                                     int topk) {
   if (check_shape(B, H_q, H_kv, S_q, S_k, D) != INFV2_OK || block_size != infv2::kBS || topk < 0) return 0;

@@ -60,8 +60,9 @@ hipError_t launch_compress_k(const uint16_t* k, uint16_t* k_cmp, int B, int H_kv
 hipError_t launch_compress_append(const uint16_t* k_pages, const AttnShape& s, const int* old_len,
                                   uint16_t* k_cmp, int max_new, hipStream_t stream);
 
+// lse_stride 1: exact pass-1 log-sum-exp; 2, 4 or 8: the strided approximation
 hipError_t launch_select_blocks(const uint16_t* q, const uint16_t* k_cmp, int32_t* blk_idx,
-                                float* blk_score, const AttnShape& s, hipStream_t stream);
+                                float* blk_score, const AttnShape& s, hipStream_t stream, int lse_stride = 1);
 
 // bytes of workspace the attention kernels need (V relayout + split partials)
 size_t attn_workspace_bytes(const AttnShape& s);

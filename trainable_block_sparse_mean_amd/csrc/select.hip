@@ -117,7 +117,11 @@ __device__ __forceinline__ void topk_row(const float* cand, int nC, int topk, in
   }
 }
 
-template <int CH>
+// R = 1: exact log-sum-exp in pass 1.  R > 1: the approximate one of
+// infv2_select_blocks_strided_lse - pass 1 scores only every R-th visible
+// compressed block, each standing for the R blocks of its group (the last
+// group for its visible count), so it streams 1/R of the compressed keys.
+template <int CH, int R>
 __global__ __launch_bounds__(kSelWaves * 64) void select_blocks_kernel(const uint16_t* __restrict__ q,
                                                                        const uint16_t* __restrict__ kc,
                                                                        int32_t* __restrict__ blk_idx,
@@ -143,7 +147,8 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_blocks_kernel(const uin
   const int nv = active ? (off + r + 1) / kBS : 0;  // fully visible blocks
   const int r_last = min(r0 + kSelWaves, s.S_q) - 1;
   const int nv_max = (off + r_last + 1) / kBS;      // largest nv of the workgroup
-  const int nch = (nv_max + CH - 1) / CH;
+  const int nch = (nv_max + CH - 1) / CH;             // pass 2 chunks (every block)
+  const int nch1 = ((nv_max + R - 1) / R + CH - 1) / CH;  // pass 1 chunks (every R-th block)
   float* sig = sig_all + wave * sel_stride(s.NB);
   const float sl2 = s.scale_log2;
 
@@ -166,11 +171,10 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_blocks_kernel(const uin
   // that row's slot (rows past NB - 1 re-read row NB - 1; never used)
   const int drow = 4 * wave + (lane >> 4);
   const uint32_t dcol = static_cast<uint32_t>(((lane & 15) ^ swz(drow)) << 4);
-  const int nit = 2 * nch;  // both passes stream the same chunks
+  const int nit = nch1 + nch;  // pass 1 chunks, then pass 2 chunks
   auto stage = [&](int it) {
     if (wave < kDmaWaves && it < nit) {
-      const int c = it < nch ? it : it - nch;
-      const int j = min(c * CH + drow, s.NB - 1);
+      const int j = min(it < nch1 ? R * (it * CH + drow) : (it - nch1) * CH + drow, s.NB - 1);
       dma16(kg, static_cast<uint32_t>(j) * kSelRowBytes + dcol,
             ring + (it % kSelSlots) * kSlotBytes + wave * 1024);
     }
@@ -243,12 +247,12 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_blocks_kernel(const uin
 
   stage(0);
   stage(1);
-  for (int it = 0; it < nit; ++it) {  // chunk it % nch: pass 1, then pass 2
+  for (int it = 0; it < nit; ++it) {  // pass 1 chunks, then pass 2 chunks
     if (it + 1 < nit) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // chunk `it` is in LDS; every wave is done with chunk it - 1
     stage(it + 2);    // into the slot chunk it - 1 used
-    if (it == nch) {
+    if (it == nch1) {
       // end of pass 1: merge the 16 lanes of each row (one head per register i)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -259,27 +263,42 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_blocks_kernel(const uin
         lse2[i] = 4 * gq + i < s.G ? m[i] + log2f(l[i]) : INFINITY;
       }
     }
-    const int c = it < nch ? it : it - nch;
-    const int jc = c * CH;  // first block of the chunk
-    if (!active || jc >= nv) continue;
     const unsigned char* buf = sel_smem + (it % kSelSlots) * kSlotBytes;
-    const bool full = jc + CH <= nv;
-    if (it < nch) {
-      if (full) {
+    if (it < nch1) {
+      // pass 1 over rows jc .. jc + CH - 1 of the sampled sequence: sampled
+      // row x is block R * x, standing for blocks R*x .. R*x + R-1 that are
+      // visible (weight w: log2(w) / sl2 added to its scores)
+      const int jc = it * CH;
+      if (!active || R * jc >= nv) continue;
+      if (R * (jc + CH) <= nv) {
         floatx4 acc[kTiles];
         scores(buf, 0, AllTiles{}, acc);
+        if constexpr (R > 1) {
+          const float wl = log2f(static_cast<float>(R)) / sl2;
+#pragma unroll
+          for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[t][i] += wl;
+        }
         lse_update(acc, AllTiles{});
       } else {
-        for (int t = 0; t < kTiles && jc + 16 * t < nv; ++t) {
+        for (int t = 0; t < kTiles && R * (jc + 16 * t) < nv; ++t) {
           floatx4 acc[1];
           scores(buf, t, OneTile{}, acc);
-          const bool vis = jc + 16 * t + hl < nv;
+          const int j = R * (jc + 16 * t + hl);
+          const int w = min(R, nv - j);  // visible blocks the sample stands for (<= 0: none)
+          const float wl = R > 1 && w > 0 ? log2f(static_cast<float>(w)) / sl2 : 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[0][i] = vis ? acc[0][i] : -INFINITY;
+          for (int i = 0; i < 4; ++i) acc[0][i] = w > 0 ? (R > 1 ? acc[0][i] + wl : acc[0][i]) : -INFINITY;
           lse_update(acc, OneTile{});
         }
       }
-    } else {
+      continue;
+    }
+    const int jc = (it - nch1) * CH;  // first block of the pass 2 chunk
+    if (!active || jc >= nv) continue;
+    const bool full = jc + CH <= nv;
+    {
       if (full) {
         floatx4 acc[kTiles];
         scores(buf, 0, AllTiles{}, acc);
@@ -330,18 +349,29 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_blocks_kernel(const uin
   else topk_row<32>(sig + lo, nC, s.topk, lo, out, out_s, lane);
 }
 
-hipError_t launch_select_blocks(const uint16_t* q, const uint16_t* k_cmp, int32_t* blk_idx,
-                                float* blk_score, const AttnShape& s, hipStream_t stream) {
-  if (s.B == 0 || s.S_q == 0) return hipSuccess;
+template <int R>
+static hipError_t launch_select_r(const uint16_t* q, const uint16_t* k_cmp, int32_t* blk_idx, float* blk_score,
+                                  const AttnShape& s, hipStream_t stream) {
   dim3 grid((s.S_q + kSelWaves - 1) / kSelWaves, s.B * s.H_kv);
   // 64-block chunks where the LDS holds them, else 32 (NB <= 2048 fits)
   if (select_lds<64>(s.NB) <= kSelLdsMax)
-    hipLaunchKernelGGL(select_blocks_kernel<64>, grid, dim3(64 * kSelWaves), select_lds<64>(s.NB), stream, q, k_cmp,
-                       blk_idx, blk_score, s);
+    hipLaunchKernelGGL((select_blocks_kernel<64, R>), grid, dim3(64 * kSelWaves), select_lds<64>(s.NB), stream, q,
+                       k_cmp, blk_idx, blk_score, s);
   else
-    hipLaunchKernelGGL(select_blocks_kernel<32>, grid, dim3(64 * kSelWaves), select_lds<32>(s.NB), stream, q, k_cmp,
-                       blk_idx, blk_score, s);
+    hipLaunchKernelGGL((select_blocks_kernel<32, R>), grid, dim3(64 * kSelWaves), select_lds<32>(s.NB), stream, q,
+                       k_cmp, blk_idx, blk_score, s);
   return hipGetLastError();
+}
+
+hipError_t launch_select_blocks(const uint16_t* q, const uint16_t* k_cmp, int32_t* blk_idx,
+                                float* blk_score, const AttnShape& s, hipStream_t stream, int lse_stride) {
+  if (s.B == 0 || s.S_q == 0) return hipSuccess;
+  switch (lse_stride) {
+    case 2: return launch_select_r<2>(q, k_cmp, blk_idx, blk_score, s, stream);
+    case 4: return launch_select_r<4>(q, k_cmp, blk_idx, blk_score, s, stream);
+    case 8: return launch_select_r<8>(q, k_cmp, blk_idx, blk_score, s, stream);
+    default: return launch_select_r<1>(q, k_cmp, blk_idx, blk_score, s, stream);
+  }
 }
 
 }  // namespace infv2
