@@ -435,6 +435,79 @@ def attention(q, k, v, block_size: int, topk: int, n_init: int, n_local: int,
 
 
 # ---------------------------------------------------------------------------
+# The compressed-attention branch and the mix of patterns (next row)
+# ---------------------------------------------------------------------------
+
+
+def compress_v(v: np.ndarray, block_size: int) -> tuple[np.ndarray, np.ndarray]:
+    """Block-mean compression of the values.
+
+    [skill page, Step 2, compressed_attention]: the values are compressed
+    exactly like the keys (zero padding, mean over each block's tokens, the
+    divisor being the block size).  Rounded once to bf16, nearest-even.
+    Returns (v_cmp_bits uint16, v_cmp float64), both [B, H, ceil(S/BS), D].
+    """
+    return compress_k(v, block_size)
+
+
+def compressed_attn(q, k_cmp, v_cmp, S_k: int, block_size: int, scale: float, rows=None):
+    """Output of the compressed-attention branch.
+
+    [skill page, Step 2, compressed_attention]: every query attends the
+    compressed keys with a softmax of the scaled products and takes the
+    weighted sum of the compressed values.
+
+    Readings: causal like block scoring (visible_blocks): the query at
+    position i sees only the nv = floor((i+1)/BS) blocks that lie wholly at
+    or before it; the sketch's unmasked softmax would let it read values of
+    later tokens.  The sketch's last step (repeating each row once per token
+    of a block) does not fit its own shapes, whose rows are already one per
+    query; the output here is one row per query.  A query that sees no block
+    (its position is below BS - 1) gets a zero output and a log-sum-exp of
+    -inf.
+
+    q [B,H_q,S_q,D]; k_cmp, v_cmp float64 [B,H_kv,NB,D] (NB >= the visible
+    blocks of the last query).  Returns (out [B,H_q,n_rows,D], lse
+    [B,H_q,n_rows]) for the query rows ``rows`` (default: all).
+    """
+    B, H_q, S_q, D = q.shape
+    H_kv = k_cmp.shape[1]
+    G = H_q // H_kv
+    off = S_k - S_q
+    rows = np.arange(S_q) if rows is None else np.asarray(rows)
+    out = np.zeros((B, H_q, rows.size, D))
+    lse = np.full((B, H_q, rows.size), -np.inf)
+    for b in range(B):
+        for g in range(H_kv):
+            for n, r in enumerate(rows):
+                nv = visible_blocks(off + int(r), block_size)
+                if nv == 0:
+                    continue
+                o, m = _softmax_attend(q[b, g * G:(g + 1) * G, int(r), :],
+                                       k_cmp[b, g, :nv, :], v_cmp[b, g, :nv, :], scale)
+                out[b, g * G:(g + 1) * G, n, :] = o
+                lse[b, g * G:(g + 1) * G, n] = m
+    return out, lse
+
+
+def mix_patterns(outputs, weights) -> np.ndarray:
+    """Weighted sum of pattern outputs.
+
+    [skill page, Step 3: Switchable Attention with Pattern Router]: the
+    sparse context is the sum of the pattern outputs, each multiplied by its
+    coefficient.  Readings: the coefficients are given numbers (the page
+    learns them through a softmax over a trainable vector, which a
+    parameter-free method has no place for); the block-sparse output, whose
+    one softmax already spans the selected, initial and window blocks, is one
+    pattern and the compressed branch another.
+    """
+    out = np.zeros(np.shape(outputs[0]))
+    for w, o in zip(weights, outputs):
+        out = out + float(w) * np.asarray(o, dtype=np.float64)
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Backward of the block-sparse attention (next row: training)
 # ---------------------------------------------------------------------------
 

@@ -112,6 +112,25 @@ def _strided_unweighted(q, k_cmp, b, g, i, r, G, scale, block_size, stride):
     return np.exp(z - lse).sum(axis=0)
 
 
+def _cmp_unmasked(q, k_cmp, v_cmp, S_k, block_size, scale, rows=None):
+    nb = k_cmp.shape[2]
+    return impl.__dict__["_real_cmp"](q, k_cmp, v_cmp, nb * block_size + q.shape[2] - 1, block_size, scale, rows)
+
+
+def _cmp_sees_own_block(q, k_cmp, v_cmp, S_k, block_size, scale, rows=None):
+    # counts the block holding the query as visible (floor(i/BS) + 1 blocks)
+    return impl.__dict__["_real_cmp"](q, k_cmp, v_cmp, min(S_k + block_size - 1, k_cmp.shape[2] * block_size),
+                                      block_size, scale, rows)
+
+
+def _cmp_values_from_keys(q, k_cmp, v_cmp, S_k, block_size, scale, rows=None):
+    return impl.__dict__["_real_cmp"](q, k_cmp, k_cmp, S_k, block_size, scale, rows)
+
+
+def _mix_unweighted(outputs, weights):
+    return sum(np.asarray(o, dtype=np.float64) for o in outputs)
+
+
 MUTANTS = [
     ("group_scores", _scores_no_normalisation, [pins.test_scores_sum_to_group_size_and_nonnegative,
                                                 pins.test_scores_hand_derived_golden]),
@@ -131,6 +150,12 @@ MUTANTS = [
                                                      pins.test_backward_dense_case_matches_torch_autograd_fp64]),
     ("group_scores_strided_lse", _strided_unweighted, [pins.test_strided_lse_is_exact_when_each_group_shares_one_key,
                                                        pins.test_strided_lse_hand_case]),
+    ("compressed_attn", _cmp_unmasked, [pins.test_compressed_attn_zero_keys_average_the_visible_blocks]),
+    ("compressed_attn", _cmp_sees_own_block, [pins.test_compressed_attn_zero_keys_average_the_visible_blocks,
+                                              pins.test_compressed_attn_constant_values]),
+    ("compressed_attn", _cmp_values_from_keys, [pins.test_compressed_attn_zero_keys_average_the_visible_blocks,
+                                                pins.test_compressed_attn_single_head_weights_are_the_block_scores]),
+    ("mix_patterns", _mix_unweighted, [pins.test_mix_patterns_closed_forms]),
     ("paged_sequence", _paged_blocks_reversed, [pins.test_paged_sequence_inverts_the_page_scatter,
                                                 pins.test_decode_paged_equals_per_sequence_pipeline]),
     ("paged_sequence", _paged_drops_last_key, [pins.test_paged_sequence_inverts_the_page_scatter,
@@ -142,6 +167,7 @@ MUTANTS = [
 def test_pin_catches_mutant(monkeypatch, name, mutant, catchers):
     monkeypatch.setattr(impl, "_real_grad", impl._softmax_attend_grad, raising=False)
     monkeypatch.setattr(impl, "_real_paged", impl.paged_sequence, raising=False)
+    monkeypatch.setattr(impl, "_real_cmp", impl.compressed_attn, raising=False)
     monkeypatch.setattr(impl, name, mutant)
     for pin in catchers:
         with pytest.raises(AssertionError):

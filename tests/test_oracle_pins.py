@@ -650,3 +650,110 @@ def test_strided_lse_hand_case():
     z = kc[0, 0, :, 0]
     lse = math.log(2 * math.exp(z[0]) + 2 * math.exp(z[2]) + math.exp(z[4]))
     np.testing.assert_allclose(sig, np.exp(z - lse), rtol=1e-14)
+
+
+# ------------------------------------------------ compressed-attention branch ----
+
+def test_compressed_attn_zero_keys_average_the_visible_blocks():
+    """With all keys zero every compressed key scores the same, so each query
+    averages the compressed values of the blocks it sees.  V is constant in
+    each block (bf16 values), so that average is the plain mean of V over the
+    first 64 * nv tokens: pins nv = floor((i+1)/64) and that the values, not
+    the keys, are averaged."""
+    rng = np.random.default_rng(51)
+    B, H_kv, G, S, D = 1, 2, 2, 64 * 6 + 17, 8
+    per_block = rnd_bf16(rng, B, H_kv, 7, D)
+    v = np.repeat(per_block, 64, axis=2)[:, :, :S]
+    k = np.zeros((B, H_kv, S, D))
+    _, kc = O.compress_k(k, 64)
+    _, vc = O.compress_v(np.repeat(per_block, 64, axis=2), 64)
+    q = rnd_bf16(rng, B, H_kv * G, S, D)
+    out, lse = O.compressed_attn(q, kc, vc, S, 64, 0.5)
+    for i in range(S):
+        nv = (i + 1) // 64
+        for h in range(H_kv * G):
+            if nv == 0:
+                assert not out[0, h, i].any() and lse[0, h, i] == -np.inf
+                continue
+            np.testing.assert_allclose(out[0, h, i], v[0, h // G, :64 * nv].mean(axis=0), rtol=1e-13, atol=1e-15)
+            np.testing.assert_allclose(lse[0, h, i], math.log(nv), rtol=1e-13)
+
+
+@pytest.mark.parametrize("S_q,S_k", [(200, 200), (70, 333), (1, 640)])
+def test_compressed_attn_matches_sdpa_with_block_end_positions(S_q, S_k):
+    """Compressed key j stands at the position of its block's last token
+    (64 j + 63): a query sees it iff that position is at or before its own,
+    the textbook causal mask over those positions.  torch's SDPA in fp64
+    with that mask (bottom-right aligned queries) on the rows that see at
+    least one block; the others are zero with lse -inf."""
+    rng = np.random.default_rng(52)
+    B, H_kv, G, D = 2, 2, 4, 16
+    nb = (S_k + 63) // 64
+    q = rnd_bf16(rng, B, H_kv * G, S_q, D)
+    kc = rnd_bf16(rng, B, H_kv, nb, D)
+    vc = rnd_bf16(rng, B, H_kv, nb, D)
+    out, lse = O.compressed_attn(q, kc, vc, S_k, 64, 0.3)
+    pos = torch.arange(S_q) + (S_k - S_q)
+    mask = (64 * torch.arange(nb) + 63)[None, :] <= pos[:, None]          # [S_q, nb]
+    seen = mask.any(dim=1).numpy()
+    tq = torch.from_numpy(q)
+    tk = torch.from_numpy(kc).repeat_interleave(G, dim=1)
+    tv = torch.from_numpy(vc).repeat_interleave(G, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.3).numpy()
+    z = (0.3 * (tq @ tk.transpose(-1, -2))).masked_fill(~mask, float("-inf"))
+    ref_lse = torch.logsumexp(z, dim=-1).numpy()
+    np.testing.assert_allclose(out[:, :, seen], ref[:, :, seen], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse[:, :, seen], ref_lse[:, :, seen], rtol=1e-12)
+    assert not out[:, :, ~seen].any() and np.all(lse[:, :, ~seen] == -np.inf)
+
+
+def test_compressed_attn_single_head_weights_are_the_block_scores():
+    """With one head per group the selection score of a block is that head's
+    softmax weight over the visible compressed keys, so the branch output is
+    the score-weighted sum of the compressed values."""
+    rng = np.random.default_rng(53)
+    q = rnd_bf16(rng, 1, 3, 50, 32)
+    kc = rnd_bf16(rng, 1, 3, 9, 32)
+    vc = rnd_bf16(rng, 1, 3, 9, 32)
+    S_k = 64 * 9
+    out, _ = O.compressed_attn(q, kc, vc, S_k, 64, 0.4)
+    off = S_k - 50
+    for h in range(3):
+        for r in (0, 17, 49):
+            sig = O.group_scores(q, kc, 0, h, off + r, r, 1, 0.4, 64)
+            np.testing.assert_allclose(out[0, h, r], sig @ vc[0, h, :sig.size], rtol=1e-12, atol=1e-14)
+
+
+def test_compressed_attn_last_query_is_the_unmasked_softmax():
+    """The last token of a sequence of whole blocks sees every block: there
+    the causal branch is the sketch's unmasked softmax over all compressed
+    keys (scipy's softmax)."""
+    rng = np.random.default_rng(54)
+    q = rnd_bf16(rng, 1, 2, 1, 16)
+    kc = rnd_bf16(rng, 1, 1, 11, 16)
+    vc = rnd_bf16(rng, 1, 1, 11, 16)
+    out, lse = O.compressed_attn(q, kc, vc, 64 * 11, 64, 0.25)
+    for h in range(2):
+        z = 0.25 * kc[0, 0] @ q[0, h, 0]
+        np.testing.assert_allclose(out[0, h, 0], scipy.special.softmax(z) @ vc[0, 0], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse[0, h, 0], scipy.special.logsumexp(z), rtol=1e-13)
+
+
+def test_compressed_attn_constant_values():
+    rng = np.random.default_rng(55)
+    q = rnd_bf16(rng, 1, 4, 130, 8)
+    kc = rnd_bf16(rng, 1, 2, 3, 8)
+    vc = np.full((1, 2, 3, 8), -1.75)
+    out, _ = O.compressed_attn(q, kc, vc, 130, 64, 1.0)
+    np.testing.assert_array_equal(out[:, :, :63], 0.0)
+    np.testing.assert_allclose(out[:, :, 63:], -1.75, rtol=1e-14)
+
+
+def test_mix_patterns_closed_forms():
+    rng = np.random.default_rng(56)
+    a, b = rng.standard_normal((2, 3, 5, 8)), rng.standard_normal((2, 3, 5, 8))
+    np.testing.assert_array_equal(O.mix_patterns([a, b], [1.0, 0.0]), a)
+    np.testing.assert_array_equal(O.mix_patterns([a, b], [0.0, 1.0]), b)
+    np.testing.assert_allclose(O.mix_patterns([a, b], [0.25, 0.75]), 0.25 * a + 0.75 * b, rtol=1e-15)
+    c = np.full((2, 3, 5, 8), 3.0)
+    np.testing.assert_allclose(O.mix_patterns([c, -c, c], [0.5, 0.25, 0.125]), 3.0 * 0.375, rtol=1e-15)
