@@ -201,6 +201,8 @@ def main():
                     help="only run the sparse attention backward this many times (for profiler runs)")
     ap.add_argument("--no-bwd", action="store_true", help="skip timing the sparse attention backward")
     ap.add_argument("--no-decode", action="store_true", help="skip timing the paged decode step")
+    ap.add_argument("--no-compressed", action="store_true",
+                    help="skip timing the compressed-attention branch and the mixed output")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -334,6 +336,47 @@ def main():
         del approx, hit
     del exact, valid
 
+    # ---- the compressed-attention branch, alone and mixed with the sparse output --
+    compressed = None
+    if not args.no_compressed:
+        # one (query head, visible compressed key) pair costs 4 D flops, as for
+        # a key of the sparse attention: the same pairs and count as the two
+        # scoring passes of selection (2 x 2 D each)
+        cmp_flops = select_flops
+        kc, vc = tb.compress_k(k), tb.compress_v(v)
+        idx = tb.select_blocks(q, kc, wl.S_k, wl.topk, wl.n_init, wl.n_local)
+        o_sp, _ = tb.sparse_attn_fwd(q, k, v, idx, wl.n_init, wl.n_local)
+        buf = torch.empty_like(q)
+
+        def mixed_step():
+            kc2, vc2 = tb.compress_k(k), tb.compress_v(v)
+            idx2 = tb.select_blocks(q, kc2, wl.S_k, wl.topk, wl.n_init, wl.n_local)
+            o2, _ = tb.sparse_attn_fwd(q, k, v, idx2, wl.n_init, wl.n_local, return_lse=False)
+            tb.compressed_attn_fwd(q, kc2, vc2, wl.S_k, o_sparse=o2, w_sparse=0.5, w_cmp=0.5, out=o2,
+                                   return_lse=False)
+
+        def avg_ms(f, n=5):
+            f()
+            torch.cuda.synchronize()
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record()
+            for _ in range(n):
+                f()
+            c1.record()
+            torch.cuda.synchronize()
+            return c0.elapsed_time(c1) / n
+
+        branch_ms = avg_ms(lambda: tb.compressed_attn_fwd(q, kc, vc, wl.S_k, out=buf, return_lse=False))
+        mix_ms = avg_ms(lambda: tb.compressed_attn_fwd(q, kc, vc, wl.S_k, o_sparse=o_sp, w_sparse=0.5, w_cmp=0.5,
+                                                       out=buf, return_lse=False))
+        compressed = {"branch_ms": round(branch_ms, 4),
+                      "branch_tflops": round(cmp_flops / (branch_ms * 1e-3) / 1e12, 2),
+                      "branch_mixed_ms": round(mix_ms, 4),
+                      "compress_v_ms": round(avg_ms(lambda: tb.compress_v(v)), 4),
+                      "mixed_step_ms": round(avg_ms(mixed_step), 4),
+                      "branch_flops": cmp_flops}
+        del kc, vc, idx, o_sp, buf
+
     attn_tflops = sparse_flops / (stages["sparse_attn"] * 1e-3) / 1e12
     value = sparse_flops / (ms_step * 1e-3) / 1e12
     traffic = stored_traffic()
@@ -375,6 +418,7 @@ def main():
         "sparse_attn_bwd_tflops": None if bwd_ms is None else round(2 * sparse_flops / (bwd_ms * 1e-3) / 1e12, 2),
         "decode_b16_32k_paged": decode,
         "select_strided_lse": strided,
+        "compressed_branch": compressed,
         "algorithmic_flops": {"sparse_attn": sparse_flops, "dense_attn": dense_flops, "select": select_flops,
                               "sparse_attn_bwd": 2 * sparse_flops},
         "wall_ms_per_step": round(wall_ms, 4),

@@ -270,6 +270,50 @@ int infv2_decode_attn(const void* q, const void* k_pages, const void* v_pages,
                       float softmax_scale,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Compressed-attention branch and the mix of patterns (skill page, Step 2,
+ * compressed_attention: queries attend block means of the keys and values;
+ * Step 3: the sparse context is a weighted sum of the pattern outputs).
+ * Readings: the branch is causal like block scoring - the query at position
+ * i (bottom-right aligned, i = S_k - S_q + r) attends the compressed keys of
+ * the nv = floor((i+1)/block_size) blocks wholly at or before it; the mixing
+ * coefficients are arguments (the page learns them; this library has no
+ * parameters); the block-sparse output (selected, initial and window blocks
+ * in one softmax) is one pattern, this branch the other.
+ *   q                bf16 [B][H_q][S_q][D]
+ *   k_cmp, v_cmp     bf16 [B][H_kv][NB][D], NB = ceil(S_k/block_size), from
+ *                    infv2_compress_k and infv2_compress_v
+ *   o_sparse         bf16 [B][H_q][S_q][D] (optional, may be NULL): e.g.
+ *                    the output of infv2_sparse_attn_fwd
+ *   out              bf16 [B][H_q][S_q][D]; may be o_sparse itself
+ *   lse              fp32 [B][H_q][S_q] (optional): the branch's own natural
+ *                    log-sum-exp, -inf where nv = 0
+ * out = w_cmp * softmax_{j<nv}(scale q.k_cmp_j) v_cmp  [+ w_sparse * o_sparse]
+ * A query with nv = 0 (position below block_size - 1) contributes a zero
+ * branch output.  w_sparse, w_cmp must be finite (else INFV2_ERR_INVALID).
+ * No workspace.  Errors as for infv2_sparse_attn_fwd.
+ */
+int infv2_compress_v(const void* v, void* v_cmp,
+                     int B, int H_kv, int S_k, int D, int block_size,
+                     void* stream);
+int infv2_compressed_attn_fwd(const void* q, const void* k_cmp, const void* v_cmp,
+                              const void* o_sparse, void* out, float* lse,
+                              int B, int H_q, int H_kv, int S_q, int S_k, int D,
+                              int block_size, float softmax_scale,
+                              float w_sparse, float w_cmp, void* stream);
+
+/* The compressed-attention branch of each decode query (as
+ * infv2_compressed_attn_fwd for S_q = 1 on that sequence): k_cmp, v_cmp
+ * [B][H_kv][max_blocks][D] from infv2_decode_compress_append on the key and
+ * on the value pages; q, o_sparse, out bf16 [B][H_q][D]; lse fp32 [B][H_q].
+ * Lengths are clamped on the GPU as for the other decode calls. */
+int infv2_decode_compressed_attn(const void* q, const void* k_cmp, const void* v_cmp,
+                                 const int32_t* seqlens, const void* o_sparse,
+                                 void* out, float* lse,
+                                 int B, int H_q, int H_kv, int D, int block_size,
+                                 int max_blocks, float softmax_scale,
+                                 float w_sparse, float w_cmp, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,8 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ["infv2_compress_k", "infv2_select_blocks", "infv2_sparse_attn_fwd", "infv2_dense_attn_fwd",
               "infv2_attn_fwd", "infv2_sparse_attn_bwd", "infv2_status_string", "infv2_decode_compress_append",
-              "infv2_decode_select", "infv2_decode_attn"]:
+              "infv2_decode_select", "infv2_decode_attn", "infv2_compress_v", "infv2_compressed_attn_fwd",
+              "infv2_decode_compressed_attn"]:
         assert n in names
 
 
@@ -234,3 +235,43 @@ def test_decode_workspace_sizes():
     # writing 132 fp32 per (batch, query head)
     assert lib.infv2_decode_attn_workspace_bytes(16, 32, 2, 128, 64, 512, 64) == 16 * 16 * 32 * 132 * 4
     assert lib.infv2_decode_attn_workspace_bytes(16, 32, 2, 64, 64, 512, 64) == 0      # unsupported D
+
+
+def _cmp_attn(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, o_sparse=None, out=FAKE, lse=None, B=1, H_q=32, H_kv=2, S_q=4096,
+             S_k=4096, D=128, bs=64, scale=0.0, ws=0.5, wc=0.5)
+    a.update(kw)
+    return lib.infv2_compressed_attn_fwd(a["q"], a["kc"], a["vc"], a["o_sparse"], a["out"], a["lse"], a["B"],
+                                         a["H_q"], a["H_kv"], a["S_q"], a["S_k"], a["D"], a["bs"], a["scale"],
+                                         a["ws"], a["wc"], None)
+
+
+@no_gpu
+def test_compressed_branch_validation_codes():
+    lib = tb.load_library()
+    assert lib.infv2_compress_v(FAKE, FAKE, 1, 2, 100, 96, 64, None) == tb.ERR_UNSUPPORTED
+    assert lib.infv2_compress_v(FAKE, None, 1, 2, 100, 128, 64, None) == tb.ERR_INVALID
+    assert lib.infv2_compress_v(FAKE, FAKE, 0, 2, 100, 128, 64, None) == tb.OK
+    assert _cmp_attn(lib, H_q=31) == tb.ERR_INVALID
+    assert _cmp_attn(lib, S_q=4097) == tb.ERR_INVALID               # more queries than keys
+    assert _cmp_attn(lib, vc=None) == tb.ERR_INVALID
+    assert _cmp_attn(lib, out=FAKE_MIS) == tb.ERR_INVALID
+    assert _cmp_attn(lib, o_sparse=FAKE_MIS) == tb.ERR_INVALID
+    assert _cmp_attn(lib, lse=FAKE + 4) == tb.ERR_INVALID
+    assert _cmp_attn(lib, ws=float("nan")) == tb.ERR_INVALID
+    assert _cmp_attn(lib, wc=float("inf")) == tb.ERR_INVALID
+    assert _cmp_attn(lib, bs=0) == tb.ERR_INVALID
+    assert _cmp_attn(lib, bs=32) == tb.ERR_UNSUPPORTED
+    assert _cmp_attn(lib, D=64) == tb.ERR_UNSUPPORTED
+    assert _cmp_attn(lib, H_q=34, H_kv=2) == tb.ERR_UNSUPPORTED       # 17 heads per group
+    assert _cmp_attn(lib, S_q=0) == tb.OK
+    dec = lambda **kw: lib.infv2_decode_compressed_attn(FAKE, FAKE, FAKE, kw.get("lens", FAKE), None, FAKE, None,
+                                                        kw.get("B", 16), 32, 2, 128, kw.get("bs", 64),
+                                                        kw.get("max_blocks", 512), 0.0, kw.get("ws", 0.0), 1.0,
+                                                        None)
+    assert dec(lens=None) == tb.ERR_INVALID
+    assert dec(lens=FAKE + 2) == tb.ERR_INVALID
+    assert dec(max_blocks=0) == tb.ERR_INVALID
+    assert dec(ws=float("nan")) == tb.ERR_INVALID
+    assert dec(bs=128) == tb.ERR_UNSUPPORTED
+    assert dec(B=0) == tb.OK

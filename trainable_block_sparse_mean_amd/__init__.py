@@ -8,7 +8,8 @@ the GPU.
 
 Names follow the C entry points without their ``infv2_`` prefix:
 ``compress_k``, ``select_blocks``, ``sparse_attn_fwd``, ``dense_attn_fwd``,
-``attn_fwd``.
+``attn_fwd``, the decode calls (``decode_*``), ``compress_v`` and
+``compressed_attn_fwd``.
 """
 from __future__ import annotations
 
@@ -44,6 +45,9 @@ SIGNATURES = {
     "infv2_decode_select": (_c_int, [_vp] * 5 + [_c_int] * 9 + [_c_float, _vp]),
     "infv2_decode_attn_workspace_bytes": (_c_size, [_c_int] * 7),
     "infv2_decode_attn": (_c_int, [_vp] * 8 + [_c_int] * 10 + [_c_float, _vp, _c_size, _vp]),
+    "infv2_compress_v": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
+    "infv2_compressed_attn_fwd": (_c_int, [_vp] * 6 + [_c_int] * 7 + [_c_float] * 3 + [_vp]),
+    "infv2_decode_compressed_attn": (_c_int, [_vp] * 7 + [_c_int] * 6 + [_c_float] * 3 + [_vp]),
 }
 
 _lib = None
@@ -262,6 +266,58 @@ def decode_attn(q, k_pages, v_pages, block_table, seqlens, blk_idx, n_init: int 
     _call("infv2_decode_attn", _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seqlens),
           _ptr(blk_idx), _ptr(out), _ptr(lse), B, H_q, H_kv, D, block_size, max_blocks, num_pages, topk, n_init,
           n_local, _scale(softmax_scale), _ptr(ws), ws.numel(), _stream())
+    return out, lse
+
+
+def compress_v(v: torch.Tensor, block_size: int = 64) -> torch.Tensor:
+    """Per-block value means, bf16 [B, H_kv, ceil(S_k/block_size), D]."""
+    _need(v, "v", torch.bfloat16, 4)
+    B, H_kv, S_k, D = v.shape
+    nb = (S_k + block_size - 1) // block_size
+    v_cmp = torch.empty(B, H_kv, nb, D, dtype=torch.bfloat16, device=v.device)
+    _call("infv2_compress_v", _ptr(v), _ptr(v_cmp), B, H_kv, S_k, D, block_size, _stream())
+    return v_cmp
+
+
+def compressed_attn_fwd(q, k_cmp, v_cmp, S_k: int, o_sparse=None, w_sparse: float = 0.0, w_cmp: float = 1.0,
+                        softmax_scale=None, block_size: int = 64, out=None, return_lse: bool = True):
+    """Compressed-attention branch, causal over whole blocks, optionally mixed
+    with another pattern's output: out = w_cmp * O_cmp (+ w_sparse * o_sparse).
+    q bf16 [B,H_q,S_q,D]; k_cmp, v_cmp bf16 [B,H_kv,ceil(S_k/64),D].  ``out``
+    may be given (also ``out is o_sparse``, in place).  Returns (out, lse)."""
+    _need(q, "q", torch.bfloat16, 4)
+    for t, n in ((k_cmp, "k_cmp"), (v_cmp, "v_cmp")):
+        _need(t, n, torch.bfloat16, 4)
+    if o_sparse is not None:
+        _need(o_sparse, "o_sparse", torch.bfloat16, 4)
+    B, H_q, S_q, D = q.shape
+    H_kv = k_cmp.shape[1]
+    out = torch.empty_like(q) if out is None else out
+    _need(out, "out", torch.bfloat16, 4)
+    lse = torch.empty(B, H_q, S_q, dtype=torch.float32, device=q.device) if return_lse else None
+    _call("infv2_compressed_attn_fwd", _ptr(q), _ptr(k_cmp), _ptr(v_cmp), _ptr(o_sparse), _ptr(out), _ptr(lse),
+          B, H_q, H_kv, S_q, S_k, D, block_size, _scale(softmax_scale), float(w_sparse), float(w_cmp), _stream())
+    return out, lse
+
+
+def decode_compressed_attn(q, k_cmp, v_cmp, seqlens, o_sparse=None, w_sparse: float = 0.0, w_cmp: float = 1.0,
+                           softmax_scale=None, block_size: int = 64, return_lse: bool = True):
+    """Compressed-attention branch of one query per sequence.  q bf16
+    [B,H_q,D]; k_cmp, v_cmp bf16 [B,H_kv,max_blocks,D]; seqlens int32 [B];
+    o_sparse bf16 [B,H_q,D] or None.  Returns (out, lse)."""
+    _need(q, "q", torch.bfloat16, 3)
+    for t, n in ((k_cmp, "k_cmp"), (v_cmp, "v_cmp")):
+        _need(t, n, torch.bfloat16, 4)
+    _need(seqlens, "seqlens", torch.int32, 1)
+    if o_sparse is not None:
+        _need(o_sparse, "o_sparse", torch.bfloat16, 3)
+    B, H_q, D = q.shape
+    H_kv, max_blocks = k_cmp.shape[1], k_cmp.shape[2]
+    out = torch.empty_like(q)
+    lse = torch.empty(B, H_q, dtype=torch.float32, device=q.device) if return_lse else None
+    _call("infv2_decode_compressed_attn", _ptr(q), _ptr(k_cmp), _ptr(v_cmp), _ptr(seqlens), _ptr(o_sparse),
+          _ptr(out), _ptr(lse), B, H_q, H_kv, D, block_size, max_blocks, _scale(softmax_scale), float(w_sparse),
+          float(w_cmp), _stream())
     return out, lse
 
 

@@ -370,4 +370,45 @@ int infv2_decode_attn(const void* q, const void* k_pages, const void* v_pages, c
       blk_idx, static_cast<uint16_t*>(out), lse, s, workspace, static_cast<hipStream_t>(stream)));
 }
 
+int infv2_compress_v(const void* v, void* v_cmp, int B, int H_kv, int S_k, int D, int block_size, void* stream) {
+  // the values are compressed exactly like the keys
+  return infv2_compress_k(v, v_cmp, B, H_kv, S_k, D, block_size, stream);
+}
+
+int infv2_compressed_attn_fwd(const void* q, const void* k_cmp, const void* v_cmp, const void* o_sparse, void* out,
+                              float* lse, int B, int H_q, int H_kv, int S_q, int S_k, int D, int block_size,
+                              float softmax_scale, float w_sparse, float w_cmp, void* stream) {
+  int st = check_shape(B, H_q, H_kv, S_q, S_k, D);
+  if (st != INFV2_OK) return st;
+  if (block_size < 1 || !isfinite(w_sparse) || !isfinite(w_cmp)) return INFV2_ERR_INVALID;
+  if (block_size != infv2::kBS) return INFV2_ERR_UNSUPPORTED;
+  if (B == 0 || S_q == 0) return INFV2_OK;
+  if (!tensor_ok(q) || !tensor_ok(k_cmp) || !tensor_ok(v_cmp) || !tensor_ok(out)) return INFV2_ERR_INVALID;
+  if ((o_sparse && !aligned(o_sparse, 16)) || (lse && !aligned(lse, 16))) return INFV2_ERR_INVALID;
+  const AttnShape s = make_shape(B, H_q, H_kv, S_q, S_k, block_size, 0, 0, 1, scale_log2(softmax_scale, D), 1);
+  return hip_status(infv2::launch_compressed_attn(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cmp), static_cast<const uint16_t*>(v_cmp),
+      static_cast<const uint16_t*>(o_sparse), static_cast<uint16_t*>(out), lse, s, w_sparse, w_cmp,
+      static_cast<hipStream_t>(stream)));
+}
+
+int infv2_decode_compressed_attn(const void* q, const void* k_cmp, const void* v_cmp, const int32_t* seqlens,
+                                 const void* o_sparse, void* out, float* lse, int B, int H_q, int H_kv, int D,
+                                 int block_size, int max_blocks, float softmax_scale, float w_sparse, float w_cmp,
+                                 void* stream) {
+  int st = check_decode(B, H_q, H_kv, D, block_size, max_blocks);
+  if (st != INFV2_OK) return st;
+  if (!isfinite(w_sparse) || !isfinite(w_cmp)) return INFV2_ERR_INVALID;
+  if (B == 0) return INFV2_OK;
+  if (!tensor_ok(q) || !tensor_ok(k_cmp) || !tensor_ok(v_cmp) || !tensor_ok(out) || !ints_ok(seqlens))
+    return INFV2_ERR_INVALID;
+  if ((o_sparse && !aligned(o_sparse, 16)) || (lse && !aligned(lse, 16))) return INFV2_ERR_INVALID;
+  const AttnShape s = decode_shape(B, H_q, H_kv, max_blocks, 0, 0, 1, scale_log2(softmax_scale, D), seqlens,
+                                   nullptr, 0);
+  return hip_status(infv2::launch_compressed_attn(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cmp), static_cast<const uint16_t*>(v_cmp),
+      static_cast<const uint16_t*>(o_sparse), static_cast<uint16_t*>(out), lse, s, w_sparse, w_cmp,
+      static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -193,6 +193,23 @@ __device__ __forceinline__ void sparse_blocks(SparseState& st, const SparseLane&
   pv_half(st, ln, kl + kTileBytes, softmax_half(st, b, sl2), 1);
 }
 
+// The wave's token over one streamed pair of stages (blocks js[0], js[1]):
+// m0 / m1 say whether it attends each (wave-uniform).  A block that holds
+// keys past the token (its own block) takes the masked pipeline.
+__device__ __forceinline__ void attend_pair(SparseState& st, const SparseLane& spl, const unsigned char* const* stg,
+                                            const int* js, bool m0, bool m1, int lane, float sl2) {
+  const int lim = __builtin_amdgcn_readfirstlane(st.lim);
+  const bool d0 = js[0] * kBS + kBS - 1 > lim, d1 = js[1] * kBS + kBS - 1 > lim;
+  const int f0 = st.lim - js[0] * kBS - 4 * (lane >> 4), f1 = st.lim - js[1] * kBS - 4 * (lane >> 4);
+  if (m0 || m1) {
+    const unsigned char* ka = m0 ? stg[0] : stg[1];
+    if ((m0 && d0) || (m1 && d1))
+      sparse_blocks<true>(st, spl, ka, stg[1], m0 && m1, m0 ? d0 : d1, d1, m0 ? f0 : f1, f1, sl2);
+    else
+      sparse_blocks<false>(st, spl, ka, stg[1], m0 && m1, false, false, 0, 0, sl2);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Dense: 32x32x16 MFMAs, the wave's two tokens side by side in the 32
 // columns (lane column c32 = 16 * token + head, key/dim half h2).
@@ -420,20 +437,8 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
                          [&](const unsigned char* const* stg, const int* js, uint32_t cur0, uint32_t cur1) {
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        const uint32_t bit = 1u << (16 + wave * T + t);
-        const bool m0 = (cur0 & bit) != 0u, m1 = (cur1 & bit) != 0u;   // cur1 = 0 past the list
-        // wave-uniform: which blocks the token attends, and whether one holds
-        // keys past the token (its own block)
-        const int lim = __builtin_amdgcn_readfirstlane(sp[t].lim);
-        const bool d0 = js[0] * kBS + kBS - 1 > lim, d1 = js[1] * kBS + kBS - 1 > lim;
-        const int f0 = sp[t].lim - js[0] * kBS - 4 * (lane >> 4), f1 = sp[t].lim - js[1] * kBS - 4 * (lane >> 4);
-        if (m0 || m1) {
-          const unsigned char* ka = m0 ? stg[0] : stg[1];
-          if ((m0 && d0) || (m1 && d1))
-            sparse_blocks<true>(sp[t], spl, ka, stg[1], m0 && m1, m0 ? d0 : d1, d1, m0 ? f0 : f1, f1, sl2);
-          else
-            sparse_blocks<false>(sp[t], spl, ka, stg[1], m0 && m1, false, false, 0, 0, sl2);
-        }
+        const uint32_t bit = 1u << (16 + wave * T + t);   // cur1 = 0 past the list
+        attend_pair(sp[t], spl, stg, js, (cur0 & bit) != 0u, (cur1 & bit) != 0u, lane, sl2);
       }
     });
   }
@@ -512,6 +517,110 @@ __global__ __launch_bounds__(128) void combine_splits_kernel(const float* __rest
   }
   out[row * kD + d] = static_cast<uint16_t>(f32_to_bf16_bits(o / l));
   if (lse && d == 0) lse[row] = (m + log2f(l)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// Compressed-attention branch (skill page, Step 2, compressed_attention, made
+// causal like block scoring): the query at position i attends the compressed
+// keys of the nv = floor((i+1)/64) blocks that end at or before it and takes
+// the softmax-weighted sum of their compressed values.  A KV head's
+// compressed keys (values) are NB rows of 128 dims; 64 of them side by side
+// have the layout of one key block, so the sparse pipeline streams them
+// unchanged: group e of this kernel is compressed rows 64e .. 64e+63, and a
+// token attends rows 0 .. nv-1 (its "last visible key" is nv - 1).  Same
+// work unit as the sparse forward: 16 tokens x one KV head, one token per
+// wave, the G heads of the group in the MFMA columns.
+// Epilogue: out = w_cmp * O_cmp, plus w_sparse * o_sparse when o_sparse is
+// given (the weighted mix of pattern outputs of skill page Step 3, with given
+// coefficients).  out may be o_sparse itself: each lane reads its four
+// values of a row before it writes them.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kWin * 64, 1) void compressed_attn_kernel(const uint16_t* __restrict__ q,
+                                                                       const uint16_t* __restrict__ kc,
+                                                                       const uint16_t* __restrict__ vc,
+                                                                       const uint16_t* o_sparse, uint16_t* out,
+                                                                       float* __restrict__ lse, AttnShape s,
+                                                                       float w_sparse, float w_cmp) {
+  constexpr int kWaves = kWin;  // one token per wave
+  extern __shared__ __align__(1024) unsigned char smem[];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int hl = lane & 15, gq = lane >> 4;
+  const int nwin = (s.S_q + kWin - 1) / kWin;
+  int bg_i, win;
+  if (!map_window(blockIdx.x, nwin, s.B * s.H_kv, bg_i, win)) return;
+  const int g = bg_i % s.H_kv;
+  const int b = bg_i / s.H_kv;
+  const size_t bg = static_cast<size_t>(bg_i);
+  const int r0 = win * kWin;
+  const int r = r0 + wave;
+  const int off = seq_keys(s, b) - s.S_q;    // query row r sits at key position off + r
+  const int nq = min(kWin, s.S_q - r0);      // tokens of the window
+  const int nv_max = (off + r0 + nq) / kBS;  // compressed rows the window's last token sees
+  const int ngrp = (nv_max + kBS - 1) / kBS; // groups of 64 rows to stream
+  const BlockSrc src{kc + bg * s.NB * kD, vc + bg * s.NB * kD, nullptr, s.NB, 0, s.H_kv, b, g, s.NB};
+  const float sl2 = s.scale_log2;
+
+  SparseState st;
+  {
+    const bool valid = r < s.S_q && hl < s.G;
+    const uint16_t* qrow = q + (static_cast<size_t>(b * s.H_q + g * s.G + hl) * s.S_q + r) * kD + gq * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) st.qf[ks] = valid ? as_bf16x8(load16(qrow + ks * 32)) : bf16x8{};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) st.qf[ks] = settle(st.qf[ks]);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) st.o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    st.m = -INFINITY;
+    st.l = 0.f;
+    st.lim = (off + r + 1) / kBS - 1;  // last visible compressed row (-1: none)
+  }
+  // list entry e: group e | the window's tokens that see its first row
+  // (token t sees row 64e iff off + r0 + t + 1 >= 64 (64e + 1))
+  auto entry_at = [&](int e) -> uint32_t {
+    const int t_min = max(0, kBS * (kBS * e + 1) - 1 - off - r0);
+    const uint32_t mask = t_min >= nq ? 0u : ((1u << nq) - 1u) & ~((1u << t_min) - 1u);
+    return static_cast<uint32_t>(e) | (mask << 16);
+  };
+  const SparseLane spl = sparse_lane(hl, gq);
+  stream_pairs<kWaves>(smem, src, 0, ngrp, entry_at, wave, lane,
+                       [&](const unsigned char* const* stg, const int* js, uint32_t cur0, uint32_t cur1) {
+    const uint32_t bit = 1u << (16 + wave);
+    attend_pair(st, spl, stg, js, (cur0 & bit) != 0u, (cur1 & bit) != 0u, lane, sl2);
+  });
+
+  const float l = sum_xor32(sum_xor16(st.l));
+  if (r >= s.S_q || hl >= s.G) return;
+  const int h = g * s.G + hl;
+  const size_t row = static_cast<size_t>(b * s.H_q + h) * s.S_q + r;
+  const float scl = l > 0.f ? w_cmp / l : 0.f;  // a token that sees no block: the branch is zero
+  uint16_t* orow = out + row * kD + 4 * gq;
+  const uint16_t* srow = o_sparse ? o_sparse + row * kD + 4 * gq : nullptr;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = st.o[dt][e] * scl;
+    if (srow) {
+      const u32x2 x = *reinterpret_cast<const u32x2*>(srow + 16 * dt);
+      y[0] = fmaf(w_sparse, bf16_lo(x[0]), y[0]);
+      y[1] = fmaf(w_sparse, bf16_hi(x[0]), y[1]);
+      y[2] = fmaf(w_sparse, bf16_lo(x[1]), y[2]);
+      y[3] = fmaf(w_sparse, bf16_hi(x[1]), y[3]);
+    }
+    *reinterpret_cast<u32x2*>(orow + 16 * dt) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+  }
+  if (lse && gq == 0) lse[row] = l > 0.f ? (st.m + log2f(l)) * kLn2 : -INFINITY;
+}
+
+hipError_t launch_compressed_attn(const uint16_t* q, const uint16_t* k_cmp, const uint16_t* v_cmp,
+                                  const uint16_t* o_sparse, uint16_t* out, float* lse, const AttnShape& s,
+                                  float w_sparse, float w_cmp, hipStream_t stream) {
+  if (s.B == 0 || s.S_q == 0) return hipSuccess;
+  const int nwin = (s.S_q + kWin - 1) / kWin;
+  hipLaunchKernelGGL(compressed_attn_kernel, dim3(padded_grid(nwin, s.B * s.H_kv)), dim3(kWin * 64),
+                     kStages * kStageBytes, stream, q, k_cmp, v_cmp, o_sparse, out, lse, s, w_sparse, w_cmp);
+  return hipGetLastError();
 }
 
 int sparse_splits(int B, int H_kv, int S_q, int topk) {

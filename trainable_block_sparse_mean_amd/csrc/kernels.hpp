@@ -75,6 +75,14 @@ hipError_t launch_dense_attn(const uint16_t* q, const uint16_t* k, const uint16_
                              uint16_t* out, float* lse, const AttnShape& s, void* workspace,
                              hipStream_t stream);
 
+// Compressed-attention branch over k_cmp / v_cmp [B][H_kv][NB][D] (NB = s.NB
+// compressed rows per KV head): out = w_cmp * O_cmp (+ w_sparse * o_sparse
+// when o_sparse is not null; out may equal o_sparse); lse (optional) is the
+// branch's own log-sum-exp, -inf for a query that sees no block.
+hipError_t launch_compressed_attn(const uint16_t* q, const uint16_t* k_cmp, const uint16_t* v_cmp,
+                                  const uint16_t* o_sparse, uint16_t* out, float* lse, const AttnShape& s,
+                                  float w_sparse, float w_cmp, hipStream_t stream);
+
 // workspace of the sparse backward: D = <dO, O> per (token, head), then the
 // selected-entry bitmap (one bit per KV head, block and query token)
 size_t attn_bwd_workspace_bytes(const AttnShape& s);
