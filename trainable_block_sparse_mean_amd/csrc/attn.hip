@@ -312,7 +312,9 @@ __device__ __forceinline__ void dense_block(DenseState& st, const DenseLane& ln,
   }
 }
 
-template <bool DENSE>
+// PAGED: K/V in the pages of a paged cache, per-sequence lengths (decode);
+// otherwise contiguous K/V of one key length.
+template <bool DENSE, bool PAGED>
 __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel(const uint16_t* __restrict__ q,
                                                                      const uint16_t* __restrict__ k,
                                                                      const uint16_t* __restrict__ v,
@@ -338,14 +340,13 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
   const size_t bg = static_cast<size_t>(bg_i);
   const int r0 = win * kWin;
   const int rw = r0 + wave * T;              // first token of this wave
-  const int S_k = seq_keys(s, b);            // keys of this sequence
+  const int S_k = PAGED ? seq_keys(s, b) : s.S_k;  // keys of this sequence
   const int off = S_k - s.S_q;
   const int i_last = off + min(r0 + kWin, s.S_q) - 1;
   const int qb_last = i_last / kBS;
-  const uint16_t* kg = k + bg * s.S_k * kD;  // contiguous K/V (dense, and sparse without pages)
-  const uint16_t* vg = v + bg * s.S_k * kD;
-  const BlockSrc src{s.block_table ? k : kg, s.block_table ? v : vg, s.block_table, s.NB, s.num_pages, s.H_kv, b, g,
-                     S_k};
+  const uint16_t* kg = PAGED ? k : k + bg * s.S_k * kD;  // pages, or this KV head's contiguous rows
+  const uint16_t* vg = PAGED ? v : v + bg * s.S_k * kD;
+  const BlockSrc<PAGED> src{kg, vg, s.block_table, s.NB, s.num_pages, s.H_kv, b, g, S_k};
   const uint32_t ring = lds_addr(smem);
   const float sl2 = s.scale_log2;
 
@@ -558,7 +559,7 @@ __global__ __launch_bounds__(kWin * 64, 1) void compressed_attn_kernel(const uin
   const int nq = min(kWin, s.S_q - r0);      // tokens of the window
   const int nv_max = (off + r0 + nq) / kBS;  // compressed rows the window's last token sees
   const int ngrp = (nv_max + kBS - 1) / kBS; // groups of 64 rows to stream
-  const BlockSrc src{kc + bg * s.NB * kD, vc + bg * s.NB * kD, nullptr, s.NB, 0, s.H_kv, b, g, s.NB};
+  const BlockSrc<false> src{kc + bg * s.NB * kD, vc + bg * s.NB * kD, nullptr, s.NB, 0, s.H_kv, b, g, s.NB};
   const float sl2 = s.scale_log2;
 
   SparseState st;
@@ -643,7 +644,14 @@ static hipError_t launch_window(const uint16_t* q, const uint16_t* k, const uint
   const int nwin = (s.S_q + kWin - 1) / kWin;
   const dim3 grid(padded_grid(nwin, s.B * s.H_kv), DENSE ? 1 : s.nsplit);
   const size_t lds = kStages * kStageBytes + (DENSE ? 0 : 2 * sizeof(int) * static_cast<size_t>(s.NB));
-  hipLaunchKernelGGL((attn_window_kernel<DENSE>), grid, dim3(Cfg<DENSE>::kWaves * 64), lds, stream, q, k, v,
+  if constexpr (!DENSE) {  // the dense kernel has no paged form
+    if (s.block_table) {
+      hipLaunchKernelGGL((attn_window_kernel<false, true>), grid, dim3(Cfg<false>::kWaves * 64), lds, stream, q, k,
+                         v, blk_idx, out, lse, part, s);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((attn_window_kernel<DENSE, false>), grid, dim3(Cfg<DENSE>::kWaves * 64), lds, stream, q, k, v,
                      blk_idx, out, lse, part, s);
   return hipGetLastError();
 }

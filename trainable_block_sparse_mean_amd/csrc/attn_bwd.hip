@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(
   };
 
   const uint32_t bit = 1u << (16 + wave);
-  const BlockSrc src{kg, vg, nullptr, s.NB, 0, s.H_kv, 0, 0, s.S_k};
+  const BlockSrc<false> src{kg, vg, nullptr, s.NB, 0, s.H_kv, 0, 0, s.S_k};
   stream_pairs<kBwdDqWaves>(smem, src, 0, nblk, entry_at, wave, lane,
                             [&](const unsigned char* const* stg, const int* js, uint32_t cur0, uint32_t cur1) {
                               // one copy of the item code for both blocks of the pair

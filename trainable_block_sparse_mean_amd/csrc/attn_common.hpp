@@ -98,27 +98,33 @@ __device__ __forceinline__ void stage_block(uint32_t stage_lds, const uint16_t* 
   }
 }
 
-// Where a KV head's blocks live: the contiguous [S_k][D] rows of one
-// (batch, KV head) at k / v, or, with a block table, pages of a paged cache
-// based at k / v (see block_rows).  krows(j) / vrows(j) give block j's first
-// row, keys(j) how many of its rows hold keys.
+// Where a KV head's blocks live: PAGED = false, the contiguous [S_k][D] rows
+// of one (batch, KV head) at k / v; PAGED = true, pages of a paged cache based
+// at k / v, found through the block table (page ids clamped into range, so a
+// bad table cannot address past the pages).  krows(j) / vrows(j) give block
+// j's first row, keys(j) how many of its rows hold keys.  The contiguous form
+// is a separate instantiation so that prefill carries none of the paging.
+template <bool PAGED>
 struct BlockSrc {
   const uint16_t* k;
   const uint16_t* v;
-  const int* table;  // null: contiguous
+  const int* table;  // PAGED only
   int nb, num_pages, H_kv, b, g, S_k;
   __device__ __forceinline__ size_t rows(int j) const {
-    if (!table) return static_cast<size_t>(j) * kBS * kD;
-    const int page = min(max(table[static_cast<size_t>(b) * nb + j], 0), num_pages - 1);
-    return (static_cast<size_t>(page) * H_kv + g) * kBS * kD;
+    if constexpr (!PAGED) {
+      return static_cast<size_t>(j) * kBS * kD;
+    } else {
+      const int page = min(max(table[static_cast<size_t>(b) * nb + j], 0), num_pages - 1);
+      return (static_cast<size_t>(page) * H_kv + g) * kBS * kD;
+    }
   }
   __device__ __forceinline__ const uint16_t* krows(int j) const { return k + rows(j); }
   __device__ __forceinline__ const uint16_t* vrows(int j) const { return v + rows(j); }
   __device__ __forceinline__ int keys(int j) const { return min(kBS, S_k - j * kBS); }
 };
 
-template <int WAVES>
-__device__ __forceinline__ void stage_src(uint32_t stage_lds, const BlockSrc& src, int j, const DmaLane<WAVES>& d,
+template <int WAVES, typename Src>
+__device__ __forceinline__ void stage_src(uint32_t stage_lds, const Src& src, int j, const DmaLane<WAVES>& d,
                                           int wave, int lane) {
   stage_block<WAVES>(stage_lds, src.krows(j), src.vrows(j), src.keys(j), d, wave, lane);
 }
@@ -218,8 +224,8 @@ __device__ __forceinline__ int build_union_list(uint32_t* bmask, int* blist, int
 // ring holds the pair being multiplied (2 stages) and the next pair in flight
 // (the other 2); one barrier per pair.  on_pair(stg, js, cur0, cur1) gets the
 // two stages, their blocks and their list entries (cur1 = 0 past the end).
-template <int WAVES, typename Entry, typename F>
-__device__ __forceinline__ void stream_pairs(unsigned char* smem, const BlockSrc& src, int e_lo, int e_hi,
+template <int WAVES, typename Src, typename Entry, typename F>
+__device__ __forceinline__ void stream_pairs(unsigned char* smem, const Src& src, int e_lo, int e_hi,
                                              Entry entry_at, int wave, int lane, F&& on_pair) {
   static_assert(kStages == 4, "two pairs of stages");
   const uint32_t ring = lds_addr(smem);
