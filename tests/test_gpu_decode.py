@@ -183,3 +183,26 @@ def test_decode_full_size_b16_32k():
         ref_out[b], ref_lse[b] = ob[0, :, 0], lb[0, :, 0]
     log("  selection rows:", counts)
     log("  attention:", assert_attn_close(out, lse, ref_out, ref_lse, "decode b16 32k"))
+
+
+def test_decode_other_forced_blocks():
+    """n_init = 0 and a 3-block window (the defaults elsewhere are 1 and 2)."""
+    lens = [4000, 129, 2600, 64 * 30 + 1]
+    c = paged_cache(lens, 16, 2, seed=16)
+    k_cmp = compressed(c)
+    idx, score = tb.decode_select(c["q"], k_cmp, c["lens"], 12, n_init=0, n_local=3, return_scores=True)
+    out, lse = tb.decode_attn(c["q"], c["kp"], c["vp"], c["table"], c["lens"], idx, n_init=0, n_local=3)
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(128)
+    q64, kp, vp = np64(c["q"]), np64(c["kp"]), np64(c["vp"])
+    table, kc64, gidx = c["table"].cpu().numpy(), np64(k_cmp), idx.cpu().numpy()
+    ref_out, ref_lse = np.zeros((len(lens), 16, 128)), np.zeros((len(lens), 16))
+    for b, L in enumerate(lens):
+        qb = q64[b][None, :, None, :]
+        ref_idx, scores = O.select_blocks(qb, kc64[b][None], L, 12, 0, 3, BS, scale, return_scores=True)
+        check_selection(gidx[b][None, :, None, :], ref_idx, scores, [0], 1, L, 12, 0, 3)
+        kb = O.paged_sequence(kp, table[b], L, BS)[None]
+        vb = O.paged_sequence(vp, table[b], L, BS)[None]
+        ob, lb = O.sparse_attn(qb, kb, vb, gidx[b][None, :, None, :], BS, 0, 3, scale)
+        ref_out[b], ref_lse[b] = ob[0, :, 0], lb[0, :, 0]
+    log("  n_init 0, n_local 3:", assert_attn_close(out, lse, ref_out, ref_lse, "decode forced blocks"))
