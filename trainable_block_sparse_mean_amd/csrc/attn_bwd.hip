@@ -221,11 +221,13 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(
 // ---------------------------------------------------------------------------
 // LDS: a ring of kPairBufs buffers, each holding one token pair's Q rows,
 // dO rows and the 32 rows' log-sum-exp and D (64 floats), then the member
-// list of the current chunk and its length.
-constexpr int kPairBufs = 4;                                      // 3 pairs in flight
+// list of the current chunk (16-bit offsets from the chunk's first token)
+// and its length: 51 KB, so that three workgroups (12 waves of at most 168
+// VGPRs) share a CU.
+constexpr int kPairBufs = 3;                                      // 2 pairs in flight
 constexpr int kStatsBytes = 2 * kPairRows * 4;                    // lse[32], D[32]
 constexpr int kKvBufBytes = 2 * kPairBytes + kStatsBytes;         // Q + dO + stats of one pair
-constexpr int kKvLdsBytes = kPairBufs * kKvBufBytes + kMemberChunk * 4 + 16;
+constexpr int kKvLdsBytes = kPairBufs * kKvBufBytes + kMemberChunk * 2 + 16;
 constexpr int kPairDma = 5;                                       // loads per wave per pair
 
 // Issue the loads of one token pair into an LDS buffer: Q and dO rows (row
@@ -253,14 +255,14 @@ __device__ __forceinline__ void stage_pair(uint32_t buf_lds, const uint16_t* qg,
   if (lane < 16) dma4(wave < 2 ? lg : sg, soff, buf_lds + 2 * kPairBytes + wave * 64);
 }
 
-__global__ __launch_bounds__(kBwdKvWaves * 64, 2) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(kBwdKvWaves * 64, 3) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ lse, const uint16_t* __restrict__ dout, const float* __restrict__ dsum,
     const uint32_t* __restrict__ bm, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
     float* __restrict__ part, AttnShape s, float scale) {
   extern __shared__ __align__(1024) unsigned char smem[];
-  int* mlist = reinterpret_cast<int*>(smem + kPairBufs * kKvBufBytes);
-  int* mcount = mlist + kMemberChunk;
+  uint16_t* mlist = reinterpret_cast<uint16_t*>(smem + kPairBufs * kKvBufBytes);
+  int* mcount = reinterpret_cast<int*>(mlist + kMemberChunk);
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -344,7 +346,7 @@ __global__ __launch_bounds__(kBwdKvWaves * 64, 2) void attn_bwd_dkdv_kernel(
       int pos = pre - cnt;
       while (bits) {
         const int bt = __builtin_ctz(bits);
-        mlist[pos++] = r32 + bt;
+        mlist[pos++] = static_cast<uint16_t>(r32 + bt - c0);
         bits &= bits - 1u;
       }
       if (lane == 0) *mcount = total;
@@ -352,7 +354,7 @@ __global__ __launch_bounds__(kBwdKvWaves * 64, 2) void attn_bwd_dkdv_kernel(
     __syncthreads();
     const int nm = *mcount;
     const int npair = (nm + 1) / 2;
-    auto pair_tok = [&](int p, int x) { return 2 * p + x < nm ? mlist[2 * p + x] : mlist[2 * p]; };
+    auto pair_tok = [&](int p, int x) { return c0 + (2 * p + x < nm ? mlist[2 * p + x] : mlist[2 * p]); };
     auto stage = [&](int p) {
       stage_pair(lbase + (p % kPairBufs) * kKvBufBytes, qg, dg, lg, sg, s.S_q, s.G, pair_tok(p, 0), pair_tok(p, 1),
                  wave, lane);
@@ -370,9 +372,9 @@ __global__ __launch_bounds__(kBwdKvWaves * 64, 2) void attn_bwd_dkdv_kernel(
       const unsigned char* qt = smem + (p % kPairBufs) * kKvBufBytes;
       const unsigned char* dt_ = qt + kPairBytes;
       const float* st = reinterpret_cast<const float*>(qt + 2 * kPairBytes);  // lse[32], D[32]
-      const int tA = mlist[2 * p];
+      const int tA = c0 + mlist[2 * p];
       const bool hasB = 2 * p + 1 < nm;
-      const int tB = hasB ? mlist[2 * p + 1] : tA;
+      const int tB = hasB ? c0 + mlist[2 * p + 1] : tA;
       // log-sum-exp (log2 units) and D of the rows this lane holds: (token t, heads 4*gq .. 4*gq+3)
       float lr[2][4], dr[2][4];
 #pragma unroll
