@@ -89,7 +89,9 @@ def test_workspace_sizes():
     assert lib.infv2_sparse_workspace_bytes(1, 32, 2, 32768, 32768, 128, 64, 64) == 0
     assert lib.infv2_dense_workspace_bytes(2, 8, 1, 64, 64, 128) == 0
     dec = lib.infv2_sparse_workspace_bytes(16, 32, 2, 1, 32768, 128, 64, 64)
-    assert dec == 16 * 16 * 32 * 1 * 132 * 4                   # 16 splits
+    assert dec == 8 * 16 * 32 * 1 * 132 * 4                    # 8 splits: 256 workgroups over 32 windows
+    one = lib.infv2_sparse_workspace_bytes(1, 32, 2, 1, 32768, 128, 64, 64)
+    assert one == 16 * 1 * 32 * 1 * 132 * 4                    # at most 16 splits
     assert lib.infv2_sparse_workspace_bytes(1, 32, 2, 1, 1000, 128, 64, 4) == 0   # one split: no partials
     dense = lib.infv2_attn_workspace_bytes(1, 32, 2, 4096, 4096, 128, 64, 16, 4096)
     sparse = lib.infv2_attn_workspace_bytes(1, 32, 2, 4097, 4097, 128, 64, 16, 4096)
@@ -231,9 +233,9 @@ def test_decode_validation_codes():
 
 def test_decode_workspace_sizes():
     lib = tb.load_library()
-    # B * H_kv = 32 windows of one query: 16 splits of the block list, each
-    # writing 132 fp32 per (batch, query head)
-    assert lib.infv2_decode_attn_workspace_bytes(16, 32, 2, 128, 64, 512, 64) == 16 * 16 * 32 * 132 * 4
+    # B * H_kv = 32 windows of one query: 8 splits of the block list (about
+    # one workgroup per CU), each writing 132 fp32 per (batch, query head)
+    assert lib.infv2_decode_attn_workspace_bytes(16, 32, 2, 128, 64, 512, 64) == 8 * 16 * 32 * 132 * 4
     assert lib.infv2_decode_attn_workspace_bytes(16, 32, 2, 64, 64, 512, 64) == 0      # unsupported D
 
 

@@ -498,23 +498,35 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
 
 // Merge the split partials of each query row: m = max_s m_s,
 // l = sum_s l_s 2^(m_s - m), O = sum_s o_s 2^(m_s - m) / l.  One workgroup of
-// 128 threads (one per dim) per row.
+// 128 threads (one per dim) per row.  Every split's values are loaded up front
+// (unrolled to the largest split count), so the row waits on one round of
+// loads rather than on one per split.
+constexpr int kMaxSplits = 16;  // sparse_splits never returns more
 __global__ __launch_bounds__(128) void combine_splits_kernel(const float* __restrict__ part,
                                                              uint16_t* __restrict__ out, float* __restrict__ lse,
                                                              int nsplit, size_t rows) {
   const size_t row = blockIdx.x;
   const int d = threadIdx.x;
   const size_t stride = rows * kPartFloats;
+  const float* pr = part + row * kPartFloats;
+  float ms[kMaxSplits], ls[kMaxSplits], os[kMaxSplits];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) {
+    const bool ok = sp < nsplit;
+    ms[sp] = ok ? pr[sp * stride + 128] : -INFINITY;
+    ls[sp] = ok ? pr[sp * stride + 129] : 0.f;
+    os[sp] = ok ? pr[sp * stride + d] : 0.f;
+  }
   float m = -INFINITY;
-  for (int sp = 0; sp < nsplit; ++sp) m = fmaxf(m, part[sp * stride + row * kPartFloats + 128]);
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) m = fmaxf(m, ms[sp]);
   float l = 0.f, o = 0.f;
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const float* pr = part + sp * stride + row * kPartFloats;
-    const float ms = pr[128];
-    if (ms == -INFINITY) continue;  // a split that saw no block of this row
-    const float w = exp2f(ms - m);
-    l += pr[129] * w;
-    o += pr[d] * w;
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) {
+    if (ms[sp] == -INFINITY) continue;  // a split that saw no block of this row
+    const float w = exp2f(ms[sp] - m);
+    l += ls[sp] * w;
+    o += os[sp] * w;
   }
   out[row * kD + d] = static_cast<uint16_t>(f32_to_bf16_bits(o / l));
   if (lse && d == 0) lse[row] = (m + log2f(l)) * kLn2;
@@ -627,7 +639,8 @@ hipError_t launch_compressed_attn(const uint16_t* q, const uint16_t* k_cmp, cons
 int sparse_splits(int B, int H_kv, int S_q, int topk) {
   const long long units = static_cast<long long>(B) * H_kv * ((S_q + kWin - 1) / kWin);
   if (units >= 128) return 1;
-  const int by_units = static_cast<int>(512 / units);
+  // about one workgroup per CU (256 CUs): more splits only add a second round
+  const int by_units = static_cast<int>(256 / units);
   const int by_blocks = max(1, (topk + 3) / 4);  // keep >= ~4 blocks per split
   return max(1, min(16, min(by_units, by_blocks)));
 }
