@@ -349,6 +349,158 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_blocks_kernel(const uin
   else topk_row<32>(sig + lo, nC, s.topk, lo, out, out_s, lane);
 }
 
+// One query per sequence (decode): the 16 waves of a workgroup share the
+// token and split its visible compressed blocks, so the whole workgroup works
+// on one selection.  Wave w scores the 16-block tiles [w*tpw, (w+1)*tpw), its
+// compressed keys loaded straight into the B operands (each block is read by
+// one wave only, so nothing is staged in LDS), and keeps the scores in
+// registers: the two passes become one pass over the keys.  The waves' (max,
+// sum) per head are merged in LDS into the exact log-sum-exp, each wave turns
+// its own scores into group scores in LDS, and wave 0 takes the top-k as the
+// token-per-wave kernel does.  Same lane layout as that kernel.
+constexpr int kDecTiles = 8;  // tiles per wave: 16 waves x 8 x 16 blocks covers 2048 blocks
+__global__ __launch_bounds__(kSelWaves * 64) void select_decode_kernel(const uint16_t* __restrict__ q,
+                                                                       const uint16_t* __restrict__ kc,
+                                                                       int32_t* __restrict__ blk_idx,
+                                                                       float* __restrict__ blk_score, AttnShape s) {
+  extern __shared__ __align__(16) unsigned char dec_smem[];
+  float* part = reinterpret_cast<float*>(dec_smem);              // [16 waves][16 heads][2]
+  float* sig = part + kSelWaves * kMaxG * 2;                        // [NB]
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int hl = lane & 15, gq = lane >> 4;
+  const int g = blockIdx.x % s.H_kv;
+  const int b = blockIdx.x / s.H_kv;
+  const int pos = seq_keys(s, b) - 1;      // the query is the last key
+  const int nv = (pos + 1) / kBS;          // fully visible blocks
+  const int ntile = (nv + 15) / 16;
+  const int tpw = (ntile + kSelWaves - 1) / kSelWaves;   // <= kDecTiles (NB <= 2048)
+  const int tw0 = wave * tpw;
+  const float sl2 = s.scale_log2;
+
+  const int tend = min(ntile, tw0 + tpw);  // this wave's tiles: [tw0, tend)
+  const uint16_t* kg = kc + static_cast<size_t>(b * s.H_kv + g) * s.NB * kD;
+  // B operands of tile tw0 + t: lane (block hl of the tile, dims 8*gq + 32*ks);
+  // rows past nv - 1 read row nv - 1 (their scores are dropped)
+  auto kload = [&](int t, u32x4 (&kr)[4]) {
+    const uint16_t* krow = kg + static_cast<size_t>(min(16 * (tw0 + t) + hl, max(nv - 1, 0))) * kD + gq * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kr[ks] = load16(krow + ks * 32);
+  };
+  // the query and the first two tiles' keys are loaded together
+  u32x4 kra[4], krb[4];
+  if (tw0 < tend) kload(0, kra);
+  if (tw0 + 1 < tend) kload(1, krb);
+  bf16x8 qa[4];
+  {
+    const bool ok = hl < s.G;
+    const uint16_t* qrow = q + (static_cast<size_t>(b * s.H_q + g * s.G + hl) * s.S_q) * kD + gq * 8;
+    u32x4 raw[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) raw[ks] = ok ? load16(qrow + ks * 32) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qa[ks] = settle(as_bf16x8(raw[ks]));
+  }
+
+  // scores of this wave's tiles (log2 units); blocks >= nv are -inf.  Tiles go
+  // in pairs, the next pair's keys loaded under the current pair's products.
+  floatx4 z[kDecTiles];
+  float m[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+  }
+  auto score = [&](const u32x4 (&kr)[4], int t) {
+    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) acc = mfma_16x16x32(qa[ks], as_bf16x8(kr[ks]), acc);
+    const int j = 16 * (tw0 + t) + hl;
+    floatx4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = j < nv ? acc[i] * sl2 : -INFINITY;
+    return r;
+  };
+#pragma unroll
+  for (int t = 0; t < kDecTiles; ++t) z[t] = floatx4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+  for (int t = 0; t < kDecTiles; t += 2) {
+    if (tw0 + t < tend) {  // wave-uniform
+      z[t] = score(kra, t);
+      if (tw0 + t + 1 < tend) z[t + 1] = score(krb, t + 1);
+      if (t + 2 < kDecTiles && tw0 + t + 2 < tend) kload(t + 2, kra);
+      if (t + 3 < kDecTiles && tw0 + t + 3 < tend) kload(t + 3, krb);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int t = 0; t < kDecTiles; ++t) m[i] = fmaxf(m[i], z[t][i]);
+    if (m[i] != -INFINITY) {
+#pragma unroll
+      for (int t = 0; t < kDecTiles; ++t) l[i] += __builtin_amdgcn_exp2f(z[t][i] - m[i]);
+    }
+    // the 16 lanes of the row hold the same head's other blocks
+    lse_merge_row<0x128>(m[i], l[i]);
+    lse_merge_row<0x124>(m[i], l[i]);
+    lse_merge_row<0x122>(m[i], l[i]);
+    lse_merge_row<0x121>(m[i], l[i]);
+    if (hl == 0) {
+      part[(wave * kMaxG + 4 * gq + i) * 2] = m[i];
+      part[(wave * kMaxG + 4 * gq + i) * 2 + 1] = l[i];
+    }
+  }
+  __syncthreads();
+  float lse2[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * gq + i;
+    float mm = -INFINITY;
+    for (int w = 0; w < kSelWaves; ++w) mm = fmaxf(mm, part[(w * kMaxG + h) * 2]);
+    float ll = 0.f;
+    for (int w = 0; w < kSelWaves; ++w) {
+      const float mw = part[(w * kMaxG + h) * 2];
+      if (mw != -INFINITY) ll += part[(w * kMaxG + h) * 2 + 1] * exp2f(mw - mm);
+    }
+    lse2[i] = h < s.G && mm != -INFINITY ? mm + log2f(ll) : INFINITY;  // heads >= G add nothing
+  }
+  // group scores of this wave's blocks
+#pragma unroll
+  for (int t = 0; t < kDecTiles; ++t) {
+    if (t < tpw && tw0 + t < ntile) {
+      float p = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p += __builtin_amdgcn_exp2f(z[t][i] - lse2[i]);
+      p = sum_xor32(sum_xor16(p));
+      const int j = 16 * (tw0 + t) + hl;
+      if (gq == 0 && j < nv) sig[j] = p;
+    }
+  }
+  __syncthreads();
+  if (wave != 0 || s.topk == 0) return;
+
+  const int qb = pos / kBS;
+  const int lo = s.n_init;
+  const int hi = qb - s.n_local;
+  const int nC = hi >= lo ? hi - lo + 1 : 0;
+  int32_t* out = blk_idx + static_cast<size_t>(b * s.H_kv + g) * s.S_q * s.topk;
+  float* out_s = blk_score ? blk_score + static_cast<size_t>(b * s.H_kv + g) * s.S_q * s.topk : nullptr;
+  if (nC <= s.topk) {
+    for (int e = lane; e < s.topk; e += 64) {
+      out[e] = e < nC ? lo + e : -1;
+      if (out_s) out_s[e] = e < nC ? sig[lo + e] : 0.f;
+    }
+    return;
+  }
+  const int nIt = (nC + 63) / 64;
+  if (nIt <= 1) topk_row<1>(sig + lo, nC, s.topk, lo, out, out_s, lane);
+  else if (nIt <= 2) topk_row<2>(sig + lo, nC, s.topk, lo, out, out_s, lane);
+  else if (nIt <= 4) topk_row<4>(sig + lo, nC, s.topk, lo, out, out_s, lane);
+  else if (nIt <= 8) topk_row<8>(sig + lo, nC, s.topk, lo, out, out_s, lane);
+  else if (nIt <= 16) topk_row<16>(sig + lo, nC, s.topk, lo, out, out_s, lane);
+  else topk_row<32>(sig + lo, nC, s.topk, lo, out, out_s, lane);
+}
+
 template <int R>
 static hipError_t launch_select_r(const uint16_t* q, const uint16_t* k_cmp, int32_t* blk_idx, float* blk_score,
                                   const AttnShape& s, hipStream_t stream) {
@@ -366,6 +518,12 @@ static hipError_t launch_select_r(const uint16_t* q, const uint16_t* k_cmp, int3
 hipError_t launch_select_blocks(const uint16_t* q, const uint16_t* k_cmp, int32_t* blk_idx,
                                 float* blk_score, const AttnShape& s, hipStream_t stream, int lse_stride) {
   if (s.B == 0 || s.S_q == 0) return hipSuccess;
+  if (s.S_q == 1 && lse_stride == 1) {  // one query per sequence: the workgroup splits its blocks
+    const size_t lds = (static_cast<size_t>(kSelWaves) * kMaxG * 2 + sel_stride(s.NB)) * sizeof(float);
+    hipLaunchKernelGGL(select_decode_kernel, dim3(s.B * s.H_kv), dim3(64 * kSelWaves), lds, stream, q, k_cmp,
+                       blk_idx, blk_score, s);
+    return hipGetLastError();
+  }
   switch (lse_stride) {
     case 2: return launch_select_r<2>(q, k_cmp, blk_idx, blk_score, s, stream);
     case 4: return launch_select_r<4>(q, k_cmp, blk_idx, blk_score, s, stream);
