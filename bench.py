@@ -172,6 +172,22 @@ def time_decode_paged(torch, tb, workloads, dev, reps=50):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
+    # the same step captured once as a HIP graph and replayed: a decode step is
+    # a chain of small launches, which a graph issues without per-launch host work
+    graph_ms = None
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph_ms = timed(graph.replay, reps)
+    except RuntimeError as e:  # report, do not fail the benchmark line
+        graph_ms = f"capture failed: {e}"
+
     res = {"paged_step_ms": timed(step, reps),
            "append_ms": timed(lambda: tb.decode_compress_append(kp, table, cur, nxt, k_cmp, 1), reps)}
     idx = tb.decode_select(q, k_cmp, nxt, wl.topk, wl.n_init, wl.n_local)
@@ -184,7 +200,9 @@ def time_decode_paged(torch, tb, workloads, dev, reps=50):
     plan = tb.AttnPlan(wl.B, wl.H_q, wl.H_kv, wl.S_q, wl.S_k, wl.D, wl.block_size, wl.topk, wl.n_init,
                        wl.n_local, 0, None, dev)
     res["contiguous_step_ms"] = timed(lambda: plan.run(qc, kc, vc), reps)
-    return {k: round(v, 4) for k, v in res.items()}
+    res = {k: round(v, 4) for k, v in res.items()}
+    res["paged_step_graph_ms"] = round(graph_ms, 4) if isinstance(graph_ms, float) else graph_ms
+    return res
 
 
 def main():
