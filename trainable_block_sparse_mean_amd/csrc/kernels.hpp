@@ -64,7 +64,8 @@ hipError_t launch_compress_append(const uint16_t* k_pages, const AttnShape& s, c
 hipError_t launch_select_blocks(const uint16_t* q, const uint16_t* k_cmp, int32_t* blk_idx,
                                 float* blk_score, const AttnShape& s, hipStream_t stream, int lse_stride = 1);
 
-// bytes of workspace the attention kernels need (V relayout + split partials)
+// bytes of workspace the sparse forward needs: the split-KV partials (0 when
+// a shape runs unsplit)
 size_t attn_workspace_bytes(const AttnShape& s);
 
 hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
