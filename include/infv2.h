@@ -1,6 +1,9 @@
 /*
- * infv2.h — C ABI of the InfLLM-V2 block-sparse attention forward path for
- * AMD Instinct MI355X (gfx950).
+ * infv2.h — C ABI of the InfLLM-V2 block-sparse attention path for AMD
+ * Instinct MI355X (gfx950): the forward (compression, block selection,
+ * sparse and dense attention, the switch), the sparse backward, decode over a
+ * paged cache, the approximate-LSE selection and the compressed-attention
+ * branch with its mix.
  *
  * The method (pages: "Infllm V2 Dense Sparse Switchable Attention", skill
  * page; "InfLLM-V2: Dense-Sparse Switchable Attention for Seamless
@@ -17,7 +20,9 @@
  *    head dim), as in the shape docstrings of the skill page, Step 2.
  *    bf16 tensors are passed as raw 16-bit patterns (void*).
  *  - All tensor pointers are DEVICE pointers owned by the caller; every
- *    pointer must be 16-byte aligned.  Outputs must not alias inputs.
+ *    pointer must be 16-byte aligned (int32 length and table arrays: 4-byte).
+ *    Outputs must not alias inputs, except where an entry point says so
+ *    (the compressed branch may write its mix over the sparse output).
  *  - GQA: query head h reads KV head h / G with G = H_q / H_kv.
  *  - Query row r sits at absolute position i = (S_k - S_q) + r (bottom-right
  *    alignment; a single decode query is the last token of its cache).

@@ -277,3 +277,23 @@ def test_compressed_branch_validation_codes():
     assert dec(ws=float("nan")) == tb.ERR_INVALID
     assert dec(bs=128) == tb.ERR_UNSUPPORTED
     assert dec(B=0) == tb.OK
+
+
+@no_gpu
+def test_c_program_compiles_links_and_validates(tmp_path):
+    """The header is plain C99 (warnings are errors) and a C program links
+    against the library and gets validation codes back (no GPU call)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not found")
+    exe = tmp_path / "c_abi_smoke"
+    libdir = os.path.dirname(tb.LIB_PATH)
+    src = os.path.join(ROOT, "tests", "c_abi_smoke.c")
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"), src,
+           "-o", str(exe), "-L", libdir, "-linfv2", f"-Wl,-rpath,{libdir}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0 and "c abi ok" in run.stdout, (run.returncode, run.stdout, run.stderr)
