@@ -15,7 +15,7 @@ constexpr int kTileBytes = kBS * kRowBytes;       // one 64-key block of K (or V
 constexpr int kStageBytes = 2 * kTileBytes;       // K + V of one block
 constexpr int kStages = 4;                        // LDS ring: 3 blocks in flight
 constexpr int kXcds = 8;                          // workgroups are dealt round-robin to 8 XCDs
-constexpr int kXcdGroup = 32;                     // windows kept together on one XCD (one per CU)
+constexpr int kXcdGroup = 4;                      // adjacent windows kept together on one XCD
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
