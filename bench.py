@@ -373,6 +373,11 @@ def main():
             tb.compressed_attn_fwd(q, kc2, vc2, wl.S_k, o_sparse=o2, w_sparse=0.5, w_cmp=0.5, out=o2,
                                    return_lse=False)
 
+        def fused_mixed_step():
+            kc2, vc2 = tb.compress_k(k), tb.compress_v(v)
+            idx2 = tb.select_blocks(q, kc2, wl.S_k, wl.topk, wl.n_init, wl.n_local)
+            tb.mixed_attn_fwd(q, k, v, idx2, kc2, vc2, 0.5, 0.5, wl.n_init, wl.n_local, return_lse=False)
+
         def avg_ms(f, n=5):
             f()
             torch.cuda.synchronize()
@@ -392,6 +397,9 @@ def main():
                       "branch_mixed_ms": round(mix_ms, 4),
                       "compress_v_ms": round(avg_ms(lambda: tb.compress_v(v)), 4),
                       "mixed_step_ms": round(avg_ms(mixed_step), 4),
+                      "fused_mixed_attn_ms": round(avg_ms(lambda: tb.mixed_attn_fwd(
+                          q, k, v, idx, kc, vc, 0.5, 0.5, wl.n_init, wl.n_local, return_lse=False)), 4),
+                      "fused_mixed_step_ms": round(avg_ms(fused_mixed_step), 4),
                       "branch_flops": cmp_flops}
         del kc, vc, idx, o_sp, buf
 

@@ -307,6 +307,24 @@ int infv2_compressed_attn_fwd(const void* q, const void* k_cmp, const void* v_cm
                               int block_size, float softmax_scale,
                               float w_sparse, float w_cmp, void* stream);
 
+/* The block-sparse attention and the compressed branch in one call:
+ *   out = w_sparse * infv2_sparse_attn_fwd(...) + w_cmp * compressed branch
+ * with the arguments and layouts of infv2_sparse_attn_fwd plus k_cmp, v_cmp
+ * of infv2_compressed_attn_fwd; lse is the sparse attention's.  One launch
+ * streams each query window's compressed groups and then its selected blocks
+ * through the same pipeline; the branch passes through out (rounded once to
+ * bf16) before the sparse part is added.  Shapes whose block lists are split
+ * over several workgroups (few query windows, as in decode) run the two
+ * calls one after the other instead, with the same result definition.
+ * Workspace: infv2_sparse_workspace_bytes(...). */
+int infv2_mixed_attn_fwd(const void* q, const void* k, const void* v,
+                         const int32_t* blk_idx, const void* k_cmp, const void* v_cmp,
+                         void* out, float* lse,
+                         int B, int H_q, int H_kv, int S_q, int S_k, int D,
+                         int block_size, int topk, int n_init, int n_local,
+                         float softmax_scale, float w_sparse, float w_cmp,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* The compressed-attention branch of each decode query (as
  * infv2_compressed_attn_fwd for S_q = 1 on that sequence): k_cmp, v_cmp
  * [B][H_kv][max_blocks][D] from infv2_decode_compress_append on the key and

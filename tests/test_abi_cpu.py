@@ -34,7 +34,7 @@ def test_header_declares_expected_entry_points():
     for n in ["infv2_compress_k", "infv2_select_blocks", "infv2_sparse_attn_fwd", "infv2_dense_attn_fwd",
               "infv2_attn_fwd", "infv2_sparse_attn_bwd", "infv2_status_string", "infv2_decode_compress_append",
               "infv2_decode_select", "infv2_decode_attn", "infv2_compress_v", "infv2_compressed_attn_fwd",
-              "infv2_decode_compressed_attn"]:
+              "infv2_decode_compressed_attn", "infv2_mixed_attn_fwd"]:
         assert n in names
 
 
@@ -297,3 +297,21 @@ def test_c_program_compiles_links_and_validates(tmp_path):
     assert r.returncode == 0, r.stderr
     run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert run.returncode == 0 and "c abi ok" in run.stdout, (run.returncode, run.stdout, run.stderr)
+
+
+@no_gpu
+def test_mixed_attn_validation_codes():
+    lib = tb.load_library()
+    mix = lambda **kw: lib.infv2_mixed_attn_fwd(
+        kw.get("q", FAKE), FAKE, FAKE, kw.get("idx", FAKE), kw.get("kc", FAKE), FAKE, FAKE, kw.get("lse", None),
+        kw.get("B", 1), 32, 2, kw.get("S_q", 4096), 4096, kw.get("D", 128), 64, kw.get("topk", 8), 1,
+        kw.get("n_local", 2), 0.0, kw.get("ws", 0.5), 0.5, kw.get("wsp", None), kw.get("wsb", 0), None)
+    assert mix(kc=None) == tb.ERR_INVALID
+    assert mix(idx=None) == tb.ERR_INVALID                       # topk > 0 needs the selection
+    assert mix(lse=FAKE + 8) == tb.ERR_INVALID
+    assert mix(ws=float("nan")) == tb.ERR_INVALID
+    assert mix(n_local=0) == tb.ERR_INVALID
+    assert mix(D=64) == tb.ERR_UNSUPPORTED
+    assert mix(topk=300) == tb.ERR_UNSUPPORTED
+    assert mix(S_q=1) == tb.ERR_WORKSPACE                        # one query row: split partials needed
+    assert mix(B=0) == tb.OK

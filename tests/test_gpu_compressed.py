@@ -200,3 +200,29 @@ def test_decode_compressed_branch_and_mix(name, lens, H_q, H_kv):
     log("  branch:", assert_attn_close(out[sm], lse[sm], ref[seen], ref_lse[seen], name))
     ref_mix = O.mix_patterns([np64(o_sp), ref], [0.5, 0.5])
     log("  mix:", assert_attn_close(mixed, None, ref_mix, None, name + " mix"))
+
+
+MIX_CASES = CASES[:4] + [("long_32k_rows", workloads.LONG_32K, np.unique(np.concatenate(
+    [np.arange(0, 100), np.linspace(100, 32767, 200).astype(int)])))]
+
+
+@pytest.mark.parametrize("name,w,rows", MIX_CASES, ids=[c[0] for c in MIX_CASES])
+def test_mixed_attn_in_one_call_matches_oracle(name, w, rows):
+    """infv2_mixed_attn_fwd: w_sparse * sparse + w_cmp * branch against the
+    oracle's sparse attention (on the GPU's selection) and branch (on the
+    GPU's compressed keys and values).  ragged_sq37 takes the two-call path
+    (its block lists are split), the others the fused kernel."""
+    log("mixed one call", name)
+    q, k, v, kc, vc, rows = _branch_case(w, rows)
+    idx = tb.select_blocks(q, kc, w.S_k, w.topk, w.n_init, w.n_local)
+    ws_, wc_ = 0.7, 0.3
+    out, lse = tb.mixed_attn_fwd(q, k, v, idx, kc, vc, ws_, wc_, w.n_init, w.n_local)
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(w.D)
+    qr = sparse_rows_q(q, rows)
+    ti = torch.as_tensor(rows, device=DEV)
+    so, sl = O.sparse_attn(qr, np64(k), np64(v), idx.cpu().numpy()[:, :, rows], BS, w.n_init, w.n_local, scale,
+                           rows=rows)
+    co, _ = O.compressed_attn(qr, np64(kc), np64(vc), w.S_k, BS, scale, rows=rows)
+    ref = O.mix_patterns([so, co], [ws_, wc_])
+    log("  ", assert_attn_close(out[:, :, ti], lse[:, :, ti], ref, sl, name))

@@ -8,8 +8,8 @@ the GPU.
 
 Names follow the C entry points without their ``infv2_`` prefix:
 ``compress_k``, ``select_blocks``, ``sparse_attn_fwd``, ``dense_attn_fwd``,
-``attn_fwd``, the decode calls (``decode_*``), ``compress_v`` and
-``compressed_attn_fwd``.
+``attn_fwd``, the decode calls (``decode_*``), ``compress_v``,
+``compressed_attn_fwd`` and ``mixed_attn_fwd``.
 """
 from __future__ import annotations
 
@@ -48,6 +48,7 @@ SIGNATURES = {
     "infv2_compress_v": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
     "infv2_compressed_attn_fwd": (_c_int, [_vp] * 6 + [_c_int] * 7 + [_c_float] * 3 + [_vp]),
     "infv2_decode_compressed_attn": (_c_int, [_vp] * 7 + [_c_int] * 6 + [_c_float] * 3 + [_vp]),
+    "infv2_mixed_attn_fwd": (_c_int, [_vp] * 8 + [_c_int] * 10 + [_c_float] * 3 + [_vp, _c_size, _vp]),
 }
 
 _lib = None
@@ -297,6 +298,28 @@ def compressed_attn_fwd(q, k_cmp, v_cmp, S_k: int, o_sparse=None, w_sparse: floa
     lse = torch.empty(B, H_q, S_q, dtype=torch.float32, device=q.device) if return_lse else None
     _call("infv2_compressed_attn_fwd", _ptr(q), _ptr(k_cmp), _ptr(v_cmp), _ptr(o_sparse), _ptr(out), _ptr(lse),
           B, H_q, H_kv, S_q, S_k, D, block_size, _scale(softmax_scale), float(w_sparse), float(w_cmp), _stream())
+    return out, lse
+
+
+def mixed_attn_fwd(q, k, v, blk_idx, k_cmp, v_cmp, w_sparse: float, w_cmp: float, n_init: int = 1,
+                   n_local: int = 2, softmax_scale=None, block_size: int = 64, return_lse: bool = True):
+    """Block-sparse attention and the compressed branch in one call:
+    out = w_sparse * O_sparse + w_cmp * O_cmp.  Arguments as sparse_attn_fwd
+    plus k_cmp, v_cmp (bf16 [B,H_kv,ceil(S_k/64),D]).  Returns (out, lse of
+    the sparse attention)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (k_cmp, "k_cmp"), (v_cmp, "v_cmp")):
+        _need(t, n, torch.bfloat16, 4)
+    _need(blk_idx, "blk_idx", torch.int32, 4)
+    B, H_q, S_q, D = q.shape
+    H_kv, S_k = k.shape[1], k.shape[2]
+    topk = blk_idx.shape[3]
+    out = torch.empty_like(q)
+    lse = torch.empty(B, H_q, S_q, dtype=torch.float32, device=q.device) if return_lse else None
+    nbytes = load_library().infv2_sparse_workspace_bytes(B, H_q, H_kv, S_q, S_k, D, block_size, topk)
+    ws = _workspace(nbytes, q.device)
+    _call("infv2_mixed_attn_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(blk_idx), _ptr(k_cmp), _ptr(v_cmp), _ptr(out),
+          _ptr(lse), B, H_q, H_kv, S_q, S_k, D, block_size, topk, n_init, n_local, _scale(softmax_scale),
+          float(w_sparse), float(w_cmp), _ptr(ws), ws.numel(), _stream())
     return out, lse
 
 

@@ -392,6 +392,32 @@ int infv2_compressed_attn_fwd(const void* q, const void* k_cmp, const void* v_cm
       static_cast<hipStream_t>(stream)));
 }
 
+int infv2_mixed_attn_fwd(const void* q, const void* k, const void* v, const int32_t* blk_idx, const void* k_cmp,
+                         const void* v_cmp, void* out, float* lse, int B, int H_q, int H_kv, int S_q, int S_k, int D,
+                         int block_size, int topk, int n_init, int n_local, float softmax_scale, float w_sparse,
+                         float w_cmp, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(B, H_q, H_kv, S_q, S_k, D);
+  if (st != INFV2_OK) return st;
+  st = check_sparse_params(block_size, topk, n_init, n_local);
+  if (st != INFV2_OK) return st;
+  if (!isfinite(w_sparse) || !isfinite(w_cmp)) return INFV2_ERR_INVALID;
+  if (num_blocks(S_k, block_size) > kMaxSparseBlocks) return INFV2_ERR_UNSUPPORTED;
+  if (B == 0 || S_q == 0) return INFV2_OK;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(k_cmp) || !tensor_ok(v_cmp) || !tensor_ok(out))
+    return INFV2_ERR_INVALID;
+  if (topk > 0 && !tensor_ok(blk_idx)) return INFV2_ERR_INVALID;
+  if (lse && !aligned(lse, 16)) return INFV2_ERR_INVALID;
+  const size_t need = sparse_ws(B, H_q, H_kv, S_q, S_k, block_size, topk);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return INFV2_ERR_WORKSPACE;
+  if (workspace && !aligned(workspace, 256)) return INFV2_ERR_INVALID;
+  const AttnShape s = make_shape(B, H_q, H_kv, S_q, S_k, block_size, topk, n_init, n_local,
+                                 scale_log2(softmax_scale, D), 1);
+  return hip_status(infv2::launch_mixed_attn(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), blk_idx,
+      static_cast<const uint16_t*>(k_cmp), static_cast<const uint16_t*>(v_cmp), static_cast<uint16_t*>(out), lse, s,
+      w_sparse, w_cmp, workspace, static_cast<hipStream_t>(stream)));
+}
+
 int infv2_decode_compressed_attn(const void* q, const void* k_cmp, const void* v_cmp, const int32_t* seqlens,
                                  const void* o_sparse, void* out, float* lse, int B, int H_q, int H_kv, int D,
                                  int block_size, int max_blocks, float softmax_scale, float w_sparse, float w_cmp,

@@ -312,16 +312,36 @@ __device__ __forceinline__ void dense_block(DenseState& st, const DenseLane& ln,
   }
 }
 
+// The compressed-attention branch of the mixed launch (see launch_mixed_attn)
+struct MixArgs {
+  const uint16_t* kc;  // compressed keys / values [B][H_kv][NB][D]
+  const uint16_t* vc;
+  float w_sparse, w_cmp;
+};
+
+// List entry e of the compressed branch: group e (compressed rows 64e ..
+// 64e+63) | the window's tokens that see its first row (token t of a window
+// of nq tokens from query row r0, key position off + r0 + t, sees row 64e iff
+// off + r0 + t + 1 >= 64 (64e + 1)).
+__device__ __forceinline__ uint32_t cmp_entry(int e, int off, int r0, int nq) {
+  const int t_min = max(0, kBS * (kBS * e + 1) - 1 - off - r0);
+  const uint32_t mask = t_min >= nq ? 0u : ((1u << nq) - 1u) & ~((1u << t_min) - 1u);
+  return static_cast<uint32_t>(e) | (mask << 16);
+}
+
 // PAGED: K/V in the pages of a paged cache, per-sequence lengths (decode);
-// otherwise contiguous K/V of one key length.
-template <bool DENSE, bool PAGED>
+// otherwise contiguous K/V of one key length.  MIX: the compressed branch runs
+// first on the same pipeline and the epilogue mixes it into the output.
+template <bool DENSE, bool PAGED, bool MIX>
 __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel(const uint16_t* __restrict__ q,
                                                                      const uint16_t* __restrict__ k,
                                                                      const uint16_t* __restrict__ v,
                                                                      const int32_t* __restrict__ blk_idx,
                                                                      uint16_t* __restrict__ out,
                                                                      float* __restrict__ lse,
-                                                                     float* __restrict__ part, AttnShape s) {
+                                                                     float* __restrict__ part, AttnShape s,
+                                                                     MixArgs mx) {
+  static_assert(!MIX || (!DENSE && !PAGED), "the mix runs on the contiguous sparse path");
   constexpr int kWaves = Cfg<DENSE>::kWaves;
   constexpr int T = Cfg<DENSE>::kTok;
   constexpr int NT = kWaves * 64;
@@ -398,6 +418,40 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
     nblk = s.causal ? qb_last + 1 : s.NB;
   } else {
     nblk = build_union_list<NT>(bmask, blist, &n_list, blk_idx, bg, r0, off, qb_last, s, wave, lane);
+    if constexpr (MIX) {
+      // The compressed branch first, streamed like a block list (64
+      // compressed rows side by side have a key block's layout; the token
+      // sees rows 0 .. nv-1): its output times w_cmp goes to out, which the
+      // epilogue reads back.  Then the state restarts for the sparse part.
+      static_assert(T == 1, "one token per wave");
+      const int hl = lane & 15, gq = lane >> 4;
+      const int nq = min(kWin, s.S_q - r0);
+      const int ngrp = ((off + r0 + nq) / kBS + kBS - 1) / kBS;
+      const BlockSrc<false> csrc{mx.kc + bg * s.NB * kD, mx.vc + bg * s.NB * kD, nullptr, s.NB, 0, s.H_kv, b, g,
+                                 s.NB};
+      sp[0].lim = (off + rw + 1) / kBS - 1;  // last visible compressed row (-1: none)
+      const SparseLane cspl = sparse_lane(hl, gq);
+      stream_pairs<kWaves>(smem, csrc, 0, ngrp, [&](int e) { return cmp_entry(e, off, r0, nq); }, wave, lane,
+                           [&](const unsigned char* const* stg, const int* js, uint32_t cur0, uint32_t cur1) {
+        const uint32_t bit = 1u << (16 + wave);
+        attend_pair(sp[0], cspl, stg, js, (cur0 & bit) != 0u, (cur1 & bit) != 0u, lane, sl2);
+      });
+      const float l = sum_xor32(sum_xor16(sp[0].l));
+      if (rw < s.S_q && hl < s.G) {
+        const float scl = l > 0.f ? mx.w_cmp / l : 0.f;  // no visible block: the branch is zero
+        uint16_t* orow = out + (static_cast<size_t>(b * s.H_q + g * s.G + hl) * s.S_q + rw) * kD + 4 * gq;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          *reinterpret_cast<u32x2*>(orow + 16 * dt) = u32x2{pack_bf16x2(sp[0].o[dt][0] * scl, sp[0].o[dt][1] * scl),
+                                                           pack_bf16x2(sp[0].o[dt][2] * scl, sp[0].o[dt][3] * scl)};
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) sp[0].o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      sp[0].m = -INFINITY;
+      sp[0].l = 0.f;
+      sp[0].lim = min(off + rw, S_k - 1);
+      __syncthreads();  // every wave is done with the ring
+    }
   }
   // entry e of the list (dense: every block in order)
   auto entry_at = [&](int e) -> uint32_t {
@@ -483,12 +537,21 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
         }
         continue;
       }
-      const float inv = 1.f / l;
+      const float inv = MIX ? mx.w_sparse / l : 1.f / l;
       uint16_t* orow = out + (static_cast<size_t>(b * s.H_q + h) * s.S_q + r) * kD + 4 * gq;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const u32x2 w = {pack_bf16x2(sp[t].o[dt][0] * inv, sp[t].o[dt][1] * inv),
-                         pack_bf16x2(sp[t].o[dt][2] * inv, sp[t].o[dt][3] * inv)};
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = sp[t].o[dt][e] * inv;
+        if constexpr (MIX) {  // this lane wrote these four values in the branch phase
+          const u32x2 c = *reinterpret_cast<const u32x2*>(orow + 16 * dt);
+          y[0] += bf16_lo(c[0]);
+          y[1] += bf16_hi(c[0]);
+          y[2] += bf16_lo(c[1]);
+          y[3] += bf16_hi(c[1]);
+        }
+        const u32x2 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
         *reinterpret_cast<u32x2*>(orow + 16 * dt) = w;
       }
       if (lse && gq == 0) lse[static_cast<size_t>(b * s.H_q + h) * s.S_q + r] = (sp[t].m + log2f(l)) * kLn2;
@@ -590,11 +653,7 @@ __global__ __launch_bounds__(kWin * 64, 1) void compressed_attn_kernel(const uin
   }
   // list entry e: group e | the window's tokens that see its first row
   // (token t sees row 64e iff off + r0 + t + 1 >= 64 (64e + 1))
-  auto entry_at = [&](int e) -> uint32_t {
-    const int t_min = max(0, kBS * (kBS * e + 1) - 1 - off - r0);
-    const uint32_t mask = t_min >= nq ? 0u : ((1u << nq) - 1u) & ~((1u << t_min) - 1u);
-    return static_cast<uint32_t>(e) | (mask << 16);
-  };
+  auto entry_at = [&](int e) -> uint32_t { return cmp_entry(e, off, r0, nq); };
   const SparseLane spl = sparse_lane(hl, gq);
   stream_pairs<kWaves>(smem, src, 0, ngrp, entry_at, wave, lane,
                        [&](const unsigned char* const* stg, const int* js, uint32_t cur0, uint32_t cur1) {
@@ -651,21 +710,27 @@ size_t attn_workspace_bytes(const AttnShape& s) {
   return static_cast<size_t>(ns) * s.B * s.H_q * s.S_q * kPartFloats * sizeof(float);
 }
 
-template <bool DENSE>
+template <bool DENSE, bool MIX = false>
 static hipError_t launch_window(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* blk_idx,
-                                uint16_t* out, float* lse, float* part, const AttnShape& s, hipStream_t stream) {
+                                uint16_t* out, float* lse, float* part, const AttnShape& s, hipStream_t stream,
+                                MixArgs mx = MixArgs{nullptr, nullptr, 0.f, 0.f}) {
   const int nwin = (s.S_q + kWin - 1) / kWin;
   const dim3 grid(padded_grid(nwin, s.B * s.H_kv), DENSE ? 1 : s.nsplit);
   const size_t lds = kStages * kStageBytes + (DENSE ? 0 : 2 * sizeof(int) * static_cast<size_t>(s.NB));
+  if constexpr (MIX) {
+    hipLaunchKernelGGL((attn_window_kernel<false, false, true>), grid, dim3(Cfg<false>::kWaves * 64), lds, stream, q,
+                       k, v, blk_idx, out, lse, part, s, mx);
+    return hipGetLastError();
+  }
   if constexpr (!DENSE) {  // the dense kernel has no paged form
     if (s.block_table) {
-      hipLaunchKernelGGL((attn_window_kernel<false, true>), grid, dim3(Cfg<false>::kWaves * 64), lds, stream, q, k,
-                         v, blk_idx, out, lse, part, s);
+      hipLaunchKernelGGL((attn_window_kernel<false, true, false>), grid, dim3(Cfg<false>::kWaves * 64), lds, stream, q,
+                         k, v, blk_idx, out, lse, part, s, mx);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((attn_window_kernel<DENSE, false>), grid, dim3(Cfg<DENSE>::kWaves * 64), lds, stream, q, k, v,
-                     blk_idx, out, lse, part, s);
+  hipLaunchKernelGGL((attn_window_kernel<DENSE, false, false>), grid, dim3(Cfg<DENSE>::kWaves * 64), lds, stream, q,
+                     k, v, blk_idx, out, lse, part, s, mx);
   return hipGetLastError();
 }
 
@@ -681,6 +746,21 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16
   const size_t rows = static_cast<size_t>(s.B) * s.H_q * s.S_q;
   hipLaunchKernelGGL(combine_splits_kernel, dim3(rows), dim3(128), 0, stream, part, out, lse, s.nsplit, rows);
   return hipGetLastError();
+}
+
+hipError_t launch_mixed_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* blk_idx,
+                             const uint16_t* k_cmp, const uint16_t* v_cmp, uint16_t* out, float* lse,
+                             const AttnShape& s_in, float w_sparse, float w_cmp, void* workspace, hipStream_t stream) {
+  if (s_in.B == 0 || s_in.S_q == 0) return hipSuccess;
+  AttnShape s = s_in;
+  s.nsplit = sparse_splits(s.B, s.H_kv, s.S_q, s.topk);
+  if (s.nsplit > 1) {  // few query windows: the sparse output, then the branch mixed into it in place
+    hipError_t err = launch_sparse_attn(q, k, v, blk_idx, out, lse, s_in, workspace, stream);
+    if (err != hipSuccess) return err;
+    return launch_compressed_attn(q, k_cmp, v_cmp, out, out, nullptr, s_in, w_sparse, w_cmp, stream);
+  }
+  return launch_window<false, true>(q, k, v, blk_idx, out, lse, nullptr, s, stream,
+                                    MixArgs{k_cmp, v_cmp, w_sparse, w_cmp});
 }
 
 hipError_t launch_dense_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -84,6 +84,14 @@ hipError_t launch_compressed_attn(const uint16_t* q, const uint16_t* k_cmp, cons
                                   const uint16_t* o_sparse, uint16_t* out, float* lse, const AttnShape& s,
                                   float w_sparse, float w_cmp, hipStream_t stream);
 
+// The block-sparse attention and the compressed branch in one launch: out =
+// w_sparse * O_sparse + w_cmp * O_cmp (the branch goes through out in bf16 on
+// its way); lse is the sparse attention's.  Shapes that split the block list
+// (few query windows) run the two kernels one after the other instead.
+hipError_t launch_mixed_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* blk_idx,
+                             const uint16_t* k_cmp, const uint16_t* v_cmp, uint16_t* out, float* lse,
+                             const AttnShape& s, float w_sparse, float w_cmp, void* workspace, hipStream_t stream);
+
 // workspace of the sparse backward: D = <dO, O> per (token, head), then the
 // selected-entry bitmap (one bit per KV head, block and query token)
 size_t attn_bwd_workspace_bytes(const AttnShape& s);
