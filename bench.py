@@ -120,6 +120,41 @@ def cpu_baseline(w, x, target_s=15.0):
                 step_s_estimate=step_s)
 
 
+def dist(ms):
+    """Median, 10th and 90th percentile of per-call times (ms)."""
+    a = sorted(ms)
+    pick = lambda f: a[min(len(a) - 1, int(round(f * (len(a) - 1))))]
+    return {"median": round(pick(0.5), 4), "p10": round(pick(0.1), 4), "p90": round(pick(0.9), 4), "calls": len(a)}
+
+
+def measured_gemm_tflops(torch, dev, n=8192, reps=10):
+    """bf16 GEMM throughput of the installed BLAS (torch.matmul, n x n x n):
+    the practical MFMA ceiling the kernels are also set against."""
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    c0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    c1.record()
+    torch.cuda.synchronize()
+    return 2.0 * n ** 3 / (c0.elapsed_time(c1) / reps * 1e-3) / 1e12
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def seeded_dout(q, torch):
     """A seeded gradient of the attention output (bf16, N(0,1))."""
     g = torch.Generator(device="cpu")
@@ -287,6 +322,7 @@ def main():
     stages = {"compress": 0.0, "select": 0.0, "sparse_attn": 0.0}
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     reps = max(3, args.steps)
+    attn_calls = []
     for _ in range(reps):
         ev[0].record()
         kc = tb.compress_k(k)
@@ -299,6 +335,22 @@ def main():
         stages["compress"] += ev[0].elapsed_time(ev[1]) / reps
         stages["select"] += ev[1].elapsed_time(ev[2]) / reps
         stages["sparse_attn"] += ev[2].elapsed_time(ev[3]) / reps
+        attn_calls.append(ev[2].elapsed_time(ev[3]))
+
+    # ---- the same call with a cold last-level cache: 512 MiB written between
+    # calls (outside the timed events) evicts the 256 MB MALL, which otherwise
+    # holds the whole K/V of one layer at 32k ---------------------------------
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold_calls = []
+    for i in range(reps):
+        flush.fill_(i & 0xFF)
+        ev[0].record()
+        tb.sparse_attn_fwd(q, k, v, idx, wl.n_init, wl.n_local, return_lse=False)
+        ev[1].record()
+        torch.cuda.synchronize()
+        cold_calls.append(ev[0].elapsed_time(ev[1]))
+    del flush
+    gemm_tflops = measured_gemm_tflops(torch, dev)
 
     dense_ms = None
     if not args.no_dense:
@@ -414,6 +466,8 @@ def main():
         cb = cpu_baseline(wl, x)
         cpu = {kk: cb[kk] for kk in ("value", "unit", "cores", "kind", "sample")}
         cpu["value"] = round(cpu["value"], 6)
+        cpu["cpu_model"] = cpu_model()
+        cpu["host_cpus"] = os.cpu_count()
 
     out = {
         "metric": "sparse-attn fwd ms & effective TFLOP/s at 32k; speedup vs dense; % MFMA peak",
@@ -437,6 +491,10 @@ def main():
         "sparse_attn_tflops": round(attn_tflops, 2),
         "mfma_peak_frac_attn": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
         "mfma_peak_frac_step": round(value / PEAK_BF16_TFLOPS, 4),
+        "sparse_attn_call_ms": dist(attn_calls),
+        "sparse_attn_cold_mall_ms": dist(cold_calls),
+        "measured_gemm_tflops": round(gemm_tflops, 1),
+        "frac_of_measured_gemm": round(attn_tflops / gemm_tflops, 4),
         "dense_attn_ms": None if dense_ms is None else round(dense_ms, 4),
         "dense_attn_tflops": None if dense_ms is None else round(dense_flops / (dense_ms * 1e-3) / 1e12, 2),
         "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms_step, 3),
