@@ -157,8 +157,8 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
           const int kt = 2 * s2 + x;
-          kf[x] = as_bf16x8(load16(stg + ln.k(ks) + kt * 16 * kRowBytes));
-          vf[x] = as_bf16x8(load16(stg + kTileBytes + ln.k(ks) + kt * 16 * kRowBytes));
+          kf[x] = as_bf16x8(lds_load16(stg + ln.k(ks) + kt * 16 * kRowBytes));
+          vf[x] = as_bf16x8(lds_load16(stg + kTileBytes + ln.k(ks) + kt * 16 * kRowBytes));
         }
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(
 
   const uint32_t bit = 1u << (16 + wave);
   const BlockSrc<false> src{kg, vg, nullptr, s.NB, 0, s.H_kv, 0, 0, s.S_k};
-  stream_pairs<kBwdDqWaves>(smem, src, 0, nblk, entry_at, wave, lane,
+  stream_pairs<kBwdDqWaves, true>(smem, src, 0, nblk, entry_at, wave, lane,
                             [&](const unsigned char* const* stg, const int* js, uint32_t cur0, uint32_t cur1) {
                               // one copy of the item code for both blocks of the pair
 #pragma unroll 1

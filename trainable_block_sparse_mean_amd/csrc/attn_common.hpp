@@ -25,6 +25,13 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
+// 16 bytes from LDS through an LDS pointer.  A generic load of an address the
+// compiler cannot trace back to shared memory (a stage pointer picked at run
+// time) becomes a flat load, which also counts against vmcnt: every wait for
+// it would then wait for the ring's direct-to-LDS loads in flight as well.
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+__device__ __forceinline__ u32x4 lds_load16(const unsigned char* p) { return *(const lds_u32x4*)(p); }
+
 __device__ __forceinline__ floatx16 mfma_32x32x16(bf16x8 a, bf16x8 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -56,6 +63,14 @@ struct DmaLane {
   static constexpr int kChunks = 16 / WAVES;
   uint32_t off[kChunks];
 };
+// The lane id, read in asm so that it is recomputed where it is used rather
+// than kept live (and possibly spilled) across a loop.
+__device__ __forceinline__ int lane_id_opaque() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 template <int WAVES>
 __device__ __forceinline__ DmaLane<WAVES> dma_lane(int wave, int lane) {
   DmaLane<WAVES> d;
@@ -224,27 +239,33 @@ __device__ __forceinline__ int build_union_list(uint32_t* bmask, int* blist, int
 // ring holds the pair being multiplied (2 stages) and the next pair in flight
 // (the other 2); one barrier per pair.  on_pair(stg, js, cur0, cur1) gets the
 // two stages, their blocks and their list entries (cur1 = 0 past the end).
-template <int WAVES, typename Src, typename Entry, typename F>
+// FRESH_DMA rebuilds the lane's DMA offsets at every issue from a lane id the
+// compiler cannot hoist.  A kernel at its register limit would otherwise
+// spill them and reload each from scratch just before its loads; the vmcnt
+// wait for that reload also waits for the loads issued before it, which
+// serialises the issue.
+template <int WAVES, bool FRESH_DMA = false, typename Src, typename Entry, typename F>
 __device__ __forceinline__ void stream_pairs(unsigned char* smem, const Src& src, int e_lo, int e_hi,
                                              Entry entry_at, int wave, int lane, F&& on_pair) {
   static_assert(kStages == 4, "two pairs of stages");
   const uint32_t ring = lds_addr(smem);
-  const DmaLane<WAVES> dl = dma_lane<WAVES>(wave, lane);
+  const DmaLane<WAVES> dl_kept = dma_lane<WAVES>(wave, lane);
+  auto dl_fresh = [&]() { return FRESH_DMA ? dma_lane<WAVES>(wave, lane_id_opaque()) : dl_kept; };
   const int nseg = e_hi - e_lo;
   auto seg_at = [&](int x) -> uint32_t { return x < nseg ? entry_at(e_lo + x) : 0u; };
   const int npair = (nseg + 1) / 2;
   uint32_t cur0 = __builtin_amdgcn_readfirstlane(seg_at(0)), cur1 = __builtin_amdgcn_readfirstlane(seg_at(1));
   uint32_t nxt0 = __builtin_amdgcn_readfirstlane(seg_at(2)), nxt1 = __builtin_amdgcn_readfirstlane(seg_at(3));
-  if (nseg > 0) stage_src(ring, src, cur0 & 0xffffu, dl, wave, lane);
-  if (nseg > 1) stage_src(ring + kStageBytes, src, cur1 & 0xffffu, dl, wave, lane);
+  if (nseg > 0) stage_src(ring, src, cur0 & 0xffffu, dl_fresh(), wave, lane);
+  if (nseg > 1) stage_src(ring + kStageBytes, src, cur1 & 0xffffu, dl_fresh(), wave, lane);
   for (int pi = 0; pi < npair; ++pi) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // pair pi is in LDS; every wave is done with pair pi - 1
     const int half = (pi & 1) * 2;  // first stage of pair pi
     if (2 * pi + 2 < nseg) {
-      stage_src(ring + (half ^ 2) * kStageBytes, src, nxt0 & 0xffffu, dl, wave, lane);
+      stage_src(ring + (half ^ 2) * kStageBytes, src, nxt0 & 0xffffu, dl_fresh(), wave, lane);
       if (2 * pi + 3 < nseg)
-        stage_src(ring + ((half ^ 2) + 1) * kStageBytes, src, nxt1 & 0xffffu, dl, wave, lane);
+        stage_src(ring + ((half ^ 2) + 1) * kStageBytes, src, nxt1 & 0xffffu, dl_fresh(), wave, lane);
     }
     const unsigned char* stg[2] = {smem + half * kStageBytes, smem + (half + 1) * kStageBytes};
     const int js[2] = {static_cast<int>(cur0 & 0xffffu), static_cast<int>(cur1 & 0xffffu)};
