@@ -313,14 +313,22 @@ __global__ __launch_bounds__(kBwdKvWaves * 64, 3) void attn_bwd_dkdv_kernel(
   const int r_first = max(0, j * kBS - off);
   const int f_hi = j < s.n_init ? s.S_q : min(s.S_q, (j + s.n_local) * kBS - off);
   const uint32_t* bmrow = bm + (bg * s.NB + j) * W;
-  // this piece's tokens: [t_lo, t_hi), a share of [r_first, S_q) rounded to whole bitmap words
-  const int w0 = r_first & ~31;                                   // word holding r_first
-  const int share = ((max(0, s.S_q - w0) + s.nsplit - 1) / s.nsplit + 31) & ~31;
-  const int t_lo = min(s.S_q, w0 + piece * share);
-  const int t_hi = min(s.S_q, w0 + (piece + 1) * share);
+  // this piece's tokens: [t_lo, t_hi), the same token range for every block
+  // (whole bitmap words).  The chunks, and the pairs within a chunk, are
+  // walked downwards from the top of the piece: on unrelated selections every
+  // visible block has about the same share of member tokens at any position,
+  // so the workgroups of a piece start at the same token and move down it at
+  // about the same pace, and the Q and dO rows they gather are shared through
+  // L2 instead of each being fetched once per block.
+  const int share = ((s.S_q + s.nsplit - 1) / s.nsplit + 31) & ~31;
+  const int t_lo = min(s.S_q, piece * share);
+  const int t_hi = min(s.S_q, (piece + 1) * share);
   const int m_lo = max(r_first, t_lo);  // first token that can be a member
+  const int nchunk = t_hi > m_lo ? (t_hi - t_lo + kMemberChunk - 1) / kMemberChunk : 0;
 
-  for (int c0 = t_lo; c0 < t_hi; c0 += kMemberChunk) {
+  for (int ci = nchunk - 1; ci >= 0; --ci) {
+    const int c0 = t_lo + ci * kMemberChunk;
+    if (c0 + kMemberChunk <= m_lo) break;  // this chunk and those below hold no member
     // member tokens of [c0, c0 + kMemberChunk), ascending, built by wave 0
     if (wave == 0) {
       const int r32 = c0 + 32 * lane;  // this lane's word (lanes 0..31)
@@ -354,7 +362,11 @@ __global__ __launch_bounds__(kBwdKvWaves * 64, 3) void attn_bwd_dkdv_kernel(
     __syncthreads();
     const int nm = *mcount;
     const int npair = (nm + 1) / 2;
-    auto pair_tok = [&](int p, int x) { return c0 + (2 * p + x < nm ? mlist[2 * p + x] : mlist[2 * p]); };
+    // the p-th pair walked is the (npair - 1 - p)-th of the ascending list
+    auto pair_tok = [&](int p, int x) {
+      const int pq = npair - 1 - p;
+      return c0 + (2 * pq + x < nm ? mlist[2 * pq + x] : mlist[2 * pq]);
+    };
     auto stage = [&](int p) {
       stage_pair(lbase + (p % kPairBufs) * kKvBufBytes, qg, dg, lg, sg, s.S_q, s.G, pair_tok(p, 0), pair_tok(p, 1),
                  wave, lane);
@@ -372,9 +384,10 @@ __global__ __launch_bounds__(kBwdKvWaves * 64, 3) void attn_bwd_dkdv_kernel(
       const unsigned char* qt = smem + (p % kPairBufs) * kKvBufBytes;
       const unsigned char* dt_ = qt + kPairBytes;
       const float* st = reinterpret_cast<const float*>(qt + 2 * kPairBytes);  // lse[32], D[32]
-      const int tA = c0 + mlist[2 * p];
-      const bool hasB = 2 * p + 1 < nm;
-      const int tB = hasB ? c0 + mlist[2 * p + 1] : tA;
+      const int pq = npair - 1 - p;
+      const int tA = c0 + mlist[2 * pq];
+      const bool hasB = 2 * pq + 1 < nm;
+      const int tB = hasB ? c0 + mlist[2 * pq + 1] : tA;
       // log-sum-exp (log2 units) and D of the rows this lane holds: (token t, heads 4*gq .. 4*gq+3)
       float lr[2][4], dr[2][4];
 #pragma unroll
