@@ -90,6 +90,8 @@ CASES = [
     # long enough that each key block's tokens are split into 2 / 4 pieces summed in a second pass
     ("pieces2_g8", workloads.TINY.with_(S_q=5000, S_k=5000, topk=4), "arbitrary"),
     ("pieces4_g4", workloads.TINY.with_(H_q=4, H_kv=1, S_q=12300, S_k=12300, topk=3), "select"),
+    # queries offset into the keys with 2 pieces: the first piece is empty for every block past it
+    ("pieces2_offset_sq4200_sk6000", workloads.TINY.with_(H_q=4, H_kv=1, S_q=4200, S_k=6000, topk=5), "arbitrary"),
     # group sizes that are not powers of two (heads >= G of the MFMA columns stay empty)
     ("g3_ragged_sq777_sk900", workloads.TINY.with_(H_q=9, H_kv=3, S_q=777, S_k=900, topk=5, n_init=2, n_local=3),
      "select"),
