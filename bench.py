@@ -237,6 +237,23 @@ def time_decode_paged(torch, tb, workloads, dev, reps=50):
     res["contiguous_step_ms"] = timed(lambda: plan.run(qc, kc, vc), reps)
     res = {k: round(v, 4) for k, v in res.items()}
     res["paged_step_graph_ms"] = round(graph_ms, 4) if isinstance(graph_ms, float) else graph_ms
+    # HBM roofline of the step: the K and V rows of the attended blocks (the
+    # last block holds only the sequence's tail), the compressed keys selection
+    # scores, and Q, O
+    per = wl.topk + wl.n_init + wl.n_local
+    kv = 0
+    for L in [n + 1 for n in lens]:
+        nb = (L + 63) // 64
+        blocks = min(nb, per)
+        kv += ((blocks - 1) * 64 + (L - 64 * (nb - 1))) * H_kv * D * 2 * 2
+    kcmp = sum((n + 1) // 64 for n in lens) * H_kv * D * 2
+    qo = 2 * B * H_q * D * 2
+    res["hbm_roofline"] = {"attn_bytes": kv + qo, "attn_tbs": round((kv + qo) / (res["attn_ms"] * 1e-3) / 1e12, 3),
+                           "attn_frac": round((kv + qo) / (res["attn_ms"] * 1e-3) / 8e12, 4),
+                           "step_bytes": kv + kcmp + qo,
+                           "step_ideal_ms": round((kv + kcmp + qo) / 8e12 * 1e3, 4),
+                           "step_frac": round((kv + kcmp + qo) / (res["paged_step_ms"] * 1e-3) / 8e12, 4),
+                           "peak_tbs": 8.0}
     return res
 
 
@@ -500,6 +517,13 @@ def main():
         "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms_step, 3),
         "sparse_attn_bwd_ms": None if bwd_ms is None else round(bwd_ms, 4),
         "sparse_attn_bwd_tflops": None if bwd_ms is None else round(2 * sparse_flops / (bwd_ms * 1e-3) / 1e12, 2),
+        "stage_mfma_frac": {
+            "select": round(select_flops / (stages["select"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "sparse_attn": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "sparse_attn_bwd": None if bwd_ms is None else
+            round(2 * sparse_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "dense_attn": None if dense_ms is None else
+            round(dense_flops / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
         "decode_b16_32k_paged": decode,
         "select_strided_lse": strided,
         "compressed_branch": compressed,

@@ -129,7 +129,12 @@ struct BlockSrc {
     if constexpr (!PAGED) {
       return static_cast<size_t>(j) * kBS * kD;
     } else {
-      const int page = min(max(table[static_cast<size_t>(b) * nb + j], 0), num_pages - 1);
+      // read through the constant address space: the index is wave-uniform,
+      // so this is a scalar load (counted by lgkmcnt).  A vector load here
+      // would be counted by vmcnt, and waiting for it would also wait for the
+      // direct-to-LDS loads just issued for the previous block.
+      typedef __attribute__((address_space(4))) const int const_int;
+      const int page = min(max(((const_int*)(table))[static_cast<size_t>(b) * nb + j], 0), num_pages - 1);
       return (static_cast<size_t>(page) * H_kv + g) * kBS * kD;
     }
   }
