@@ -145,7 +145,8 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(
   // Two halves of 32 keys (key tiles 2*s2 and 2*s2+1): S^T and dP^T of the
   // half, dS, then k-step s2 of dQ^T += K^T dS^T, which takes exactly those
   // two tiles (slots 0..3 and 4..7).
-  auto item = [&](const unsigned char* stg, int j) {
+  auto item = [&](const unsigned char* stg_ptr, int j) {
+    const uint32_t stg = lds_addr(stg_ptr);           // the stage's LDS address, converted once
     const bool need_mask = j * kBS + kBS - 1 > lim;   // wave-uniform
     const int first = lim - j * kBS - 4 * gq;         // keys 16*kt + e > first are masked
 #pragma unroll
@@ -157,8 +158,8 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
           const int kt = 2 * s2 + x;
-          kf[x] = as_bf16x8(lds_load16(stg + ln.k(ks) + kt * 16 * kRowBytes));
-          vf[x] = as_bf16x8(lds_load16(stg + kTileBytes + ln.k(ks) + kt * 16 * kRowBytes));
+          kf[x] = as_bf16x8(lds_load16_at(stg + ln.k(ks) + kt * 16 * kRowBytes));
+          vf[x] = as_bf16x8(lds_load16_at(stg + kTileBytes + ln.k(ks) + kt * 16 * kRowBytes));
         }
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
@@ -186,8 +187,9 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(
         bf16x8 kt_f[4];
 #pragma unroll
         for (int dd = 0; dd < 4; ++dd) {
-          const unsigned char* p = stg + ln.v(d0 + dd) + s2 * 32 * kRowBytes;
-          kt_f[dd] = __builtin_shufflevector(lds_read_tr(p), lds_read_tr(p + 16 * kRowBytes), 0, 1, 2, 3, 4, 5, 6, 7);
+          const uint32_t p = stg + ln.v(d0 + dd) + s2 * 32 * kRowBytes;
+          kt_f[dd] = __builtin_shufflevector(lds_read_tr_at(p), lds_read_tr_at(p + 16 * kRowBytes), 0, 1, 2, 3, 4, 5,
+                                             6, 7);
         }
 #pragma unroll
         for (int dd = 0; dd < 4; ++dd) dqa[d0 + dd] = mfma_16x16x32(kt_f[dd], dsf, dqa[d0 + dd]);

@@ -25,12 +25,18 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
-// 16 bytes from LDS through an LDS pointer.  A generic load of an address the
-// compiler cannot trace back to shared memory (a stage pointer picked at run
-// time) becomes a flat load, which also counts against vmcnt: every wait for
-// it would then wait for the ring's direct-to-LDS loads in flight as well.
+// Reads at a 32-bit LDS address.  Where a stage pointer is picked at run time
+// the compiler cannot trace it back to shared memory: plain reads of it become
+// flat loads (which also count against vmcnt, so every wait for them would
+// wait for the ring's direct-to-LDS loads in flight too), and even LDS-typed
+// reads of it rebuild and null-check the 64-bit generic address each time.
+// Converting the stage pointer once (lds_addr) and reading at offsets from it
+// avoids both.
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-__device__ __forceinline__ u32x4 lds_load16(const unsigned char* p) { return *(const lds_u32x4*)(p); }
+__device__ __forceinline__ u32x4 lds_load16_at(uint32_t a) { return *(const lds_u32x4*)(a); }
+__device__ __forceinline__ bf16x4 lds_read_tr_at(uint32_t a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a));
+}
 
 __device__ __forceinline__ floatx16 mfma_32x32x16(bf16x8 a, bf16x8 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
