@@ -182,18 +182,17 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(
         w[c] = pack_bf16x2(d2[0], d2[1]);
       }
       const bf16x8 dsf = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+      // all eight K^T fragments in flight before the dQ products
+      bf16x8 kt_f[8];
 #pragma unroll
-      for (int d0 = 0; d0 < 8; d0 += 4) {
-        bf16x8 kt_f[4];
-#pragma unroll
-        for (int dd = 0; dd < 4; ++dd) {
-          const uint32_t p = stg + ln.v(d0 + dd) + s2 * 32 * kRowBytes;
-          kt_f[dd] = __builtin_shufflevector(lds_read_tr_at(p), lds_read_tr_at(p + 16 * kRowBytes), 0, 1, 2, 3, 4, 5,
-                                             6, 7);
-        }
-#pragma unroll
-        for (int dd = 0; dd < 4; ++dd) dqa[d0 + dd] = mfma_16x16x32(kt_f[dd], dsf, dqa[d0 + dd]);
+      for (int dd = 0; dd < 8; ++dd) {
+        const uint32_t p = stg + ln.v(dd) + s2 * 32 * kRowBytes;
+        kt_f[dd] = __builtin_shufflevector(lds_read_tr_at(p), lds_read_tr_at(p + 16 * kRowBytes), 0, 1, 2, 3, 4, 5, 6,
+                                           7);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) dqa[dd] = mfma_16x16x32(kt_f[dd], dsf, dqa[dd]);
     }
   };
 
