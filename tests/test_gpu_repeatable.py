@@ -1,0 +1,82 @@
+"""Every forward entry point, called twice on the same inputs, returns the same
+bits.  None of these kernels uses floating-point atomics or a data-dependent
+order of accumulation, so any difference between two calls is a race or a
+timing-dependent read (such as a matrix-core result read before its wait
+states have passed); the oracle tolerances would not show it.  Shapes span
+several windows, a ragged tail, split block lists (few windows) and a paged
+cache."""
+import sys
+
+import pytest
+import torch
+
+import trainable_block_sparse_mean_amd as tb
+import workloads
+from tests.test_gpu_decode import paged_cache
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def same(name, a, b):
+    for x, y in zip(a, b):
+        if x is None:
+            continue
+        assert torch.equal(x, y), f"{name}: two calls on the same inputs differ"
+
+
+SHAPES = [
+    ("g16_sq3000", workloads.TINY.with_(H_q=32, H_kv=2, S_q=3000, S_k=3000, topk=12)),
+    ("g8_sq200_sk2500", workloads.TINY.with_(H_q=8, H_kv=1, S_q=200, S_k=2500, topk=9)),  # split lists
+    ("g5_b2_sq777", workloads.TINY.with_(B=2, H_q=10, H_kv=2, S_q=777, S_k=900, topk=5)),
+]
+
+
+@pytest.mark.parametrize("name,w", SHAPES, ids=[s[0] for s in SHAPES])
+def test_prefill_entry_points_repeat_bitwise(name, w):
+    log("repeatable prefill", name)
+    x = workloads.make_inputs(w)
+    q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+
+    def run():
+        kc, vc = tb.compress_k(k), tb.compress_v(v)
+        idx = tb.select_blocks(q, kc, w.S_k, w.topk, w.n_init, w.n_local)
+        sp = tb.sparse_attn_fwd(q, k, v, idx, w.n_init, w.n_local)
+        de = tb.dense_attn_fwd(q, k, v, causal=True)
+        cb = tb.compressed_attn_fwd(q, kc, vc, w.S_k)
+        mx = tb.mixed_attn_fwd(q, k, v, idx, kc, vc, 0.6, 0.4, w.n_init, w.n_local)
+        torch.cuda.synchronize()
+        return [t.clone() for t in (kc, vc, idx, *sp, *de, *cb, *mx) if t is not None]
+
+    first = run()
+    for _ in range(2):
+        same(name, run(), first)
+
+
+def test_paged_decode_entry_points_repeat_bitwise():
+    lens = [3000, 4097, 129, 64 * 20, 700]
+    log("repeatable decode", lens)
+    c = paged_cache(lens, 32, 2, seed=41)
+    nxt = c["lens"]
+    k_cmp = torch.zeros(len(lens), 2, c["max_blocks"], 128, dtype=torch.bfloat16, device=DEV)
+    v_cmp = torch.zeros_like(k_cmp)
+    zero = torch.zeros_like(nxt)
+
+    def run():
+        tb.decode_compress_append(c["kp"], c["table"], zero, nxt, k_cmp, c["max_blocks"])
+        tb.decode_compress_append(c["vp"], c["table"], zero, nxt, v_cmp, c["max_blocks"])
+        idx = tb.decode_select(c["q"], k_cmp, nxt, 16)
+        out, lse = tb.decode_attn(c["q"], c["kp"], c["vp"], c["table"], nxt, idx)
+        mixed, mlse = tb.decode_compressed_attn(c["q"], k_cmp, v_cmp, nxt, o_sparse=out, w_sparse=0.7, w_cmp=0.3)
+        torch.cuda.synchronize()
+        return [t.clone() for t in (k_cmp, v_cmp, idx, out, lse, mixed, mlse)]
+
+    first = run()
+    for _ in range(2):
+        same("paged decode", run(), first)
