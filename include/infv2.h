@@ -173,9 +173,11 @@ int infv2_sparse_attn_fwd(const void* q, const void* k, const void* v,
  * attends the key.  Accumulation is fp32, each output rounded once to bf16;
  * the result does not depend on scheduling (no atomics on gradients).
  * workspace: at least infv2_sparse_bwd_workspace_bytes(...) bytes, 256-byte
- * aligned, contents on entry irrelevant (4 bytes per query row and head, plus
- * one bit per KV head, block and query token).  S_q = 0 needs none and writes
- * zero dk, dv.
+ * aligned, contents on entry irrelevant (4 bytes per query row and head, one
+ * bit per KV head, block and query token, and from 4096 queries the fp32
+ * partial key and value gradients of each token piece: 64 KB per KV head, key
+ * block and piece, 2 pieces from 4096 queries and 16 from 12288, so 1.07 GB
+ * for 2 KV heads at 32768 keys).  S_q = 0 needs none and writes zero dk, dv.
  */
 size_t infv2_sparse_bwd_workspace_bytes(int B, int H_q, int H_kv, int S_q, int S_k,
                                         int D, int block_size, int topk);

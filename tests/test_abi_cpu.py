@@ -174,9 +174,9 @@ def test_backward_validation_codes():
 def test_backward_workspace_sizes():
     lib = tb.load_library()
     # D (4 bytes per row and head, rounded to 256) + one bit per (KV head, block, token)
-    # (rounded to 256) + fp32 dk/dv partials of 4 token pieces per block from 3 * 4096 queries on
+    # (rounded to 256) + fp32 dk/dv partials of 16 token pieces per block from 3 * 4096 queries on
     assert lib.infv2_sparse_bwd_workspace_bytes(1, 32, 2, 32768, 32768, 128, 64, 64) == \
-        32 * 32768 * 4 + 2 * 512 * 1024 * 4 + 2 * 512 * 4 * (2 * 64 * 128 * 4)
+        32 * 32768 * 4 + 2 * 512 * 1024 * 4 + 2 * 512 * 16 * (2 * 64 * 128 * 4)
     assert lib.infv2_sparse_bwd_workspace_bytes(2, 6, 3, 37, 1000, 128, 64, 5) == \
         ((2 * 6 * 37 * 4 + 255) // 256) * 256 + 2 * 3 * 16 * 2 * 4
     assert lib.infv2_sparse_bwd_workspace_bytes(1, 32, 2, 10, 10, 64, 64, 4) == 0   # unsupported D

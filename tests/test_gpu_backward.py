@@ -87,9 +87,9 @@ CASES = [
     ("g1_no_init", workloads.TINY.with_(H_q=2, H_kv=2, S_q=500, S_k=500, topk=3, n_init=0, n_local=1), "select"),
     ("decode_b2", workloads.TINY.with_(B=2, H_q=16, H_kv=1, S_q=1, S_k=3000, topk=8), "select"),
     ("planted_g16_select", workloads.SWITCH_SPARSE.with_(S_q=2048, S_k=2048, switch_len=0), "select"),
-    # long enough that each key block's tokens are split into 2 / 4 pieces summed in a second pass
+    # long enough that each key block's tokens are split into 2 / 16 pieces summed in a second pass
     ("pieces2_g8", workloads.TINY.with_(S_q=5000, S_k=5000, topk=4), "arbitrary"),
-    ("pieces4_g4", workloads.TINY.with_(H_q=4, H_kv=1, S_q=12300, S_k=12300, topk=3), "select"),
+    ("pieces16_g4", workloads.TINY.with_(H_q=4, H_kv=1, S_q=12300, S_k=12300, topk=3), "select"),
     # queries offset into the keys with 2 pieces: the first piece is empty for every block past it
     ("pieces2_offset_sq4200_sk6000", workloads.TINY.with_(H_q=4, H_kv=1, S_q=4200, S_k=6000, topk=5), "arbitrary"),
     # group sizes that are not powers of two (heads >= G of the MFMA columns stay empty)
