@@ -271,9 +271,25 @@ __global__ __launch_bounds__(kBwdKvWaves * 64, 3) void attn_bwd_dkdv_kernel(
   // (KV head, piece, block): the workgroups that run together read the Q and
   // dO rows of one token range of one KV head (a working set the last-level
   // cache can hold), heaviest blocks first
-  const int j = blockIdx.x % s.NB;
-  const int piece = (blockIdx.x / s.NB) % s.nsplit;
-  const size_t bg = blockIdx.x / s.NB / s.nsplit;
+  // With a multiple of 8 pieces, each XCD takes its own pieces (XCD x:
+  // pieces x, x + 8, ...; the hardware deals workgroup n to XCD n % 8), so a
+  // token's Q and dO rows are gathered into one XCD's L2 rather than into
+  // every XCD that runs one of its blocks.  Every piece holds the same number
+  // of (token, block) items, so the XCDs stay balanced.
+  int j, piece;
+  size_t bg;
+  if (s.nsplit % kXcds == 0) {
+    const int xcd = static_cast<int>(blockIdx.x % kXcds);
+    const int kx = static_cast<int>(blockIdx.x / kXcds);
+    const int per = s.nsplit / kXcds;  // pieces per XCD
+    j = kx % s.NB;
+    piece = ((kx / s.NB) % per) * kXcds + xcd;
+    bg = static_cast<size_t>(kx / s.NB / per);
+  } else {
+    j = blockIdx.x % s.NB;
+    piece = (blockIdx.x / s.NB) % s.nsplit;
+    bg = blockIdx.x / s.NB / s.nsplit;
+  }
   const int g = static_cast<int>(bg % s.H_kv);
   const int b = static_cast<int>(bg / s.H_kv);
   const int off = s.S_k - s.S_q;
