@@ -12,8 +12,8 @@
 // Three kernels, in stream order:
 //   1. bitmap: one bit per (KV head, block j, query token r) for the selected
 //      entries of blk_idx that are not forced blocks of r (forced blocks are
-//      recognised arithmetically).  Set with atomicOr: the result does not
-//      depend on the order of the writes.
+//      recognised arithmetically).  Built per 32-token word in LDS, so every
+//      bitmap word is written once and the result does not depend on order.
 //   2. attn_bwd_dq_kernel, window-major like the forward (one workgroup = one
 //      KV head x 16 query tokens, one token per wave, the window's union of
 //      blocks streamed through the LDS ring in pairs).  Per member block:
@@ -49,23 +49,32 @@ __global__ void bwd_bitmap_zero_kernel(uint32_t* __restrict__ bm, size_t n) {
     bm[i] = 0u;
 }
 
-// one thread per (b, g, r, slot)
-__global__ void bwd_bitmap_scatter_kernel(const int32_t* __restrict__ blk_idx, uint32_t* __restrict__ bm,
-                                          AttnShape s) {
-  const size_t n = static_cast<size_t>(s.B) * s.H_kv * s.S_q * s.topk;
+// One workgroup per (b, g, 32-token word): the word's bits of every key
+// block are set in LDS (LDS atomics), then every bitmap word of the column is
+// written once, so the bitmap needs no clearing and no global atomics.
+constexpr int kBitmapThreads = 256;
+__global__ __launch_bounds__(kBitmapThreads) void bwd_bitmap_build_kernel(const int32_t* __restrict__ blk_idx,
+                                                                           uint32_t* __restrict__ bm, AttnShape s) {
+  extern __shared__ uint32_t bits[];  // [NB]
+  const size_t bg = blockIdx.y;
+  const int word = blockIdx.x;
+  const int r0 = word * 32;
   const int W = bitmap_words(s.S_q);
   const int off = s.S_k - s.S_q;
-  for (size_t e = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; e < n;
-       e += static_cast<size_t>(gridDim.x) * blockDim.x) {
-    const size_t row = e / s.topk;              // (b * H_kv + g) * S_q + r
-    const int r = static_cast<int>(row % s.S_q);
-    const size_t bg = row / s.S_q;
-    const int j = blk_idx[e];
+  for (int j = threadIdx.x; j < s.NB; j += kBitmapThreads) bits[j] = 0u;
+  __syncthreads();
+  for (int e = threadIdx.x; e < 32 * s.topk; e += kBitmapThreads) {
+    const int t = e / s.topk;
+    const int r = r0 + t;
+    if (r >= s.S_q) continue;
+    const int j = blk_idx[(bg * s.S_q + r) * s.topk + (e - t * s.topk)];
     const int qb = (off + r) / kBS;
-    // forced blocks of r (initial or window) are recognised by kernel 3 itself
+    // forced blocks of r (initial or window) are recognised by the dK/dV kernel itself
     if (j < s.n_init || j > qb - s.n_local) continue;  // also drops j < 0 and j > qb
-    atomicOr(&bm[(bg * s.NB + j) * W + (r >> 5)], 1u << (r & 31));
+    atomicOr(&bits[j], 1u << t);
   }
+  __syncthreads();
+  for (int j = threadIdx.x; j < s.NB; j += kBitmapThreads) bm[(bg * s.NB + j) * W + word] = bits[j];
 }
 
 // ---------------------------------------------------------------------------
@@ -559,9 +568,11 @@ hipError_t launch_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const ui
                                          ((bmw * sizeof(uint32_t) + 255) & ~static_cast<size_t>(255)));
   AttnShape sk = s;
   sk.nsplit = bwd_pieces(s.S_q);
-  hipLaunchKernelGGL(bwd_bitmap_zero_kernel, dim3(1024), dim3(256), 0, stream, bm, bmw);
   if (s.topk > 0)
-    hipLaunchKernelGGL(bwd_bitmap_scatter_kernel, dim3(1024), dim3(256), 0, stream, blk_idx, bm, s);
+    hipLaunchKernelGGL(bwd_bitmap_build_kernel, dim3(bitmap_words(s.S_q), s.B * s.H_kv), dim3(kBitmapThreads),
+                       static_cast<size_t>(s.NB) * sizeof(uint32_t), stream, blk_idx, bm, s);
+  else
+    hipLaunchKernelGGL(bwd_bitmap_zero_kernel, dim3(1024), dim3(256), 0, stream, bm, bmw);
   const int nwin = (s.S_q + kWin - 1) / kWin;
   const size_t dq_lds = kStages * kStageBytes + 2 * static_cast<size_t>(s.NB) * 4;
   hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(padded_grid(nwin, s.B * s.H_kv)), dim3(kBwdDqWaves * 64), dq_lds,
