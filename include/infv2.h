@@ -36,7 +36,7 @@
  *  - Return value: INFV2_OK or an error code.  All argument checks run before
  *    any HIP call; on an error nothing is launched and outputs are untouched.
  *    Supported on the GPU: D = 128, block_size = 64, 1 <= G <= 16,
- *    0 <= topk <= 256, and at most 4096 key blocks (S_k <= 262144) for the
+ *    0 <= topk <= 256, and at most 4064 key blocks (S_k <= 260096) for the
  *    sparse forward and backward (2048 for the block selection); other
  *    values give INFV2_ERR_UNSUPPORTED.
  *  - The library keeps no state between calls; calls on distinct streams

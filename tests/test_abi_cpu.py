@@ -165,7 +165,7 @@ def test_backward_validation_codes():
     assert _bwd(lib, dk=None) == tb.ERR_INVALID
     assert _bwd(lib, D=64) == tb.ERR_UNSUPPORTED
     assert _bwd(lib, H_q=64, H_kv=2) == tb.ERR_UNSUPPORTED      # G = 32 > 16
-    assert _bwd(lib, S_q=10, S_k=4096 * 64 + 1) == tb.ERR_UNSUPPORTED   # more key blocks than LDS holds
+    assert _bwd(lib, S_q=10, S_k=4064 * 64 + 1) == tb.ERR_UNSUPPORTED   # more key blocks than LDS holds
     assert _bwd(lib, ws=None) == tb.ERR_WORKSPACE
     assert _bwd(lib, wsb=1024) == tb.ERR_WORKSPACE
     assert _bwd(lib, B=0) == tb.OK                             # nothing to write
@@ -185,7 +185,9 @@ def test_backward_workspace_sizes():
 @no_gpu
 def test_sparse_block_limit_is_what_lds_holds():
     lib = tb.load_library()
-    assert _sparse(lib, S_q=10, S_k=4096 * 64 + 1) == tb.ERR_UNSUPPORTED
+    # 4064 blocks fill the 160 KB of LDS (ring, control words, union list); 4065 is the first refused
+    assert _sparse(lib, S_q=10, S_k=4064 * 64 + 1) == tb.ERR_UNSUPPORTED
+    assert _dec_attn(lib, max_blocks=4065) == tb.ERR_UNSUPPORTED
 
 
 

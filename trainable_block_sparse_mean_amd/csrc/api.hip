@@ -15,8 +15,8 @@ constexpr int kAbiVersion = 1;
 constexpr int kMaxTopk = 256;
 constexpr int kMaxSelectBlocks = 2048;  // select keeps each token's scores in LDS
 // the sparse kernels keep a member mask and a list entry (8 bytes) per key
-// block in LDS beside the 128 KB K/V ring: 160 KB holds 4096 of them
-constexpr int kMaxSparseBlocks = 4096;
+// block in LDS beside the 128 KB K/V ring (kernels.hpp)
+using infv2::kMaxSparseBlocks;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

@@ -348,7 +348,7 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
   extern __shared__ __align__(1024) unsigned char smem[];
   uint32_t* bmask = reinterpret_cast<uint32_t*>(smem + kStages * kStageBytes);  // [NB], sparse only
   int* blist = reinterpret_cast<int*>(bmask + s.NB);                           // [NB], sparse only
-  __shared__ int n_list;
+  int* n_list = blist + s.NB;                                                  // list length, sparse only
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -417,7 +417,7 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
   if constexpr (DENSE) {
     nblk = s.causal ? qb_last + 1 : s.NB;
   } else {
-    nblk = build_union_list<NT>(bmask, blist, &n_list, blk_idx, bg, r0, off, qb_last, s, wave, lane);
+    nblk = build_union_list<NT>(bmask, blist, n_list, blk_idx, bg, r0, off, qb_last, s, wave, lane);
     if constexpr (MIX) {
       // The compressed branch first, streamed like a block list (64
       // compressed rows side by side have a key block's layout; the token
@@ -710,13 +710,16 @@ size_t attn_workspace_bytes(const AttnShape& s) {
   return static_cast<size_t>(ns) * s.B * s.H_q * s.S_q * kPartFloats * sizeof(float);
 }
 
+static_assert(kStages * kStageBytes + sparse_list_bytes(kMaxSparseBlocks) <= 163840,
+              "the ring and the largest union list fit in the 160 KB of LDS");
+
 template <bool DENSE, bool MIX = false>
 static hipError_t launch_window(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* blk_idx,
                                 uint16_t* out, float* lse, float* part, const AttnShape& s, hipStream_t stream,
                                 MixArgs mx = MixArgs{nullptr, nullptr, 0.f, 0.f}) {
   const int nwin = (s.S_q + kWin - 1) / kWin;
   const dim3 grid(padded_grid(nwin, s.B * s.H_kv), DENSE ? 1 : s.nsplit);
-  const size_t lds = kStages * kStageBytes + (DENSE ? 0 : 2 * sizeof(int) * static_cast<size_t>(s.NB));
+  const size_t lds = kStages * kStageBytes + (DENSE ? 0 : sparse_list_bytes(s.NB));
   if constexpr (MIX) {
     hipLaunchKernelGGL((attn_window_kernel<false, false, true>), grid, dim3(Cfg<false>::kWaves * 64), lds, stream, q,
                        k, v, blk_idx, out, lse, part, s, mx);

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(
   extern __shared__ __align__(1024) unsigned char smem[];
   uint32_t* bmask = reinterpret_cast<uint32_t*>(smem + kStages * kStageBytes);  // [NB]
   int* blist = reinterpret_cast<int*>(bmask + s.NB);                           // [NB]
-  __shared__ int n_list;
+  int* n_list = blist + s.NB;                                                  // list length
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
   const int lane = threadIdx.x & 63;
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(
   if (valid && gq == 0) dsum[row] = Dh;
   const int lim = min(off + r, s.S_k - 1);
 
-  const int nblk = build_union_list<NT>(bmask, blist, &n_list, blk_idx, bg, r0, off, qb_last, s, wave, lane);
+  const int nblk = build_union_list<NT>(bmask, blist, n_list, blk_idx, bg, r0, off, qb_last, s, wave, lane);
   auto entry_at = [&](int e) -> uint32_t { return e < nblk ? static_cast<uint32_t>(blist[e]) : 0u; };
 
   const SparseLane ln = sparse_lane(hl, gq);
@@ -574,7 +574,7 @@ hipError_t launch_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const ui
   else
     hipLaunchKernelGGL(bwd_bitmap_zero_kernel, dim3(1024), dim3(256), 0, stream, bm, bmw);
   const int nwin = (s.S_q + kWin - 1) / kWin;
-  const size_t dq_lds = kStages * kStageBytes + 2 * static_cast<size_t>(s.NB) * 4;
+  const size_t dq_lds = kStages * kStageBytes + sparse_list_bytes(s.NB);
   hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(padded_grid(nwin, s.B * s.H_kv)), dim3(kBwdDqWaves * 64), dq_lds,
                      stream, q, k, v, out, lse, dout, blk_idx, dq, dsum, s, scale);
   hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3(s.B * s.H_kv * s.NB * sk.nsplit), dim3(kBwdKvWaves * 64), kKvLdsBytes,

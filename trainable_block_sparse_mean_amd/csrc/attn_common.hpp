@@ -198,6 +198,13 @@ __device__ __forceinline__ SparseLane sparse_lane(int hl, int gq) {
   return o;
 }
 
+// LDS bytes of a window's union list beside the ring: the member mask and the
+// list entry of every key block (8 bytes per block) and the list length,
+// rounded to 16 bytes
+__host__ __device__ constexpr size_t sparse_list_bytes(int nb) {
+  return 8 * static_cast<size_t>(nb) + 16;
+}
+
 // ---------------------------------------------------------------------------
 // The union of the blocks a window's tokens attend (sparse kernels)
 // ---------------------------------------------------------------------------

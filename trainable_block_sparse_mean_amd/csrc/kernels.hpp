@@ -9,6 +9,11 @@
 
 namespace infv2 {
 
+// Key blocks the sparse kernels take (S_k <= 260096): the 128 KB K/V ring
+// and the window's union list (8 bytes per block, plus 16) fit in the 160 KB
+// of LDS of a workgroup.
+constexpr int kMaxSparseBlocks = 4064;
+
 struct AttnShape {
   int B, H_q, H_kv, S_q, S_k, G, NB;
   int topk, n_init, n_local;
