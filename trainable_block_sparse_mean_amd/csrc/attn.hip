@@ -488,7 +488,7 @@ __global__ __launch_bounds__(Cfg<DENSE>::kWaves * 64, 1) void attn_window_kernel
     const int split = blockIdx.y;
     const int e_lo = static_cast<int>(static_cast<long long>(split) * nblk / s.nsplit);
     const int e_hi = static_cast<int>(static_cast<long long>(split + 1) * nblk / s.nsplit);
-    stream_pairs<kWaves>(smem, src, e_lo, e_hi, entry_at, wave, lane,
+    stream_pairs<kWaves, false, 8>(smem, src, e_lo, e_hi, entry_at, wave, lane,
                          [&](const unsigned char* const* stg, const int* js, uint32_t cur0, uint32_t cur1) {
 #pragma unroll
       for (int t = 0; t < T; ++t) {

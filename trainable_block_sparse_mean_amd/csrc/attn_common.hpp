@@ -257,33 +257,39 @@ __device__ __forceinline__ int build_union_list(uint32_t* bmask, int* blist, int
 // ring holds the pair being multiplied (2 stages) and the next pair in flight
 // (the other 2); one barrier per pair.  on_pair(stg, js, cur0, cur1) gets the
 // two stages, their blocks and their list entries (cur1 = 0 past the end).
+// Waves 0 .. ISSUERS-1 issue the direct-to-LDS loads (64 KB per pair): with
+// 16 waves each issuing 4, the CU moved 64 KB in about 3200 clocks in a
+// probe, with 4 waves each issuing 8 in about half that per byte; the sparse
+// forward uses 8 issuers (about 2% faster than 16 at 32k and 8k, 2 issuers 8%
+// slower), the others start on their items at once.
 // FRESH_DMA rebuilds the lane's DMA offsets at every issue from a lane id the
 // compiler cannot hoist.  A kernel at its register limit would otherwise
 // spill them and reload each from scratch just before its loads; the vmcnt
 // wait for that reload also waits for the loads issued before it, which
 // serialises the issue.
-template <int WAVES, bool FRESH_DMA = false, typename Src, typename Entry, typename F>
+template <int WAVES, bool FRESH_DMA = false, int ISSUERS = WAVES, typename Src, typename Entry, typename F>
 __device__ __forceinline__ void stream_pairs(unsigned char* smem, const Src& src, int e_lo, int e_hi,
                                              Entry entry_at, int wave, int lane, F&& on_pair) {
   static_assert(kStages == 4, "two pairs of stages");
   const uint32_t ring = lds_addr(smem);
-  const DmaLane<WAVES> dl_kept = dma_lane<WAVES>(wave, lane);
-  auto dl_fresh = [&]() { return FRESH_DMA ? dma_lane<WAVES>(wave, lane_id_opaque()) : dl_kept; };
+  const bool issuer = wave < ISSUERS;
+  const DmaLane<ISSUERS> dl_kept = dma_lane<ISSUERS>(wave % ISSUERS, lane);
+  auto dl_fresh = [&]() { return FRESH_DMA ? dma_lane<ISSUERS>(wave % ISSUERS, lane_id_opaque()) : dl_kept; };
   const int nseg = e_hi - e_lo;
   auto seg_at = [&](int x) -> uint32_t { return x < nseg ? entry_at(e_lo + x) : 0u; };
   const int npair = (nseg + 1) / 2;
   uint32_t cur0 = __builtin_amdgcn_readfirstlane(seg_at(0)), cur1 = __builtin_amdgcn_readfirstlane(seg_at(1));
   uint32_t nxt0 = __builtin_amdgcn_readfirstlane(seg_at(2)), nxt1 = __builtin_amdgcn_readfirstlane(seg_at(3));
-  if (nseg > 0) stage_src(ring, src, cur0 & 0xffffu, dl_fresh(), wave, lane);
-  if (nseg > 1) stage_src(ring + kStageBytes, src, cur1 & 0xffffu, dl_fresh(), wave, lane);
+  if (issuer && nseg > 0) stage_src<ISSUERS>(ring, src, cur0 & 0xffffu, dl_fresh(), wave % ISSUERS, lane);
+  if (issuer && nseg > 1) stage_src<ISSUERS>(ring + kStageBytes, src, cur1 & 0xffffu, dl_fresh(), wave % ISSUERS, lane);
   for (int pi = 0; pi < npair; ++pi) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // pair pi is in LDS; every wave is done with pair pi - 1
     const int half = (pi & 1) * 2;  // first stage of pair pi
-    if (2 * pi + 2 < nseg) {
-      stage_src(ring + (half ^ 2) * kStageBytes, src, nxt0 & 0xffffu, dl_fresh(), wave, lane);
+    if (issuer && 2 * pi + 2 < nseg) {
+      stage_src<ISSUERS>(ring + (half ^ 2) * kStageBytes, src, nxt0 & 0xffffu, dl_fresh(), wave % ISSUERS, lane);
       if (2 * pi + 3 < nseg)
-        stage_src(ring + ((half ^ 2) + 1) * kStageBytes, src, nxt1 & 0xffffu, dl_fresh(), wave, lane);
+        stage_src<ISSUERS>(ring + ((half ^ 2) + 1) * kStageBytes, src, nxt1 & 0xffffu, dl_fresh(), wave % ISSUERS, lane);
     }
     const unsigned char* stg[2] = {smem + half * kStageBytes, smem + (half + 1) * kStageBytes};
     const int js[2] = {static_cast<int>(cur0 & 0xffffu), static_cast<int>(cur1 & 0xffffu)};
