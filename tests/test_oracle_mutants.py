@@ -112,6 +112,24 @@ def _strided_unweighted(q, k_cmp, b, g, i, r, G, scale, block_size, stride):
     return np.exp(z - lse).sum(axis=0)
 
 
+def _strided_select_swaps_init_local(q, k_cmp, S_k, topk, n_init, n_local, block_size, scale, stride, rows=None,
+                                     return_scores=False):
+    return impl.__dict__["_real_strided_select"](q, k_cmp, S_k, topk, n_local, n_init, block_size, scale, stride,
+                                                 rows, return_scores)
+
+
+def _strided_select_row_as_position(q, k_cmp, S_k, topk, n_init, n_local, block_size, scale, stride, rows=None,
+                                    return_scores=False):
+    # takes query row r to sit at key position r (ignores S_k - S_q)
+    return impl.__dict__["_real_strided_select"](q, k_cmp, q.shape[2], topk, n_init, n_local, block_size, scale,
+                                                 stride, rows, return_scores)
+
+
+def _strided_select_exact_lse(q, k_cmp, S_k, topk, n_init, n_local, block_size, scale, stride, rows=None,
+                              return_scores=False):
+    return impl.select_blocks(q, k_cmp, S_k, topk, n_init, n_local, block_size, scale, rows, return_scores)
+
+
 def _cmp_unmasked(q, k_cmp, v_cmp, S_k, block_size, scale, rows=None):
     nb = k_cmp.shape[2]
     return impl.__dict__["_real_cmp"](q, k_cmp, v_cmp, nb * block_size + q.shape[2] - 1, block_size, scale, rows)
@@ -150,6 +168,9 @@ MUTANTS = [
                                                      pins.test_backward_dense_case_matches_torch_autograd_fp64]),
     ("group_scores_strided_lse", _strided_unweighted, [pins.test_strided_lse_is_exact_when_each_group_shares_one_key,
                                                        pins.test_strided_lse_hand_case]),
+    ("select_blocks_strided_lse", _strided_select_swaps_init_local, [pins.test_strided_select_stride_one_is_select_blocks]),
+    ("select_blocks_strided_lse", _strided_select_row_as_position, [pins.test_strided_select_stride_one_is_select_blocks]),
+    ("select_blocks_strided_lse", _strided_select_exact_lse, [pins.test_strided_select_hand_case_flips_a_choice]),
     ("compressed_attn", _cmp_unmasked, [pins.test_compressed_attn_zero_keys_average_the_visible_blocks]),
     ("compressed_attn", _cmp_sees_own_block, [pins.test_compressed_attn_zero_keys_average_the_visible_blocks,
                                               pins.test_compressed_attn_constant_values]),
@@ -168,6 +189,7 @@ def test_pin_catches_mutant(monkeypatch, name, mutant, catchers):
     monkeypatch.setattr(impl, "_real_grad", impl._softmax_attend_grad, raising=False)
     monkeypatch.setattr(impl, "_real_paged", impl.paged_sequence, raising=False)
     monkeypatch.setattr(impl, "_real_cmp", impl.compressed_attn, raising=False)
+    monkeypatch.setattr(impl, "_real_strided_select", impl.select_blocks_strided_lse, raising=False)
     monkeypatch.setattr(impl, name, mutant)
     for pin in catchers:
         with pytest.raises(AssertionError):

@@ -652,6 +652,52 @@ def test_strided_lse_hand_case():
     np.testing.assert_allclose(sig, np.exp(z - lse), rtol=1e-14)
 
 
+
+def test_strided_select_stride_one_is_select_blocks():
+    """Stride 1 samples every block with weight 1, so the selection is the
+    exact one bit for bit: two batches and two KV heads, queries that end
+    before the keys (position i = S_k - S_q + r), distinct n_init and n_local,
+    a row subset, ragged last block."""
+    rng = np.random.default_rng(43)
+    B, H_kv, G, S_q, S_k, D = 2, 2, 3, 70, 64 * 11 + 9, 8
+    q = rng.standard_normal((B, H_kv * G, S_q, D))
+    kc = rng.standard_normal((B, H_kv, (S_k + 63) // 64, D))
+    rows = np.array([0, 3, 31, 40, 69])
+    for topk, n_init, n_local in ((3, 2, 3), (5, 1, 2), (9, 0, 1)):
+        exact = O.select_blocks(q, kc, S_k, topk, n_init, n_local, 64, 0.4, rows=rows)
+        strided = O.select_blocks_strided_lse(q, kc, S_k, topk, n_init, n_local, 64, 0.4, 1, rows=rows)
+        assert exact.dtype == strided.dtype and np.array_equal(exact, strided)
+
+
+def test_strided_select_hand_case_flips_a_choice():
+    """Two heads, one KV group, query at position 383 (nv = 6 visible blocks,
+    candidates 1 .. 4 with n_init = n_local = 1), top-1, scale 1, scores
+    z_1 = (0, 2, 0, 0, 0, 0) and z_2 = (0, 0, 2.2, 0, 0, 0).
+    Exact: L_1 = log(e^2 + 5) = 2.5168, L_2 = log(e^2.2 + 5) = 2.6408, so
+    sigma_1 = e^(2-L_1) + e^(-L_2) = 0.6677 < sigma_2 = e^(-L_1) + e^(2.2-L_2)
+    = 0.7242: block 2.  Stride 2 samples blocks 0, 2, 4 for two blocks each:
+    L_1 = log 6 = 1.7918 (block 1 unseen), L_2 = log(4 + 2 e^2.2) = 3.0933,
+    so sigma_1 = 1.2767 > sigma_2 = 0.5760: block 1."""
+    q = np.zeros((1, 2, 1, 2))
+    q[0, 0, 0] = [1.0, 0.0]
+    q[0, 1, 0] = [0.0, 1.0]
+    kc = np.zeros((1, 1, 6, 2))
+    kc[0, 0, 1, 0] = 2.0
+    kc[0, 0, 2, 1] = 2.2
+    S_k = 384
+    exact = O.select_blocks(q, kc, S_k, 1, 1, 1, 64, 1.0)
+    strided = O.select_blocks_strided_lse(q, kc, S_k, 1, 1, 1, 64, 1.0, 2)
+    assert exact[0, 0, 0, 0] == 2 and strided[0, 0, 0, 0] == 1
+    # the scores behind the two choices, from the closed forms above
+    sig_e = O.group_scores(q, kc, 0, 0, 383, 0, 2, 1.0, 64)
+    sig_s = O.group_scores_strided_lse(q, kc, 0, 0, 383, 0, 2, 1.0, 64, 2)
+    L1, L2 = math.log(math.e ** 2 + 5), math.log(math.e ** 2.2 + 5)
+    np.testing.assert_allclose(sig_e[1:3], [math.exp(2 - L1) + math.exp(-L2), math.exp(-L1) + math.exp(2.2 - L2)],
+                               rtol=1e-13)
+    L1s, L2s = math.log(6.0), math.log(4 + 2 * math.e ** 2.2)
+    np.testing.assert_allclose(sig_s[1:3], [math.exp(2 - L1s) + math.exp(-L2s), math.exp(-L1s) + math.exp(2.2 - L2s)],
+                               rtol=1e-13)
+
 # ------------------------------------------------ compressed-attention branch ----
 
 def test_compressed_attn_zero_keys_average_the_visible_blocks():
