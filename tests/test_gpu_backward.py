@@ -90,6 +90,10 @@ CASES = [
     # long enough that each key block's tokens are split into 2 / 16 pieces summed in a second pass
     ("pieces2_g8", workloads.TINY.with_(S_q=5000, S_k=5000, topk=4), "arbitrary"),
     ("pieces16_g4", workloads.TINY.with_(H_q=4, H_kv=1, S_q=12300, S_k=12300, topk=3), "select"),
+    # 16 pieces mapped onto the XCDs with two batches and two KV heads (the piece
+    # decode separates them) and arbitrary rows (duplicates, -1, forced blocks)
+    ("pieces16_b2_kv2_arbitrary", workloads.TINY.with_(B=2, H_q=8, H_kv=2, S_q=12300, S_k=12300, topk=3),
+     "arbitrary"),
     # queries offset into the keys with 2 pieces: the first piece is empty for every block past it
     ("pieces2_offset_sq4200_sk6000", workloads.TINY.with_(H_q=4, H_kv=1, S_q=4200, S_k=6000, topk=5), "arbitrary"),
     # group sizes that are not powers of two (heads >= G of the MFMA columns stay empty)
@@ -158,3 +162,60 @@ def test_backward_full_size_sampled_rows_and_invariants(wl):
     rel = float((dv.sum(dim=2) - want_v).norm() / want_v.norm())
     log(f"  sum dv vs sum dout: rel {rel:.2e}")
     assert rel <= 1e-2
+
+
+def test_backward_32k_every_key_against_sampled_tokens():
+    """At the benchmark size (16 token pieces per key block, mapped onto the
+    XCDs, G = 16): dO is zero except on 256 sampled tokens, so every other
+    token contributes exactly zero to every gradient (dP = 0 and D = <dO, O>
+    = 0 make dS = 0).  Every element of dK and dV - block 0, which all 32768
+    tokens attend, the window blocks and the selected blocks - is compared
+    with the oracle's sum over the sampled tokens alone; dQ is compared on the
+    sampled rows and must be exactly zero on all others."""
+    wl = workloads.LONG_32K
+    log("backward 32k, sampled dO", wl)
+    x = workloads.make_inputs(wl)
+    q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+    idx = tb.select_blocks(q, tb.compress_k(k), wl.S_k, wl.topk, wl.n_init, wl.n_local)
+    out, lse = tb.sparse_attn_fwd(q, k, v, idx, wl.n_init, wl.n_local)
+    rng = np.random.default_rng(9)
+    edges = np.linspace(0, wl.S_q, 241).astype(np.int64)
+    toks = {int(rng.integers(a, e)) for a, e in zip(edges[:-1], edges[1:])} | {0, 1, 63, 64} | set(range(wl.S_q - 12, wl.S_q))
+    toks = np.array(sorted(toks))
+    keep = torch.zeros(wl.S_q, dtype=torch.bool, device=DEV)
+    keep[torch.as_tensor(toks, device=DEV)] = True
+    dout = bf16_randn(q.shape, 21) * keep.view(1, 1, -1, 1).to(torch.bfloat16)
+    dq, dk, dv = tb.sparse_attn_bwd(q, k, v, out, lse, dout, idx, wl.n_init, wl.n_local)
+    torch.cuda.synchronize()
+    log("  gpu done,", toks.size, "tokens with a gradient")
+    q64, k64, v64, do64 = (np64(t) for t in (q, k, v, dout))
+    idx_np = idx.cpu().numpy()
+    G = wl.H_q // wl.H_kv
+    scale = 1 / math.sqrt(wl.D)
+    ref = [np.zeros((wl.H_q, toks.size, wl.D)), np.zeros(k64.shape[1:]), np.zeros(v64.shape[1:])]
+    mag = [np.zeros_like(r) for r in ref]
+    for g in range(wl.H_kv):
+        hs = slice(g * G, (g + 1) * G)
+        for n, row in enumerate(toks):
+            i = wl.S_k - wl.S_q + int(row)
+            sel = [int(j) for j in idx_np[0, g, row] if j >= 0]
+            t = O.attend_keys(i, O.forced_blocks(i, 64, wl.n_init, wl.n_local) + sel, 64, wl.S_k)
+            p = O._softmax_attend_grad(q64[0, hs, row], k64[0, g, t], v64[0, g, t], do64[0, hs, row], scale,
+                                       magnitudes=True)
+            ref[0][hs, n] = p[0]
+            mag[0][hs, n] = p[3]
+            ref[1][g, t] += p[1]
+            ref[2][g, t] += p[2]
+            mag[1][g, t] += p[4]
+            mag[2][g, t] += p[5]
+    dq64 = np64(dq)[0]
+    rows_close(dq64[:, toks], ref[0], mag[0], "dq (sampled tokens)")
+    others = np.ones(wl.S_q, dtype=bool)
+    others[toks] = False
+    assert not np.abs(dq64[:, others]).any(), "dq of a token with zero dO is not zero"
+    rows_close(np64(dk)[0], ref[1], mag[1], "dk (every key)")
+    rows_close(np64(dv)[0], ref[2], mag[2], "dv (every key)")
+    # keys no sampled token attends get exactly zero
+    never = np.abs(mag[2]).sum(axis=-1) == 0
+    log("  keys reached by the sampled tokens:", int((~never).sum()), "of", never.size)
+    assert not np.abs(np64(dk)[0][never]).any() and not np.abs(np64(dv)[0][never]).any()

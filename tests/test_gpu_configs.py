@@ -29,7 +29,17 @@ def sample_rows(S_q, n, rng):
     return np.array(sorted(base))
 
 
-def run_and_check(w, n_rows=24, batches=None):
+def stratified_rows(S_q, n, rng, tail=16):
+    """One row drawn in each of n equal strata of the query positions, plus
+    the first rows, block edges and the last `tail` rows (the latest window)."""
+    edges = np.linspace(0, S_q, n + 1).astype(np.int64)
+    pick = {int(rng.integers(a, max(a + 1, e))) for a, e in zip(edges[:-1], edges[1:])}
+    pick |= {0, min(63, S_q - 1), min(64, S_q - 1)}
+    pick |= set(range(max(0, S_q - tail), S_q))
+    return np.array(sorted(pick))
+
+
+def run_and_check(w, n_rows=24, batches=None, rows=None):
     log("workload", w)
     x = workloads.make_inputs(w)
     q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
@@ -38,7 +48,7 @@ def run_and_check(w, n_rows=24, batches=None):
     torch.cuda.synchronize()
     log("  gpu done, path", res["path"])
     rng = np.random.default_rng(1)
-    rows = sample_rows(w.S_q, n_rows, rng)
+    rows = sample_rows(w.S_q, n_rows, rng) if rows is None else rows
     bsel = list(range(w.B)) if batches is None else batches
     bt = torch.as_tensor(bsel, device=DEV)
     rt = torch.as_tensor(rows, device=DEV)
@@ -85,7 +95,12 @@ def test_switch_8k_sparse():
 
 
 def test_long_prefill_32k():
-    run_and_check(workloads.LONG_32K, n_rows=24)
+    # 512 strata over the 32768 rows: every stretch of 64 tokens, every candidate
+    # count up to 509, and the last window
+    w = workloads.LONG_32K
+    rows = stratified_rows(w.S_q, 512, np.random.default_rng(11))
+    log("  rows", rows.size)
+    run_and_check(w, rows=rows)
 
 
 def test_decode_b16_32k():
@@ -93,4 +108,13 @@ def test_decode_b16_32k():
 
 
 def test_extreme_prefill_128k():
-    run_and_check(workloads.EXTREME_128K, n_rows=8)
+    # 512 strata: three quarters of the rows have more than 512 candidates
+    # (16 slots per lane in the top-k) and half more than 1024 (32 slots); every
+    # row goes through the 32-block-chunk selection kernel (2048 blocks), and
+    # the late windows' union lists exceed 1024 entries
+    w = workloads.EXTREME_128K
+    rows = stratified_rows(w.S_q, 512, np.random.default_rng(12))
+    cand = (w.S_k - w.S_q + rows) // 64 - w.n_local - w.n_init + 1
+    log("  rows", rows.size, ">512 candidates", int((cand > 512).sum()), ">1024", int((cand > 1024).sum()))
+    assert (cand > 1024).sum() >= 200 and (cand > 512).sum() >= 300
+    run_and_check(w, rows=rows)

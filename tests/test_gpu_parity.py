@@ -189,6 +189,38 @@ def test_sparse_attention_arbitrary_indices_duplicates_and_forced():
     assert_attn_close(out, lse, ro, rl, "arbitrary idx")
 
 
+def test_sparse_forward_and_backward_at_the_block_cap():
+    """4064 key blocks (S_k = 260096), the most the sparse kernels' LDS holds:
+    the union list fills the LDS beside the ring.  Queries at the end of the
+    keys select blocks across the whole range, the highest ones included."""
+    w = workloads.TINY.with_(H_q=16, H_kv=1, S_q=40, S_k=4064 * 64, topk=12)
+    log("sparse at the block cap", w)
+    x = gpu_inputs(w)
+    rng = np.random.default_rng(4)
+    idx = np.full((1, 1, w.S_q, w.topk), -1, dtype=np.int32)
+    for r in range(w.S_q):
+        qb = (w.S_k - w.S_q + r) // 64
+        picks = rng.integers(0, qb + 1, size=w.topk)
+        picks[:3] = [qb - 2, qb - 3, 2000 + r]
+        idx[0, 0, r] = picks
+    gidx = torch.from_numpy(idx).to(DEV)
+    out, lse = tb.sparse_attn_fwd(x["q"], x["k"], x["v"], gidx, w.n_init, w.n_local)
+    dout = torch.randn(x["q"].shape, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).to(DEV)
+    dq, dk, dv = tb.sparse_attn_bwd(x["q"], x["k"], x["v"], out, lse, dout, gidx, w.n_init, w.n_local)
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(128)
+    q64, k64, v64 = np64(x["q"]), np64(x["k"]), np64(x["v"])
+    ro, rl = O.sparse_attn(q64, k64, v64, idx, 64, w.n_init, w.n_local, scale)
+    log("  ", assert_attn_close(out, lse, ro, rl, "block cap"))
+    rq, rk, rv, mq, mk, mv = O.sparse_attn_bwd(q64, k64, v64, np64(dout), idx, 64, w.n_init, w.n_local, scale,
+                                               magnitudes=True)
+    for got, ref, mag, n in ((dq, rq, mq, "dq"), (dk, rk, mk, "dk"), (dv, rv, mv, "dv")):
+        err = np.linalg.norm(np64(got) - ref, axis=-1)
+        lim = 4 * 2.0 ** -8 * np.maximum(np.linalg.norm(mag, axis=-1), 1e-30)
+        assert (err <= lim).all(), f"{n}: worst error {float((err / lim).max()):.2f} of the bound"
+        assert not np.abs(np64(got)[np.abs(mag).sum(-1) == 0]).any(), f"{n}: unattended rows not zero"
+
+
 def test_sparse_equals_dense_when_topk_covers_every_block():
     w = workloads.TINY.with_(H_q=32, H_kv=2, S_q=1536, S_k=1536, topk=24)
     log("sparse == dense", w)
