@@ -221,6 +221,27 @@ int infv2_attn_fwd(const void* q, const void* k, const void* v,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * infv2_attn_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and results as infv2_attn_fwd (blk_idx_out optional), but
+ * the workspace is a fixed array of INFV2_NOALLOC_SCRATCH_BYTES (32 MiB) in
+ * the library's device memory, one per GPU, held until the process ends;
+ * the call allocates nothing.  A shape whose infv2_attn_workspace_bytes
+ * exceeds it returns INFV2_ERR_WORKSPACE before any HIP call (32 MiB covers
+ * the switch up to 32768 tokens with 2 KV heads and top-64).  The stream must
+ * belong to the current device.  Every call on one GPU uses that GPU's one
+ * array: calls that overlap on a GPU (other streams, other threads) race and
+ * give unspecified results; calls in stream order do not.  Nothing in the
+ * array needs to start at zero (a call writes every byte it reads).
+ */
+#define INFV2_NOALLOC_SCRATCH_BYTES (32u << 20)
+int infv2_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                           void* out, float* lse, int32_t* blk_idx_out,
+                           int B, int H_q, int H_kv, int S_q, int S_k, int D,
+                           int block_size, int topk, int n_init, int n_local,
+                           float softmax_scale, int switch_len, void* stream);
+
+/*
  * Decode over a paged, variable-length KV cache (news summary, Performance
  * Evaluation: the method also speeds up decoding).  One new query token per
  * sequence; sequence b holds seqlens[b] keys and its query is the last of

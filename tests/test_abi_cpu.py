@@ -317,3 +317,21 @@ def test_mixed_attn_validation_codes():
     assert mix(topk=300) == tb.ERR_UNSUPPORTED
     assert mix(S_q=1) == tb.ERR_WORKSPACE                        # one query row: split partials needed
     assert mix(B=0) == tb.OK
+
+
+@no_gpu
+def test_noalloc_switch_refuses_shapes_beyond_its_scratch():
+    lib = tb.load_library()
+
+    def call(**kw):
+        a = dict(B=1, H_q=32, H_kv=2, S_q=131072, S_k=131072, topk=128, switch_len=0)
+        a.update(kw)
+        return lib.infv2_attn_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, None, None, a["B"], a["H_q"], a["H_kv"], a["S_q"],
+                                          a["S_k"], 128, 64, a["topk"], 1, 2, 0.0, a["switch_len"], None)
+    # 128k tokens with top-128: 134 MB of block indices, beyond the 32 MiB scratch
+    need = lib.infv2_attn_workspace_bytes(1, 32, 2, 131072, 131072, 128, 64, 128, 0)
+    assert need > 32 << 20
+    assert call() == tb.ERR_WORKSPACE
+    assert call(H_q=31) == tb.ERR_INVALID
+    assert call(B=0) == tb.OK
+    assert call(S_k=4096 * 64) == tb.ERR_UNSUPPORTED          # beyond the 2048 blocks selection keeps

@@ -41,6 +41,7 @@ SIGNATURES = {
     "infv2_dense_attn_fwd": (_c_int, [_vp] * 5 + [_c_int] * 6 + [_c_float, _c_int, _vp, _c_size, _vp]),
     "infv2_attn_workspace_bytes": (_c_size, [_c_int] * 9),
     "infv2_attn_fwd": (_c_int, [_vp] * 6 + [_c_int] * 10 + [_c_float, _c_int, _vp, _c_size, _vp]),
+    "infv2_attn_fwd_noalloc": (_c_int, [_vp] * 6 + [_c_int] * 10 + [_c_float, _c_int, _vp]),
     "infv2_decode_compress_append": (_c_int, [_vp] * 5 + [_c_int] * 7 + [_vp]),
     "infv2_decode_select": (_c_int, [_vp] * 5 + [_c_int] * 9 + [_c_float, _vp]),
     "infv2_decode_attn_workspace_bytes": (_c_size, [_c_int] * 7),
@@ -381,6 +382,20 @@ def attn_fwd(q, k, v, block_size: int = 64, topk: int = 64, n_init: int = 1, n_l
                     q.device, True, return_idx)
     out, lse = plan.run(q, k, v)
     return dict(out=out, lse=lse, path="dense" if plan.dense else "sparse", blk_idx=plan.idx)
+
+
+def attn_fwd_noalloc(q, k, v, out, lse, blk_idx=None, block_size: int = 64, topk: int = 64, n_init: int = 1,
+                     n_local: int = 2, switch_len: int = 0, softmax_scale=None) -> None:
+    """infv2_attn_fwd_noalloc: the switch into caller-given out (bf16, shaped
+    like q), lse (fp32 [B,H_q,S_q] or None) and optional blk_idx, with the
+    library's fixed per-GPU scratch as its workspace (nothing is allocated)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, n, torch.bfloat16, 4)
+    B, H_q, S_q, D = q.shape
+    H_kv, S_k = k.shape[1], k.shape[2]
+    _call("infv2_attn_fwd_noalloc", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(blk_idx),
+          B, H_q, H_kv, S_q, S_k, D, block_size, topk, n_init, n_local, _scale(softmax_scale), switch_len,
+          _stream())
 
 
 def default_scale(D: int) -> float:

@@ -3,6 +3,8 @@
 // before the first HIP call, so an invalid call launches nothing.
 #include <math.h>
 
+#include <mutex>
+
 #include "infv2.h"
 #include "common.hpp"
 #include "kernels.hpp"
@@ -301,6 +303,70 @@ int infv2_attn_fwd(const void* q, const void* k, const void* v, void* out, float
   }
   return infv2_sparse_attn_fwd(q, k, v, idx, out, lse, B, H_q, H_kv, S_q, S_k, D, block_size, topk, n_init,
                                n_local, softmax_scale, rest, rest_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of infv2_attn_fwd_noalloc: the switch's workspace (compressed keys,
+// block indices, split-KV partials), carved as in infv2_attn_fwd.  A file-scope
+// device array, so the library never allocates it; each GPU the library runs on
+// holds its own copy until the process ends.  Host code never takes the
+// array's name as an address: the device address of each GPU's copy comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kNoAllocScratchBytes = INFV2_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of the current device's scratch (looked up on its first use)
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return INFV2_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return INFV2_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return INFV2_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return INFV2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int infv2_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                           int32_t* blk_idx_out, int B, int H_q, int H_kv, int S_q, int S_k, int D, int block_size,
+                           int topk, int n_init, int n_local, float softmax_scale, int switch_len, void* stream) {
+  // the argument checks of infv2_attn_fwd, then the size check, before any HIP call
+  int st = check_shape(B, H_q, H_kv, S_q, S_k, D);
+  if (st != INFV2_OK) return st;
+  if (S_k > switch_len) {
+    st = check_sparse_params(block_size, topk, n_init, n_local);
+    if (st != INFV2_OK) return st;
+    if (num_blocks(S_k, block_size) > kMaxSelectBlocks) return INFV2_ERR_UNSUPPORTED;
+  }
+  if (B == 0 || S_q == 0) return INFV2_OK;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(out)) return INFV2_ERR_INVALID;
+  if (lse && !aligned(lse, 16)) return INFV2_ERR_INVALID;
+  if (blk_idx_out && !aligned(blk_idx_out, 16)) return INFV2_ERR_INVALID;
+  const size_t need = infv2_attn_workspace_bytes(B, H_q, H_kv, S_q, S_k, D, block_size, topk, switch_len);
+  if (need > kNoAllocScratchBytes) return INFV2_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_on_current_device(&ws);
+    if (st != INFV2_OK) return st;
+  }
+  // every byte of the scratch a call reads was written earlier in the same
+  // call (compressed keys, selected blocks, split partials): nothing is cleared
+  return infv2_attn_fwd(q, k, v, out, lse, blk_idx_out, B, H_q, H_kv, S_q, S_k, D, block_size, topk, n_init,
+                        n_local, softmax_scale, switch_len, ws, need > 0 ? kNoAllocScratchBytes : 0, stream);
 }
 
 int infv2_decode_compress_append(const void* k_pages, const int32_t* block_table, const int32_t* old_lens,
