@@ -257,6 +257,127 @@ def time_decode_paged(torch, tb, workloads, dev, reps=50):
     return res
 
 
+def event_ms(torch, f, n, warm=1, warm_s=0.1):
+    """Average ms of n back-to-back calls of f (HIP events on the current
+    stream), after at least `warm` calls and warm_s seconds of calls: the
+    clocks drop while the host runs the oracle, and short kernels timed right
+    after such a pause run up to about 1.6x slower."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < warm or time.perf_counter() - t0 < warm_s:
+        f()
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(n):
+        f()
+    c1.record()
+    torch.cuda.synchronize()
+    return c0.elapsed_time(c1) / n
+
+
+def config_entry(w, torch, tb, workloads, dev, with_cpu, steps=10):
+    """One prefill workload of the five: the whole step through the switch
+    entry point (dense or compress -> select -> sparse), its stages, this
+    build's dense attention at the same shape, and the oracle on a bounded
+    sample of rows."""
+    x = workloads.make_inputs(w)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    sparse_f, dense_f, select_f, _ = flop_counts(w)
+    plan = tb.AttnPlan(w.B, w.H_q, w.H_kv, w.S_q, w.S_k, w.D, w.block_size, w.topk, w.n_init, w.n_local,
+                       w.switch_len, None, dev)
+    step_ms = event_ms(torch, lambda: plan.run(q, k, v), steps, warm=2)
+    dense_ms = event_ms(torch, lambda: tb.dense_attn_fwd(q, k, v, causal=True), 3)
+    e = {"path": "dense" if plan.dense else "sparse", "B": w.B, "S_q": w.S_q, "S_k": w.S_k, "H_q": w.H_q,
+         "H_kv": w.H_kv, "topk": w.topk, "values": w.values, "step_ms": round(step_ms, 4),
+         "dense_attn_ms": round(dense_ms, 4),
+         "dense_attn_tflops": round(dense_f / (dense_ms * 1e-3) / 1e12, 2),
+         "speedup_vs_dense": round(dense_ms / step_ms, 3)}
+    if plan.dense:
+        e["step_tflops"] = round(dense_f / (step_ms * 1e-3) / 1e12, 2)
+        e["mfma_peak_frac"] = round(e["step_tflops"] / PEAK_BF16_TFLOPS, 4)
+    else:
+        kc = tb.compress_k(k)
+        idx = tb.select_blocks(q, kc, w.S_k, w.topk, w.n_init, w.n_local)
+        attn_ms = event_ms(torch, lambda: tb.sparse_attn_fwd(q, k, v, idx, w.n_init, w.n_local), steps)
+        sel_ms = event_ms(torch, lambda: tb.select_blocks(q, kc, w.S_k, w.topk, w.n_init, w.n_local), steps)
+        e.update({"sparse_attn_ms": round(attn_ms, 4), "select_ms": round(sel_ms, 4),
+                  "compress_ms": round(event_ms(torch, lambda: tb.compress_k(k), steps), 4),
+                  "step_tflops": round(sparse_f / (step_ms * 1e-3) / 1e12, 2),
+                  "sparse_attn_tflops": round(sparse_f / (attn_ms * 1e-3) / 1e12, 2),
+                  "mfma_peak_frac_attn": round(sparse_f / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                  "mfma_peak_frac_select": round(select_f / (sel_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                  "algorithmic_flops": {"sparse_attn": sparse_f, "dense_attn": dense_f, "select": select_f}})
+        del kc, idx
+    if with_cpu:
+        cb = cpu_baseline(w, x, target_s=4.0 if w.S_q <= 32768 else 6.0)
+        e["cpu_baseline"] = {kk: cb[kk] for kk in ("unit", "cores", "kind", "sample")}
+        e["cpu_baseline"]["value"] = round(cb["value"], 6)
+        e["cpu_baseline"]["step_s_estimate"] = round(cb["step_s_estimate"], 3)
+    del q, k, v, x, plan
+    torch.cuda.empty_cache()
+    return e
+
+
+def decode_contiguous_entry(torch, tb, workloads, dev, with_cpu, reps=20):
+    """The decode workload as stated (16 sequences, one query each, a
+    contiguous 32768-key cache per sequence): a step is selection + sparse
+    attention over compressed keys computed once beforehand (the compression
+    of the whole cache is reported apart); against HBM, the step moves the
+    attended K/V rows, the compressed keys and Q, O."""
+    import numpy as np
+    w = workloads.DECODE_32K
+    x = workloads.make_inputs(w)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    kc = tb.compress_k(k)
+    idx = tb.select_blocks(q, kc, w.S_k, w.topk, w.n_init, w.n_local)
+
+    def step():
+        i2 = tb.select_blocks(q, kc, w.S_k, w.topk, w.n_init, w.n_local)
+        tb.sparse_attn_fwd(q, k, v, i2, w.n_init, w.n_local)
+
+    step_ms = event_ms(torch, step, reps, warm=2)
+    attn_ms = event_ms(torch, lambda: tb.sparse_attn_fwd(q, k, v, idx, w.n_init, w.n_local), reps)
+    sel_ms = event_ms(torch, lambda: tb.select_blocks(q, kc, w.S_k, w.topk, w.n_init, w.n_local), reps)
+    comp_ms = event_ms(torch, lambda: tb.compress_k(k), 5)
+    dense_ms = event_ms(torch, lambda: tb.dense_attn_fwd(q, k, v, causal=True), 5)
+    per = w.topk + w.n_init + w.n_local
+    kv = w.B * w.H_kv * min(per, w.S_k // 64) * 64 * w.D * 2 * 2
+    kcb = w.B * w.H_kv * (w.S_k // 64) * w.D * 2
+    qo = 2 * w.B * w.H_q * w.D * 2
+    dense_bytes = w.B * w.H_kv * w.S_k * w.D * 2 * 2 + qo
+    e = {"path": "sparse", "B": w.B, "S_q": w.S_q, "S_k": w.S_k, "H_q": w.H_q, "H_kv": w.H_kv, "topk": w.topk,
+         "step_ms": round(step_ms, 4), "select_ms": round(sel_ms, 4), "sparse_attn_ms": round(attn_ms, 4),
+         "compress_whole_cache_ms": round(comp_ms, 4), "dense_attn_ms": round(dense_ms, 4),
+         "speedup_vs_dense": round(dense_ms / step_ms, 3),
+         "hbm_roofline": {"step_bytes": kv + kcb + qo, "step_tbs": round((kv + kcb + qo) / (step_ms * 1e-3) / 1e12, 3),
+                          "step_frac": round((kv + kcb + qo) / (step_ms * 1e-3) / 8e12, 4),
+                          "attn_bytes": kv + qo, "attn_frac": round((kv + qo) / (attn_ms * 1e-3) / 8e12, 4),
+                          "dense_bytes": dense_bytes,
+                          "dense_frac": round(dense_bytes / (dense_ms * 1e-3) / 8e12, 4), "peak_tbs": 8.0}}
+    if with_cpu:
+        import oracle.infv2_oracle as O
+        t0 = time.perf_counter()
+        bs = [0, 5, 10, 15]
+        k64, v64 = k[bs].double().cpu().numpy(), v[bs].double().cpu().numpy()
+        q64 = q[bs].double().cpu().numpy()
+        _, kco = O.compress_k(k64, 64)
+        t1 = time.perf_counter()
+        ix = O.select_blocks(q64, kco, w.S_k, w.topk, w.n_init, w.n_local, 64, 1 / math.sqrt(w.D))
+        O.sparse_attn(q64, k64, v64, ix, 64, w.n_init, w.n_local, 1 / math.sqrt(w.D))
+        t2 = time.perf_counter()
+        e["cpu_baseline"] = {"kind": "oracle", "unit": "ms per step", "value": round((t2 - t1) / len(bs) * w.B * 1e3, 3),
+                             "sample": (f"select + attend of {len(bs)} of the 16 sequences ({t2 - t1:.2f} s) scaled "
+                                        f"to 16; their key compression took {t1 - t0:.2f} s apart"),
+                             "cores": None}
+    del q, k, v, x, kc, idx
+    torch.cuda.empty_cache()
+    return e
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,6 +394,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip timing the paged decode step")
     ap.add_argument("--no-compressed", action="store_true",
                     help="skip timing the compressed-attention branch and the mixed output")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other four workloads (tiny 2k, 4k/8k switch, decode, 128k)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -472,6 +595,18 @@ def main():
                       "branch_flops": cmp_flops}
         del kc, vc, idx, o_sp, buf
 
+    # ---- the other workloads of the five, each measured the same way ---------------
+    configs = None
+    if not args.no_configs:
+        del plan
+        torch.cuda.empty_cache()
+        configs = {}
+        for w in (workloads.TINY, workloads.SWITCH_DENSE, workloads.SWITCH_SPARSE, workloads.EXTREME_128K):
+            configs[w.name] = config_entry(w, torch, tb, workloads, dev, not args.no_cpu_baseline)
+            print(f"[bench] {w.name}: {configs[w.name]['step_ms']} ms", file=sys.stderr, flush=True)
+        configs[workloads.DECODE_32K.name] = decode_contiguous_entry(torch, tb, workloads, dev,
+                                                                     not args.no_cpu_baseline)
+
     attn_tflops = sparse_flops / (stages["sparse_attn"] * 1e-3) / 1e12
     value = sparse_flops / (ms_step * 1e-3) / 1e12
     traffic = stored_traffic()
@@ -527,6 +662,7 @@ def main():
         "decode_b16_32k_paged": decode,
         "select_strided_lse": strided,
         "compressed_branch": compressed,
+        "configs": configs,
         "algorithmic_flops": {"sparse_attn": sparse_flops, "dense_attn": dense_flops, "select": select_flops,
                               "sparse_attn_bwd": 2 * sparse_flops},
         "wall_ms_per_step": round(wall_ms, 4),
