@@ -390,6 +390,10 @@ def main():
                     help="only launch the sparse attention kernel this many times (for counter runs)")
     ap.add_argument("--profile-bwd", type=int, default=0,
                     help="only run the sparse attention backward this many times (for profiler runs)")
+    ap.add_argument("--profile-kernels", type=int, default=0,
+                    help="for counter runs: launch each kernel family of the path this many times at the "
+                         "workload's shape (compress, select, sparse attention, dense attention, backward) and "
+                         "the paged decode step (attention, combine, selection, append), then exit")
     ap.add_argument("--no-bwd", action="store_true", help="skip timing the sparse attention backward")
     ap.add_argument("--no-decode", action="store_true", help="skip timing the paged decode step")
     ap.add_argument("--no-compressed", action="store_true",
@@ -438,6 +442,28 @@ def main():
             tb.sparse_attn_bwd(q, k, v, o, lse, dout, idx, wl.n_init, wl.n_local)
         torch.cuda.synchronize()
         print(json.dumps({"profile_bwd_runs": args.profile_bwd}))
+        return
+
+    if args.profile_kernels:
+        n = args.profile_kernels
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)   # calibration copy of known size
+        torch.empty_like(a).copy_(a)
+        for _ in range(n):
+            kc = tb.compress_k(k)
+        for _ in range(n):
+            idx = tb.select_blocks(q, kc, wl.S_k, wl.topk, wl.n_init, wl.n_local)
+        for _ in range(n):
+            o, lse = tb.sparse_attn_fwd(q, k, v, idx, wl.n_init, wl.n_local)
+        for _ in range(n):
+            tb.dense_attn_fwd(q, k, v, causal=True)
+        dout = seeded_dout(q, torch)
+        for _ in range(n):
+            tb.sparse_attn_bwd(q, k, v, o, lse, dout, idx, wl.n_init, wl.n_local)
+        torch.cuda.synchronize()
+        del o, lse, dout, idx, kc
+        time_decode_paged(torch, tb, workloads, dev, reps=n)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_kernels_launches": n, "copy_bytes": 2 * a.numel()}))
         return
 
     plan = tb.AttnPlan(wl.B, wl.H_q, wl.H_kv, wl.S_q, wl.S_k, wl.D, wl.block_size, wl.topk, wl.n_init,
