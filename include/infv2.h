@@ -37,8 +37,9 @@
  *    any HIP call; on an error nothing is launched and outputs are untouched.
  *    Supported on the GPU: D = 128, block_size = 64, 1 <= G <= 16,
  *    0 <= topk <= 256, and at most 4064 key blocks (S_k <= 260096) for the
- *    sparse forward and backward (2048 for the block selection); other
- *    values give INFV2_ERR_UNSUPPORTED.
+ *    sparse forward and backward (2048 for the block selection), at most
+ *    65535 (batch, kv head) pairs and B * H_kv * S_k <= 2^25 (the launch
+ *    grids' limits); other values give INFV2_ERR_UNSUPPORTED.
  *  - The library keeps no state between calls; calls on distinct streams
  *    with distinct outputs and workspaces are independent.
  */
@@ -213,6 +214,13 @@ int infv2_dense_attn_fwd(const void* q, const void* k, const void* v,
  */
 size_t infv2_attn_workspace_bytes(int B, int H_q, int H_kv, int S_q, int S_k,
                                   int D, int block_size, int topk, int switch_len);
+/*
+ * The path infv2_attn_fwd (and infv2_attn_fwd_noalloc) takes for S_k keys
+ * under switch_len: INFV2_PATH_DENSE or INFV2_PATH_SPARSE.  Pure host
+ * function, no HIP call; the one place the switch rule is written.
+ */
+enum infv2_path { INFV2_PATH_SPARSE = 0, INFV2_PATH_DENSE = 1 };
+int infv2_attn_path(int S_k, int switch_len);
 int infv2_attn_fwd(const void* q, const void* k, const void* v,
                    void* out, float* lse, int32_t* blk_idx_out,
                    int B, int H_q, int H_kv, int S_q, int S_k, int D,

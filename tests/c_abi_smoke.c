@@ -16,6 +16,7 @@ int main(void) {
   if (infv2_compressed_attn_fwd(fake, fake, fake, NULL, fake, NULL, 1, 32, 2, 10, 9, 128, 64, 0.0f, 0.0f, 1.0f,
                                 NULL) != INFV2_ERR_INVALID) /* S_q > S_k */
     return 6;
+  if (infv2_attn_path(4096, 4096) != INFV2_PATH_DENSE || infv2_attn_path(4097, 4096) != INFV2_PATH_SPARSE) return 7;
   printf("c abi ok\n");
   return 0;
 }

@@ -34,7 +34,8 @@ def test_header_declares_expected_entry_points():
     for n in ["infv2_compress_k", "infv2_select_blocks", "infv2_sparse_attn_fwd", "infv2_dense_attn_fwd",
               "infv2_attn_fwd", "infv2_sparse_attn_bwd", "infv2_status_string", "infv2_decode_compress_append",
               "infv2_decode_select", "infv2_decode_attn", "infv2_compress_v", "infv2_compressed_attn_fwd",
-              "infv2_decode_compressed_attn", "infv2_mixed_attn_fwd"]:
+              "infv2_decode_compressed_attn", "infv2_mixed_attn_fwd", "infv2_attn_path",
+              "infv2_attn_fwd_noalloc"]:
         assert n in names
 
 
@@ -335,3 +336,30 @@ def test_noalloc_switch_refuses_shapes_beyond_its_scratch():
     assert call(H_q=31) == tb.ERR_INVALID
     assert call(B=0) == tb.OK
     assert call(S_k=4096 * 64) == tb.ERR_UNSUPPORTED          # beyond the 2048 blocks selection keeps
+
+
+@no_gpu
+def test_launch_grid_limits_are_refused_before_any_launch():
+    lib = tb.load_library()
+    # (batch, kv head) pairs go in gridDim.y: 65535 at most
+    assert _bwd(lib, B=65536, H_q=1, H_kv=1, S_q=1, S_k=1) == tb.ERR_UNSUPPORTED
+    assert _bwd(lib, B=32768, H_q=2, H_kv=2, S_q=1, S_k=1) == tb.ERR_UNSUPPORTED
+    assert _sparse(lib, B=65536, H_q=1, H_kv=1, S_q=1, S_k=1) == tb.ERR_UNSUPPORTED
+    assert lib.infv2_compress_k(FAKE, FAKE, 65536, 1, 64, 128, 64, None) == tb.ERR_UNSUPPORTED
+    assert _dec_attn(lib, B=65536, H_q=1, H_kv=1, max_blocks=1) == tb.ERR_UNSUPPORTED
+    # work-items: B * H_kv * S_k <= 2^25
+    assert _bwd(lib, B=512, H_q=2, H_kv=2, S_q=1, S_k=32769) == tb.ERR_UNSUPPORTED
+    assert _sparse(lib, B=1024, H_q=1, H_kv=1, S_q=1, S_k=32769) == tb.ERR_UNSUPPORTED
+    assert lib.infv2_compress_k(FAKE, FAKE, 512, 2, 32769, 128, 64, None) == tb.ERR_UNSUPPORTED
+    # at the limit the shape is accepted (and then stopped by the missing workspace)
+    assert _bwd(lib, B=512, H_q=2, H_kv=2, S_q=1, S_k=32768, ws=None) == tb.ERR_WORKSPACE
+    assert _bwd(lib, B=65535, H_q=1, H_kv=1, S_q=1, S_k=1, ws=None) == tb.ERR_WORKSPACE
+
+
+def test_switch_path_rule_lives_in_the_library():
+    lib = tb.load_library()
+    assert lib.infv2_attn_path(4096, 4096) == tb.PATH_DENSE
+    assert lib.infv2_attn_path(4097, 4096) == tb.PATH_SPARSE
+    assert lib.infv2_attn_path(0, 0) == tb.PATH_DENSE
+    assert lib.infv2_attn_path(1, 0) == tb.PATH_SPARSE
+    assert lib.infv2_attn_path(8192, -1) == tb.PATH_SPARSE

@@ -23,6 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libinfv2.so")
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+PATH_SPARSE, PATH_DENSE = 0, 1
 
 _c_int, _c_size, _c_float, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
 
@@ -40,6 +41,7 @@ SIGNATURES = {
     "infv2_dense_workspace_bytes": (_c_size, [_c_int] * 6),
     "infv2_dense_attn_fwd": (_c_int, [_vp] * 5 + [_c_int] * 6 + [_c_float, _c_int, _vp, _c_size, _vp]),
     "infv2_attn_workspace_bytes": (_c_size, [_c_int] * 9),
+    "infv2_attn_path": (_c_int, [_c_int, _c_int]),
     "infv2_attn_fwd": (_c_int, [_vp] * 6 + [_c_int] * 10 + [_c_float, _c_int, _vp, _c_size, _vp]),
     "infv2_attn_fwd_noalloc": (_c_int, [_vp] * 6 + [_c_int] * 10 + [_c_float, _c_int, _vp]),
     "infv2_decode_compress_append": (_c_int, [_vp] * 5 + [_c_int] * 7 + [_vp]),
@@ -353,7 +355,7 @@ class AttnPlan:
         self.args = (B, H_q, H_kv, S_q, S_k, D, block_size, topk, n_init, n_local)
         self.switch_len = switch_len
         self.scale = _scale(softmax_scale)
-        self.dense = S_k <= switch_len
+        self.dense = load_library().infv2_attn_path(S_k, switch_len) == PATH_DENSE
         nbytes = load_library().infv2_attn_workspace_bytes(B, H_q, H_kv, S_q, S_k, D, block_size, topk,
                                                            switch_len)
         self.ws = _workspace(nbytes, device)

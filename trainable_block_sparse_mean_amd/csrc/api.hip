@@ -20,6 +20,16 @@ constexpr int kMaxSelectBlocks = 2048;  // select keeps each token's scores in L
 // block in LDS beside the 128 KB K/V ring (kernels.hpp)
 using infv2::kMaxSparseBlocks;
 
+// Launch-grid limits: the kernels put the (batch, kv head) pairs in gridDim.y
+// (at most 65535), and a grid spans about 64 work-items per key and kv head,
+// which must stay below 2^32.
+constexpr long long kMaxHeadRows = 65535;
+constexpr long long kMaxHeadKeys = 1LL << 25;
+
+bool grid_fits(long long B, long long H_kv, long long S_k) {
+  return B * H_kv <= kMaxHeadRows && B * H_kv * S_k <= kMaxHeadKeys;
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -33,6 +43,7 @@ int check_shape(int B, int H_q, int H_kv, int S_q, int S_k, int D) {
   if (H_q / H_kv > infv2::kMaxG) return INFV2_ERR_UNSUPPORTED;
   // element offsets are computed in 64 bits; keep sequence indices in int range
   if (static_cast<long long>(S_k) * D >= (1LL << 31)) return INFV2_ERR_UNSUPPORTED;
+  if (!grid_fits(B, H_kv, S_k)) return INFV2_ERR_UNSUPPORTED;
   return INFV2_OK;
 }
 
@@ -80,6 +91,7 @@ int check_decode(int B, int H_q, int H_kv, int D, int block_size, int max_blocks
   if (D != infv2::kD || block_size != infv2::kBS) return INFV2_ERR_UNSUPPORTED;
   if (H_q / H_kv > infv2::kMaxG) return INFV2_ERR_UNSUPPORTED;
   if (static_cast<long long>(max_blocks) * block_size * D >= (1LL << 31)) return INFV2_ERR_UNSUPPORTED;
+  if (!grid_fits(B, H_kv, static_cast<long long>(max_blocks) * block_size)) return INFV2_ERR_UNSUPPORTED;
   return INFV2_OK;
 }
 
@@ -123,6 +135,7 @@ int infv2_compress_k(const void* k, void* k_cmp, int B, int H_kv, int S_k, int D
   if (B < 0 || H_kv < 1 || S_k < 0 || D < 1 || block_size < 1) return INFV2_ERR_INVALID;
   if (D != infv2::kD || block_size != infv2::kBS) return INFV2_ERR_UNSUPPORTED;
   if (static_cast<long long>(S_k) * D >= (1LL << 31)) return INFV2_ERR_UNSUPPORTED;
+  if (!grid_fits(B, H_kv, S_k)) return INFV2_ERR_UNSUPPORTED;
   if (B == 0 || S_k == 0) return INFV2_OK;
   if (!tensor_ok(k) || !tensor_ok(k_cmp)) return INFV2_ERR_INVALID;
   return hip_status(infv2::launch_compress_k(static_cast<const uint16_t*>(k), static_cast<uint16_t*>(k_cmp),
@@ -257,10 +270,14 @@ int infv2_dense_attn_fwd(const void* q, const void* k, const void* v, void* out,
                                              s, workspace, static_cast<hipStream_t>(stream)));
 }
 
+int infv2_attn_path(int S_k, int switch_len) {
+  return S_k <= switch_len ? INFV2_PATH_DENSE : INFV2_PATH_SPARSE;
+}
+
 size_t infv2_attn_workspace_bytes(int B, int H_q, int H_kv, int S_q, int S_k, int D, int block_size, int topk,
                                   int switch_len) {
   if (check_shape(B, H_q, H_kv, S_q, S_k, D) != INFV2_OK || block_size != infv2::kBS || topk < 0) return 0;
-  if (S_k <= switch_len) return infv2_dense_workspace_bytes(B, H_q, H_kv, S_q, S_k, D);
+  if (infv2_attn_path(S_k, switch_len) == INFV2_PATH_DENSE) return infv2_dense_workspace_bytes(B, H_q, H_kv, S_q, S_k, D);
   const size_t kc = round_up(static_cast<size_t>(B) * H_kv * num_blocks(S_k, block_size) * D * 2, 256);
   const size_t idx = round_up(static_cast<size_t>(B) * H_kv * S_q * topk * 4, 256);
   return kc + idx + sparse_ws(B, H_q, H_kv, S_q, S_k, block_size, topk);
@@ -270,7 +287,7 @@ int infv2_attn_fwd(const void* q, const void* k, const void* v, void* out, float
                    int B, int H_q, int H_kv, int S_q, int S_k, int D, int block_size, int topk, int n_init,
                    int n_local, float softmax_scale, int switch_len, void* workspace, size_t workspace_bytes,
                    void* stream) {
-  if (S_k <= switch_len)
+  if (infv2_attn_path(S_k, switch_len) == INFV2_PATH_DENSE)
     return infv2_dense_attn_fwd(q, k, v, out, lse, B, H_q, H_kv, S_q, S_k, D, softmax_scale, 1, workspace,
                                 workspace_bytes, stream);
   int st = check_shape(B, H_q, H_kv, S_q, S_k, D);
@@ -347,7 +364,7 @@ int infv2_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* ou
   // the argument checks of infv2_attn_fwd, then the size check, before any HIP call
   int st = check_shape(B, H_q, H_kv, S_q, S_k, D);
   if (st != INFV2_OK) return st;
-  if (S_k > switch_len) {
+  if (infv2_attn_path(S_k, switch_len) == INFV2_PATH_SPARSE) {
     st = check_sparse_params(block_size, topk, n_init, n_local);
     if (st != INFV2_OK) return st;
     if (num_blocks(S_k, block_size) > kMaxSelectBlocks) return INFV2_ERR_UNSUPPORTED;
