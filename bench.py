@@ -78,15 +78,20 @@ def stored_traffic():
     return d.get("hbm_bytes_per_launch")
 
 
+def blas_threads():
+    """Threads the oracle's BLAS calls use."""
+    try:
+        import threadpoolctl
+        return max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    except Exception:
+        return 1
+
+
 def cpu_baseline(w, x, target_s=15.0):
     """The fp64 oracle, as it is, on a bounded sample of query rows."""
     import numpy as np
     import oracle.infv2_oracle as O
-    try:
-        import threadpoolctl
-        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+    threads = blas_threads()
     q, k, v = (x[n] for n in ("q", "k", "v"))
     t0 = time.perf_counter()
     k64 = k.double().numpy()
@@ -372,7 +377,7 @@ def decode_contiguous_entry(torch, tb, workloads, dev, with_cpu, reps=20):
         e["cpu_baseline"] = {"kind": "oracle", "unit": "ms per step", "value": round((t2 - t1) / len(bs) * w.B * 1e3, 3),
                              "sample": (f"select + attend of {len(bs)} of the 16 sequences ({t2 - t1:.2f} s) scaled "
                                         f"to 16; their key compression took {t1 - t0:.2f} s apart"),
-                             "cores": None}
+                             "cores": blas_threads()}
     del q, k, v, x, kc, idx
     torch.cuda.empty_cache()
     return e
