@@ -8,10 +8,11 @@
 // summary, Technical Mechanism).
 //
 // One workgroup = 16 consecutive query tokens of one KV head, one token per
-// wave.  The compressed keys stream through a 3-slot LDS ring of CH-block
-// chunks (direct-to-LDS loads, two chunks in flight, one barrier per chunk)
+// wave.  The compressed keys stream through a 4-slot LDS ring of CH-block
+// chunks (direct-to-LDS loads: while a pair of chunks is read, the next pair
+// is in flight)
 // that all 16 waves read, so each chunk comes from L2 once per workgroup and
-// pass.  For a token, S = Q k_cmp^T on 16x16x32 bf16 MFMAs puts the 16 heads
+// pass.  The chunks go in pairs, one barrier per pair.  For a token, S = Q k_cmp^T on 16x16x32 bf16 MFMAs puts the 16 heads
 // of the group in the rows and 16 compressed blocks in the columns: lane
 // (column hl, row quad gq) holds heads 4*gq .. 4*gq+3 of block 16*tile + hl.
 //   pass 1: each lane keeps, per head, a running max (moved only when a
@@ -34,7 +35,7 @@
 namespace infv2 {
 
 constexpr int kSelWaves = 16;           // = tokens per workgroup
-constexpr int kSelSlots = 3;            // LDS ring: the chunk being read + 2 in flight
+constexpr int kSelSlots = 4;            // LDS ring: the pair of chunks being read + the next pair
 constexpr int kSelRowBytes = kD * 2;    // one compressed block
 constexpr size_t kSelLdsMax = 160 * 1024;
 constexpr float kSelSlack = 8.f;         // log2 units a running max may lag
@@ -166,17 +167,21 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_blocks_kernel(const uin
   }
   const uint16_t* kg = kc + static_cast<size_t>(b * s.H_kv + g) * s.NB * kD;
 
-  // chunk loads: wave w < kDmaWaves moves rows 4w .. 4w+3 of a chunk; lane
-  // (sub, slot) fetches 16-byte column slot ^ swz(row) of row 4w + sub into
-  // that row's slot (rows past NB - 1 re-read row NB - 1; never used)
-  const int drow = 4 * wave + (lane >> 4);
+  // chunk loads: loader wave d < kDmaWaves of a chunk moves rows 4d .. 4d+3;
+  // lane (sub, slot) fetches 16-byte column slot ^ swz(row) of row 4d + sub
+  // into that row's slot (rows past NB - 1 re-read row NB - 1; never used).
+  // With 8 loader waves per chunk, waves 0-7 load the even chunks and waves
+  // 8-15 the odd ones; with 16, every wave loads one row group of each.
+  static_assert(kDmaWaves == 8 || kDmaWaves == 16, "loader waves per chunk");
+  const int dwave = wave % kDmaWaves;
+  const int drow = 4 * dwave + (lane >> 4);
   const uint32_t dcol = static_cast<uint32_t>(((lane & 15) ^ swz(drow)) << 4);
   const int nit = nch1 + nch;  // pass 1 chunks, then pass 2 chunks
   auto stage = [&](int it) {
-    if (wave < kDmaWaves && it < nit) {
+    if ((kDmaWaves == kSelWaves || wave / kDmaWaves == (it & 1)) && it < nit) {
       const int j = min(it < nch1 ? R * (it * CH + drow) : (it - nch1) * CH + drow, s.NB - 1);
       dma16(kg, static_cast<uint32_t>(j) * kSelRowBytes + dcol,
-            ring + (it % kSelSlots) * kSlotBytes + wave * 1024);
+            ring + (it % kSelSlots) * kSlotBytes + dwave * 1024);
     }
   };
   // B-operand read offsets (row = block within the tile, k-step ks)
@@ -236,22 +241,39 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_blocks_kernel(const uin
   };
   // pass 2: group score of this lane's block in a tile (all 64 lanes get the
   // column sum)
-  auto group_score = [&](const floatx4& acc) {
+  auto lane_score = [&](const floatx4& acc) {  // this lane's 4 heads
     float p = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) p += __builtin_amdgcn_exp2f(fmaf(acc[i], sl2, -lse2[i]));
-    return sum_xor32(sum_xor16(p));
+    return p;
+  };
+  auto group_score = [&](const floatx4& acc) { return sum_xor32(sum_xor16(lane_score(acc))); };
+  // The group scores of a whole chunk: the row quads' partial sums of the
+  // kTiles tiles are exchanged in a transpose (quad pairs first, then wave
+  // halves), so that quad gq ends with tile gq % kTiles, summed in the same
+  // order as group_score: (quad 0 + quad 1) + (quad 2 + quad 3).
+  auto chunk_scores = [&](const floatx4* acc) {
+    auto swap16 = [](float a, float b) {  // even rows: a's own and b's odd rows; odd rows: the rest
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+      return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    };
+    if constexpr (kTiles == 4) {
+      // rows gq = 0, 2 hold tile 0 (u) and tile 2 (w), rows 1, 3 tiles 1 and 3, each summed over a quad pair
+      const float u = swap16(lane_score(acc[0]), lane_score(acc[1]));
+      const float w = swap16(lane_score(acc[2]), lane_score(acc[3]));
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(u), __float_as_uint(w), false, false);
+      return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else {
+      static_assert(kTiles == 2, "chunks of 32 or 64 blocks");
+      return sum_xor32(swap16(lane_score(acc[0]), lane_score(acc[1])));
+    }
   };
   using AllTiles = std::integral_constant<int, kTiles>;
   using OneTile = std::integral_constant<int, 1>;
 
-  stage(0);
-  stage(1);
-  for (int it = 0; it < nit; ++it) {  // pass 1 chunks, then pass 2 chunks
-    if (it + 1 < nit) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // chunk `it` is in LDS; every wave is done with chunk it - 1
-    stage(it + 2);    // into the slot chunk it - 1 used
+  // chunk `it` of the sequence (pass 1 chunks, then pass 2 chunks), read from
+  // its ring slot
+  auto chunk = [&](int it) {
     if (it == nch1) {
       // end of pass 1: merge the 16 lanes of each row (one head per register i)
 #pragma unroll
@@ -269,7 +291,7 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_blocks_kernel(const uin
       // row x is block R * x, standing for blocks R*x .. R*x + R-1 that are
       // visible (weight w: log2(w) / sl2 added to its scores)
       const int jc = it * CH;
-      if (!active || R * jc >= nv) continue;
+      if (!active || R * jc >= nv) return;
       if (R * (jc + CH) <= nv) {
         floatx4 acc[kTiles];
         scores(buf, 0, AllTiles{}, acc);
@@ -293,10 +315,10 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_blocks_kernel(const uin
           lse_update(acc, OneTile{});
         }
       }
-      continue;
+      return;
     }
     const int jc = (it - nch1) * CH;  // first block of the pass 2 chunk
-    if (!active || jc >= nv) continue;
+    if (!active || jc >= nv) return;
     const bool full = jc + CH <= nv;
     {
       if (full) {
@@ -304,13 +326,7 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_blocks_kernel(const uin
         scores(buf, 0, AllTiles{}, acc);
         // row quad gq stores tile gq % kTiles (quads with the same tile store
         // the same value to the same address)
-        float mine = 0.f;
-#pragma unroll
-        for (int t = 0; t < kTiles; ++t) {
-          const float p = group_score(acc[t]);
-          mine = (gq % kTiles) == t ? p : mine;
-        }
-        sig[jc + 16 * (gq % kTiles) + hl] = mine;
+        sig[jc + 16 * (gq % kTiles) + hl] = chunk_scores(acc);
       } else {
         for (int t = 0; t < kTiles && jc + 16 * t < nv; ++t) {
           floatx4 acc[1];
@@ -321,6 +337,17 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_blocks_kernel(const uin
         }
       }
     }
+  };
+
+  stage(0);
+  stage(1);
+  for (int it = 0; it < nit; it += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // chunks it, it + 1 are in LDS; every wave is done with it - 2, it - 1
+    stage(it + 2);    // into the slots chunks it - 2, it - 1 used
+    stage(it + 3);
+    chunk(it);
+    if (it + 1 < nit) chunk(it + 1);
   }
 
   if (!active || s.topk == 0) return;  // no barriers below
