@@ -61,6 +61,61 @@ __device__ __forceinline__ void lse_merge_row(float& m, float& l) {
   m = mn;
 }
 
+// Radix search for the threshold of an exact top-kk over keys x[t] (slot t
+// of lane l holds a key, 0 where empty: every real key has a bit set).  From
+// the state (tt, bit, cnt): tt a prefix of the answer with bits above `bit`
+// decided, cnt = #{x >= tt} >= kk, each round tries bit `bit` of tt, keeping
+// it if at least kk keys are >= the candidate.  It stops when every bit is
+// decided, when exactly kk keys are >= tt (those kk keys are then the
+// selection), or, if stop_at > 0, as soon as cnt <= stop_at.  Returns true if
+// the threshold is final.
+template <int NS>
+__device__ __forceinline__ bool radix_rounds(const uint32_t (&x)[NS], int kk, uint32_t& tt, int& bit, int& cnt,
+                                             int stop_at) {
+  for (; bit >= 0; --bit) {
+    if (cnt == kk) return true;
+    if (cnt <= stop_at) return false;
+    const uint32_t cv = tt | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int t = 0; t < NS; ++t) c += __popcll(__ballot(x[t] >= cv));
+    if (c >= kk) {
+      tt = cv;
+      cnt = c;
+    }
+  }
+  return true;
+}
+
+// The keys > tt and the first (lowest-index) ties at tt: kk of them, written
+// to out[0 .. kk) in ascending index order.  Slot t of lane l holds key x[t]
+// of index idx[t] (indices ascending in (t, lane) order), valid[t] marks the
+// slots that hold a candidate.
+template <int NS>
+__device__ __forceinline__ void emit_topk(const uint32_t (&x)[NS], const int (&idx)[NS], const bool (&valid)[NS],
+                                          uint32_t tt, int kk, int first, int32_t* out, float* out_s) {
+  int n_gt = 0;
+#pragma unroll
+  for (int t = 0; t < NS; ++t) n_gt += __popcll(__ballot(valid[t] && x[t] > tt));
+  const int need_eq = kk - n_gt;  // ties at tt, lowest indices first
+  int eq_before = 0, n_out = 0;
+#pragma unroll
+  for (int t = 0; t < NS; ++t) {
+    const bool gt = valid[t] && x[t] > tt;
+    const bool eq = valid[t] && x[t] == tt;
+    const uint64_t eqm = __ballot(eq);
+    const bool sel = gt || (eq && eq_before + mask_rank(eqm) < need_eq);
+    eq_before += __popcll(eqm);
+    const uint64_t selm = __ballot(sel);
+    const int pos = n_out + mask_rank(selm);
+    if (sel && pos < kk) {
+      out[pos] = first + idx[t];
+      if (out_s) out_s[pos] = __uint_as_float(x[t]);
+    }
+    n_out += __popcll(selm);
+  }
+}
+
 // Exact top-kk (kk = topk < nC) of the nC scores cand[0 .. nC), candidate c
 // in slot c / 64 of lane c % 64 (NS >= ceil(nC / 64) slots per lane).  Keys
 // are the fp32 bit patterns with the sign cleared: every key is below 2^31,
@@ -69,53 +124,88 @@ __device__ __forceinline__ void lse_merge_row(float& m, float& l) {
 // largest key, or any prefix of it at or below which exactly kk keys lie.
 // The keys above tt and the first (lowest-index) ties at tt are kept, written
 // to out[0 .. kk) in ascending index order (index = first + c).
+// Two shortcuts leave the result unchanged.  The bits every candidate shares
+// are taken into tt at once (a round at such a bit keeps it exactly when the
+// keys have it).  And with NS >= 8, once at most 16 NS keys are >= tt (keys
+// below tt can no longer be selected), those keys and their indices are
+// compacted, in index order, into the start of cand (this wave's own row:
+// nC > 32 NS), and the search goes on over NS / 4 slots per lane.
 template <int NS>
-__device__ __forceinline__ void topk_row(const float* cand, int nC, int topk, int first, int32_t* out,
-                                         float* out_s, int lane) {
+__device__ __forceinline__ void topk_row(float* cand, int nC, int topk, int first, int32_t* out, float* out_s,
+                                         int lane) {
   const int kk = topk;
   uint32_t x[NS];
+  int idx[NS];
+  bool valid[NS];
 #pragma unroll
   for (int t = 0; t < NS; ++t) {
     const int c = t * 64 + lane;
-    x[t] = c < nC ? __float_as_uint(cand[c]) & 0x7fffffffu : 0u;
+    valid[t] = c < nC;
+    idx[t] = c;
+    x[t] = valid[t] ? __float_as_uint(cand[c]) & 0x7fffffffu : 0u;
   }
-  // largest tt with #{x >= tt} >= kk (padding keys are 0 and never reach a
-  // candidate value, which has a bit set).  The search may stop as soon as
-  // exactly kk keys are >= the prefix found so far: those kk keys are then
-  // the selection, and the pass below keeps exactly them.
   uint32_t tt = 0;
-  for (int bit = 30; bit >= 0; --bit) {
-    const uint32_t cv = tt | (1u << bit);
-    int cnt = 0;
+  int bit = 30;
+  int cnt = nC;
+  if constexpr (NS >= 4) {
+    uint32_t o = 0u, a = 0xffffffffu;
 #pragma unroll
-    for (int t = 0; t < NS; ++t) cnt += __popcll(__ballot(x[t] >= cv));
-    if (cnt >= kk) {
-      tt = cv;
-      if (cnt == kk) break;
+    for (int t = 0; t < NS; ++t) {
+      o |= x[t];
+      a &= valid[t] ? x[t] : 0xffffffffu;
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      o |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(o), m, 64));
+      a &= static_cast<uint32_t>(__shfl_xor(static_cast<int>(a), m, 64));
+    }
+    const uint32_t d = o ^ a;  // bits in which the candidates differ (keys < 2^31)
+    if (d == 0u) {
+      tt = a;
+      bit = -1;
+    } else {
+      bit = 31 - __builtin_clz(d);
+      tt = a & ~((2u << bit) - 1u);
     }
   }
-  int n_gt = 0;
+  if constexpr (NS >= 8) {
+    constexpr int S2 = NS / 4;
+    constexpr int cap = 64 * S2;
+    if (!radix_rounds<NS>(x, kk, tt, bit, cnt, cap)) {
+      // compact the cnt keys >= tt: keys into cand[0 .. cnt), indices after them
+      uint32_t* ck = reinterpret_cast<uint32_t*>(cand);
+      int* ci = reinterpret_cast<int*>(cand) + cap;
+      int base = 0;
 #pragma unroll
-  for (int t = 0; t < NS; ++t) n_gt += __popcll(__ballot(x[t] > tt));
-  const int need_eq = kk - n_gt;  // ties at tt, lowest indices first
-
-  int eq_before = 0, n_out = 0;
+      for (int t = 0; t < NS; ++t) {
+        const bool keep = valid[t] && x[t] >= tt;
+        const uint64_t km = __ballot(keep);
+        if (keep) {
+          const int pos = base + mask_rank(km);
+          ck[pos] = x[t];
+          ci[pos] = idx[t];
+        }
+        base += __popcll(km);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave reads back what its lanes wrote
+      uint32_t y[S2];
+      int yi[S2];
+      bool yv[S2];
 #pragma unroll
-  for (int t = 0; t < NS; ++t) {
-    const bool valid = t * 64 + lane < nC;
-    const bool gt = x[t] > tt;
-    const bool eq = valid && x[t] == tt;
-    const uint64_t eqm = __ballot(eq);
-    const bool sel = gt || (eq && eq_before + mask_rank(eqm) < need_eq);
-    eq_before += __popcll(eqm);
-    const uint64_t selm = __ballot(sel);
-    const int pos = n_out + mask_rank(selm);
-    if (sel && pos < kk) {
-      out[pos] = first + t * 64 + lane;
-      if (out_s) out_s[pos] = __uint_as_float(x[t]);
+      for (int s2 = 0; s2 < S2; ++s2) {
+        const int e = s2 * 64 + lane;
+        yv[s2] = e < cnt;
+        y[s2] = yv[s2] ? ck[e] : 0u;
+        yi[s2] = yv[s2] ? ci[e] : 0;
+      }
+      radix_rounds<S2>(y, kk, tt, bit, cnt, 0);
+      emit_topk<S2>(y, yi, yv, tt, kk, first, out, out_s);
+      return;
     }
-    n_out += __popcll(selm);
+  } else {
+    radix_rounds<NS>(x, kk, tt, bit, cnt, 0);
   }
+  emit_topk<NS>(x, idx, valid, tt, kk, first, out, out_s);
 }
 
 // R = 1: exact log-sum-exp in pass 1.  R > 1: the approximate one of
