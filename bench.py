@@ -262,6 +262,38 @@ def time_decode_paged(torch, tb, workloads, dev, reps=50):
     return res
 
 
+def shared_selection(torch, w, frac, dev, seed=7):
+    """Block indices of the workload's shape in which the 16 tokens of each
+    query window share round(frac * topk) of their selected blocks, the rest
+    drawn per token: every row gets min(topk, candidates) distinct candidate
+    blocks (n_init .. qb - n_local), ascending, -1 padded, so it attends as
+    many keys as under the real selection (the same algorithmic FLOPs)."""
+    nb = (w.S_k + w.block_size - 1) // w.block_size
+    r = torch.arange(w.S_q, device=dev)
+    qb = (w.S_k - w.S_q + r) // w.block_size
+    j = torch.arange(nb, device=dev)
+    cand = (j[None, :] >= w.n_init) & (j[None, :] <= (qb - w.n_local)[:, None])
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    heads = w.B * w.H_kv
+    shared_key = torch.rand(heads, (w.S_q + 15) // 16, nb, device=dev, generator=g)[:, r // 16]
+    own_key = torch.rand(heads, w.S_q, nb, device=dev, generator=g)
+    n_sh = int(round(frac * w.topk))
+    neg = torch.tensor(-1.0, device=dev)
+    parts, taken = [], torch.zeros(heads, w.S_q, nb, dtype=torch.bool, device=dev)
+    if n_sh:
+        val, ix = torch.where(cand, shared_key, neg).topk(n_sh, dim=-1)
+        taken.scatter_(-1, ix, val >= 0)
+        parts.append(torch.where(val >= 0, ix, -1))
+    if w.topk - n_sh:
+        val, ix = torch.where(cand & ~taken, own_key, neg).topk(w.topk - n_sh, dim=-1)
+        parts.append(torch.where(val >= 0, ix, -1))
+    ix = torch.cat(parts, -1)
+    ix = torch.where(ix < 0, nb + 1, ix).sort(dim=-1).values
+    ix = torch.where(ix > nb, -1, ix).to(torch.int32)
+    return ix.view(w.B, w.H_kv, w.S_q, w.topk).contiguous()
+
+
 def event_ms(torch, f, n, warm=1, warm_s=0.1):
     """Average ms of n back-to-back calls of f (HIP events on the current
     stream), after at least `warm` calls and warm_s seconds of calls: the
@@ -577,6 +609,19 @@ def main():
         del approx, hit
     del exact, valid
 
+    # ---- the sparse kernel's dependence on how much a window's tokens share:
+    # the same shape and FLOPs, with synthetic selections in which the 16
+    # tokens of each window share 0, 1/2 or all of their top-k blocks --------
+    shared = {}
+    for frac in (0.0, 0.5, 1.0):
+        sidx = shared_selection(torch, wl, frac, dev)
+        ms = event_ms(torch, lambda: tb.sparse_attn_fwd(q, k, v, sidx, wl.n_init, wl.n_local, return_lse=False), 10)
+        tf = sparse_flops / (ms * 1e-3) / 1e12
+        shared[str(frac)] = {"sparse_attn_ms": round(ms, 4), "tflops": round(tf, 2),
+                             "mfma_peak_frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del sidx
+    torch.cuda.empty_cache()
+
     # ---- the compressed-attention branch, alone and mixed with the sparse output --
     compressed = None
     if not args.no_compressed:
@@ -692,6 +737,7 @@ def main():
             round(dense_flops / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
         "decode_b16_32k_paged": decode,
         "select_strided_lse": strided,
+        "sparse_attn_shared_selection": shared,
         "compressed_branch": compressed,
         "configs": configs,
         "algorithmic_flops": {"sparse_attn": sparse_flops, "dense_attn": dense_flops, "select": select_flops,
