@@ -481,8 +481,9 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_decode_kernel(const uin
                                                                        int32_t* __restrict__ blk_idx,
                                                                        float* __restrict__ blk_score, AttnShape s) {
   extern __shared__ __align__(16) unsigned char dec_smem[];
-  float* part = reinterpret_cast<float*>(dec_smem);              // [16 waves][16 heads][2]
-  float* sig = part + kSelWaves * kMaxG * 2;                        // [NB]
+  float* part = reinterpret_cast<float*>(dec_smem);              // max, then sum: [2][16 waves][16 heads]
+  float* lse_sh = part + kSelWaves * kMaxG * 2;                     // [16 heads]
+  float* sig = lse_sh + kMaxG;                                       // [NB]
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int hl = lane & 15, gq = lane >> 4;
@@ -552,10 +553,12 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_decode_kernel(const uin
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int t = 0; t < kDecTiles; ++t) m[i] = fmaxf(m[i], z[t][i]);
+    for (int t = 0; t < kDecTiles; ++t)
+      if (t < tpw) m[i] = fmaxf(m[i], z[t][i]);  // tiles past tpw are -inf
     if (m[i] != -INFINITY) {
 #pragma unroll
-      for (int t = 0; t < kDecTiles; ++t) l[i] += __builtin_amdgcn_exp2f(z[t][i] - m[i]);
+      for (int t = 0; t < kDecTiles; ++t)
+        if (t < tpw) l[i] += __builtin_amdgcn_exp2f(z[t][i] - m[i]);
     }
     // the 16 lanes of the row hold the same head's other blocks
     lse_merge_row<0x128>(m[i], l[i]);
@@ -563,23 +566,42 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_decode_kernel(const uin
     lse_merge_row<0x122>(m[i], l[i]);
     lse_merge_row<0x121>(m[i], l[i]);
     if (hl == 0) {
-      part[(wave * kMaxG + 4 * gq + i) * 2] = m[i];
-      part[(wave * kMaxG + 4 * gq + i) * 2 + 1] = l[i];
+      part[wave * kMaxG + 4 * gq + i] = m[i];
+      part[(kSelWaves + wave) * kMaxG + 4 * gq + i] = l[i];
+    }
+  }
+  __syncthreads();
+  // wave 0 merges the waves' (max, sum) of each head (lane: its 4 heads; each
+  // wave's four values are one 16-byte read) into the log-sum-exp
+  if (wave == 0) {
+    floatx4 mm = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+      const floatx4 a = *reinterpret_cast<const floatx4*>(part + w * kMaxG + 4 * gq);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mm[i] = fmaxf(mm[i], a[i]);
+    }
+    floatx4 ll = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+      const floatx4 a = *reinterpret_cast<const floatx4*>(part + w * kMaxG + 4 * gq);
+      const floatx4 c = *reinterpret_cast<const floatx4*>(part + (kSelWaves + w) * kMaxG + 4 * gq);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (a[i] != -INFINITY) ll[i] += c[i] * exp2f(a[i] - mm[i]);
+    }
+    if (hl == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)  // heads >= G add nothing
+        lse_sh[4 * gq + i] = 4 * gq + i < s.G && mm[i] != -INFINITY ? mm[i] + log2f(ll[i]) : INFINITY;
     }
   }
   __syncthreads();
   float lse2[4];
+  {
+    const floatx4 a = *reinterpret_cast<const floatx4*>(lse_sh + 4 * gq);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * gq + i;
-    float mm = -INFINITY;
-    for (int w = 0; w < kSelWaves; ++w) mm = fmaxf(mm, part[(w * kMaxG + h) * 2]);
-    float ll = 0.f;
-    for (int w = 0; w < kSelWaves; ++w) {
-      const float mw = part[(w * kMaxG + h) * 2];
-      if (mw != -INFINITY) ll += part[(w * kMaxG + h) * 2 + 1] * exp2f(mw - mm);
-    }
-    lse2[i] = h < s.G && mm != -INFINITY ? mm + log2f(ll) : INFINITY;  // heads >= G add nothing
+    for (int i = 0; i < 4; ++i) lse2[i] = a[i];
   }
   // group scores of this wave's blocks
 #pragma unroll
@@ -636,7 +658,7 @@ hipError_t launch_select_blocks(const uint16_t* q, const uint16_t* k_cmp, int32_
                                 float* blk_score, const AttnShape& s, hipStream_t stream, int lse_stride) {
   if (s.B == 0 || s.S_q == 0) return hipSuccess;
   if (s.S_q == 1 && lse_stride == 1) {  // one query per sequence: the workgroup splits its blocks
-    const size_t lds = (static_cast<size_t>(kSelWaves) * kMaxG * 2 + sel_stride(s.NB)) * sizeof(float);
+    const size_t lds = (static_cast<size_t>(kSelWaves) * kMaxG * 2 + kMaxG + sel_stride(s.NB)) * sizeof(float);
     hipLaunchKernelGGL(select_decode_kernel, dim3(s.B * s.H_kv), dim3(64 * kSelWaves), lds, stream, q, k_cmp,
                        blk_idx, blk_score, s);
     return hipGetLastError();
