@@ -37,7 +37,8 @@
  *    any HIP call; on an error nothing is launched and outputs are untouched.
  *    Supported on the GPU: D = 128, block_size = 64, 1 <= G <= 16,
  *    0 <= topk <= 256, and at most 4064 key blocks (S_k <= 260096) for the
- *    sparse forward and backward (2048 for the block selection), at most
+ *    block selection, the sparse forward and backward and the switch (2048
+ *    for the one-query decode selection, infv2_decode_select), at most
  *    65535 (batch, kv head) pairs and B * H_kv * S_k <= 2^25 (the launch
  *    grids' limits); other values give INFV2_ERR_UNSUPPORTED.
  *  - The library keeps no state between calls; calls on distinct streams

@@ -111,7 +111,7 @@ def test_other_entry_points_validate():
     assert lib.infv2_compress_k(FAKE, FAKE, 1, 0, 100, 128, 64, None) == tb.ERR_INVALID
     assert lib.infv2_compress_k(FAKE, FAKE, 0, 2, 100, 128, 64, None) == tb.OK
     sel = lib.infv2_select_blocks
-    assert sel(FAKE, FAKE, FAKE, None, 1, 32, 2, 10, 200000, 128, 64, 8, 1, 2, 0.0, None) == tb.ERR_UNSUPPORTED
+    assert sel(FAKE, FAKE, FAKE, None, 1, 32, 2, 10, 4065 * 64, 128, 64, 8, 1, 2, 0.0, None) == tb.ERR_UNSUPPORTED
     assert sel(FAKE, FAKE, FAKE, FAKE_MIS, 1, 32, 2, 10, 2000, 128, 64, 8, 1, 2, 0.0, None) == tb.ERR_INVALID
     assert sel(FAKE, FAKE, None, None, 1, 32, 2, 10, 2000, 128, 64, 8, 1, 2, 0.0, None) == tb.ERR_INVALID
     assert sel(FAKE, FAKE, FAKE, None, 1, 32, 2, 10, 2000, 128, 64, 8, 1, 0, 0.0, None) == tb.ERR_INVALID
@@ -335,7 +335,7 @@ def test_noalloc_switch_refuses_shapes_beyond_its_scratch():
     assert call() == tb.ERR_WORKSPACE
     assert call(H_q=31) == tb.ERR_INVALID
     assert call(B=0) == tb.OK
-    assert call(S_k=4096 * 64) == tb.ERR_UNSUPPORTED          # beyond the 2048 blocks selection keeps
+    assert call(S_k=4064 * 64 + 1, S_q=10) == tb.ERR_UNSUPPORTED   # beyond the 4064 blocks selection keeps
 
 
 @no_gpu
@@ -363,3 +363,28 @@ def test_switch_path_rule_lives_in_the_library():
     assert lib.infv2_attn_path(0, 0) == tb.PATH_DENSE
     assert lib.infv2_attn_path(1, 0) == tb.PATH_SPARSE
     assert lib.infv2_attn_path(8192, -1) == tb.PATH_SPARSE
+
+
+@no_gpu
+def test_selection_and_switch_take_up_to_4064_blocks():
+    lib = tb.load_library()
+
+    def sel(S_k, S_q=10, stride=0, **kw):
+        a = dict(q=FAKE, kc=FAKE, idx=FAKE, B=1, H_q=32, H_kv=2, topk=64)
+        a.update(kw)
+        if stride:
+            return lib.infv2_select_blocks_strided_lse(a["q"], a["kc"], a["idx"], None, a["B"], a["H_q"], a["H_kv"],
+                                                       S_q, S_k, 128, 64, a["topk"], 1, 2, 0.0, stride, None)
+        return lib.infv2_select_blocks(a["q"], a["kc"], a["idx"], None, a["B"], a["H_q"], a["H_kv"], S_q, S_k, 128,
+                                       64, a["topk"], 1, 2, 0.0, None)
+    # 4064 blocks pass the shape checks (and then stop at the missing output); 4065 do not
+    assert sel(4064 * 64, idx=None) == tb.ERR_INVALID
+    assert sel(4064 * 64 + 1) == tb.ERR_UNSUPPORTED
+    assert sel(4064 * 64, stride=4, idx=None) == tb.ERR_INVALID
+    assert sel(4064 * 64 + 1, stride=4) == tb.ERR_UNSUPPORTED
+
+    def switch(S_k, ws=None, wsb=0):
+        return lib.infv2_attn_fwd(FAKE, FAKE, FAKE, FAKE, None, None, 1, 32, 2, 10, S_k, 128, 64, 64, 1, 2, 0.0, 0,
+                                  ws, wsb, None)
+    assert switch(4064 * 64) == tb.ERR_WORKSPACE
+    assert switch(4064 * 64 + 1) == tb.ERR_UNSUPPORTED

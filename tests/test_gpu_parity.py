@@ -57,6 +57,11 @@ SELECT_CASES = [
     ("switch_4k_g16", workloads.SWITCH_SPARSE.with_(S_q=4096, S_k=4096, switch_len=0), np.arange(0, 4096, 5)),
     ("ragged_sq37_sk3000", workloads.TINY.with_(H_q=32, H_kv=2, S_q=37, S_k=3000, topk=9), None),
     ("g4_topk40", workloads.TINY.with_(H_q=8, H_kv=2, S_q=1500, S_k=1500, topk=40, n_init=2, n_local=3), None),
+    # past 2048 blocks: the 8-token workgroups (ragged last workgroup), up to
+    # 2100 candidates per row (33 slots per lane in the top-k)
+    ("wide_2100blk_sq700", workloads.TINY.with_(H_q=32, H_kv=2, S_q=700, S_k=2100 * 64, topk=64), None),
+    # the block cap: 4060 candidates per row (64 slots per lane), top-128
+    ("cap_4064blk_topk128", workloads.TINY.with_(H_q=16, H_kv=1, S_q=40, S_k=4064 * 64, topk=128), None),
 ]
 
 
@@ -334,3 +339,13 @@ def test_determinism_bitwise():
     torch.cuda.synchronize()
     assert torch.equal(r1["blk_idx"], r2["blk_idx"])
     assert torch.equal(r1["out"], r2["out"]) and torch.equal(r1["lse"], r2["lse"])
+
+
+@pytest.mark.parametrize("S_q", [1, 40])
+def test_switch_past_2048_blocks(S_q):
+    # the whole switch (compress -> selection -> sparse attention) where the
+    # selection takes the 8-token workgroups; one query goes there too (the
+    # one-query selection kernel stops at 2048 blocks)
+    from tests.test_gpu_configs import run_and_check
+    w = workloads.TINY.with_(name=f"switch_3000blk_sq{S_q}", H_q=16, H_kv=2, S_q=S_q, S_k=3000 * 64 - 17, topk=64)
+    run_and_check(w, rows=np.arange(S_q))

@@ -30,6 +30,7 @@ CASES = [
     ("tiny_2k_g8", workloads.TINY, None),
     ("switch_4k_g16", workloads.SWITCH_SPARSE.with_(S_q=4096, S_k=4096, switch_len=0), np.arange(0, 4096, 7)),
     ("ragged_sq37_sk3000", workloads.TINY.with_(H_q=32, H_kv=2, S_q=37, S_k=3000, topk=9), None),
+    ("wide_2100blk_sq70", workloads.TINY.with_(H_q=32, H_kv=2, S_q=70, S_k=2100 * 64, topk=64), None),
 ]
 
 

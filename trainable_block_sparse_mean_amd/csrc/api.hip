@@ -15,7 +15,11 @@ namespace {
 
 constexpr int kAbiVersion = 1;
 constexpr int kMaxTopk = 256;
-constexpr int kMaxSelectBlocks = 2048;  // select keeps each token's scores in LDS
+// Selection keeps each token's block scores in LDS: up to 4064 blocks for
+// prefill queries (as many as the sparse kernels take), 2048 for one-query
+// decode selection (a wave holds at most 8 tiles of 16 blocks).
+constexpr int kMaxSelectBlocks = infv2::kMaxSparseBlocks;
+constexpr int kMaxDecodeSelectBlocks = 2048;
 // the sparse kernels keep a member mask and a list entry (8 bytes) per key
 // block in LDS beside the 128 KB K/V ring (kernels.hpp)
 using infv2::kMaxSparseBlocks;
@@ -409,7 +413,7 @@ int infv2_decode_select(const void* q, const void* k_cmp, const int32_t* seqlens
   if (st != INFV2_OK) return st;
   st = check_sparse_params(block_size, topk, n_init, n_local);
   if (st != INFV2_OK) return st;
-  if (max_blocks > kMaxSelectBlocks) return INFV2_ERR_UNSUPPORTED;
+  if (max_blocks > kMaxDecodeSelectBlocks) return INFV2_ERR_UNSUPPORTED;
   if (B == 0 || topk == 0) return INFV2_OK;
   if (!tensor_ok(q) || !tensor_ok(k_cmp) || !tensor_ok(blk_idx) || !ints_ok(seqlens)) return INFV2_ERR_INVALID;
   if (blk_score && !aligned(blk_score, 16)) return INFV2_ERR_INVALID;

@@ -43,10 +43,15 @@ constexpr float kSelSlack = 8.f;         // log2 units a running max may lag
 // floats per token row of block scores in LDS
 __host__ __device__ constexpr int sel_stride(int NB) { return (NB + 3) & ~3; }
 
-template <int CH>
+template <int CH, int WAVES = kSelWaves>
 constexpr size_t select_lds(int NB) {
-  return static_cast<size_t>(kSelSlots) * CH * kSelRowBytes + static_cast<size_t>(kSelWaves) * sel_stride(NB) * 4;
+  return static_cast<size_t>(kSelSlots) * CH * kSelRowBytes + static_cast<size_t>(WAVES) * sel_stride(NB) * 4;
 }
+// Past 2048 blocks the score rows of 16 tokens no longer fit beside the ring:
+// workgroups of 8 tokens (8 waves) with 32-block chunks take up to 4064.
+constexpr int kSelWideWaves = 8;
+static_assert(select_lds<32, kSelWideWaves>(kMaxSparseBlocks) <= kSelLdsMax, "8 score rows of 4064 blocks fit");
+static_assert(select_lds<32>(2048) <= kSelLdsMax, "16 score rows of 2048 blocks fit");
 
 // (max, sum of exp2 relative to the max) of the lanes l and l ^ mask within
 // a 16-lane DPP row; dpp = row_ror control.  Both partners compute the same
@@ -89,27 +94,27 @@ __device__ __forceinline__ bool radix_rounds(const uint32_t (&x)[NS], int kk, ui
 
 // The keys > tt and the first (lowest-index) ties at tt: kk of them, written
 // to out[0 .. kk) in ascending index order.  Slot t of lane l holds key x[t]
-// of index idx[t] (indices ascending in (t, lane) order), valid[t] marks the
-// slots that hold a candidate.
-template <int NS>
-__device__ __forceinline__ void emit_topk(const uint32_t (&x)[NS], const int (&idx)[NS], const bool (&valid)[NS],
-                                          uint32_t tt, int kk, int first, int32_t* out, float* out_s) {
+// of index idx_at(t) (indices ascending in (t, lane) order); valid_at(t) says
+// whether the slot holds a candidate.
+template <int NS, typename Valid, typename Idx>
+__device__ __forceinline__ void emit_topk(const uint32_t (&x)[NS], Valid valid_at, Idx idx_at, uint32_t tt, int kk,
+                                          int first, int32_t* out, float* out_s) {
   int n_gt = 0;
 #pragma unroll
-  for (int t = 0; t < NS; ++t) n_gt += __popcll(__ballot(valid[t] && x[t] > tt));
+  for (int t = 0; t < NS; ++t) n_gt += __popcll(__ballot(valid_at(t) && x[t] > tt));
   const int need_eq = kk - n_gt;  // ties at tt, lowest indices first
   int eq_before = 0, n_out = 0;
 #pragma unroll
   for (int t = 0; t < NS; ++t) {
-    const bool gt = valid[t] && x[t] > tt;
-    const bool eq = valid[t] && x[t] == tt;
+    const bool gt = valid_at(t) && x[t] > tt;
+    const bool eq = valid_at(t) && x[t] == tt;
     const uint64_t eqm = __ballot(eq);
     const bool sel = gt || (eq && eq_before + mask_rank(eqm) < need_eq);
     eq_before += __popcll(eqm);
     const uint64_t selm = __ballot(sel);
     const int pos = n_out + mask_rank(selm);
     if (sel && pos < kk) {
-      out[pos] = first + idx[t];
+      out[pos] = first + idx_at(t);
       if (out_s) out_s[pos] = __uint_as_float(x[t]);
     }
     n_out += __popcll(selm);
@@ -135,15 +140,10 @@ __device__ __forceinline__ void topk_row(float* cand, int nC, int topk, int firs
                                          int lane) {
   const int kk = topk;
   uint32_t x[NS];
-  int idx[NS];
-  bool valid[NS];
+  auto valid = [&](int t) { return t * 64 + lane < nC; };
+  auto index = [&](int t) { return t * 64 + lane; };
 #pragma unroll
-  for (int t = 0; t < NS; ++t) {
-    const int c = t * 64 + lane;
-    valid[t] = c < nC;
-    idx[t] = c;
-    x[t] = valid[t] ? __float_as_uint(cand[c]) & 0x7fffffffu : 0u;
-  }
+  for (int t = 0; t < NS; ++t) x[t] = valid(t) ? __float_as_uint(cand[index(t)]) & 0x7fffffffu : 0u;
   uint32_t tt = 0;
   int bit = 30;
   int cnt = nC;
@@ -152,7 +152,7 @@ __device__ __forceinline__ void topk_row(float* cand, int nC, int topk, int firs
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
       o |= x[t];
-      a &= valid[t] ? x[t] : 0xffffffffu;
+      a &= valid(t) ? x[t] : 0xffffffffu;
     }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
@@ -178,12 +178,12 @@ __device__ __forceinline__ void topk_row(float* cand, int nC, int topk, int firs
       int base = 0;
 #pragma unroll
       for (int t = 0; t < NS; ++t) {
-        const bool keep = valid[t] && x[t] >= tt;
+        const bool keep = valid(t) && x[t] >= tt;
         const uint64_t km = __ballot(keep);
         if (keep) {
           const int pos = base + mask_rank(km);
           ck[pos] = x[t];
-          ci[pos] = idx[t];
+          ci[pos] = index(t);
         }
         base += __popcll(km);
       }
@@ -199,21 +199,22 @@ __device__ __forceinline__ void topk_row(float* cand, int nC, int topk, int firs
         yi[s2] = yv[s2] ? ci[e] : 0;
       }
       radix_rounds<S2>(y, kk, tt, bit, cnt, 0);
-      emit_topk<S2>(y, yi, yv, tt, kk, first, out, out_s);
+      emit_topk<S2>(y, [&](int t) { return yv[t]; }, [&](int t) { return yi[t]; }, tt, kk, first, out, out_s);
       return;
     }
   } else {
     radix_rounds<NS>(x, kk, tt, bit, cnt, 0);
   }
-  emit_topk<NS>(x, idx, valid, tt, kk, first, out, out_s);
+  emit_topk<NS>(x, valid, index, tt, kk, first, out, out_s);
 }
 
 // R = 1: exact log-sum-exp in pass 1.  R > 1: the approximate one of
 // infv2_select_blocks_strided_lse - pass 1 scores only every R-th visible
 // compressed block, each standing for the R blocks of its group (the last
 // group for its visible count), so it streams 1/R of the compressed keys.
-template <int CH, int R>
-__global__ __launch_bounds__(kSelWaves * 64) void select_blocks_kernel(const uint16_t* __restrict__ q,
+// WAVES: tokens per workgroup (16, or 8 past 2048 blocks).
+template <int CH, int R, int WAVES = kSelWaves>
+__global__ __launch_bounds__(WAVES * 64) void select_blocks_kernel(const uint16_t* __restrict__ q,
                                                                        const uint16_t* __restrict__ kc,
                                                                        int32_t* __restrict__ blk_idx,
                                                                        float* __restrict__ blk_score,
@@ -231,12 +232,12 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_blocks_kernel(const uin
   const int gq = lane >> 4;   // row quad: heads 4*gq .. 4*gq+3
   const int g = blockIdx.y % s.H_kv;
   const int b = blockIdx.y / s.H_kv;
-  const int r0 = (gridDim.x - 1 - blockIdx.x) * kSelWaves;  // latest (heaviest) tokens first
+  const int r0 = (gridDim.x - 1 - blockIdx.x) * WAVES;  // latest (heaviest) tokens first
   const int r = r0 + wave;    // this wave's token
   const int off = seq_keys(s, b) - s.S_q;  // query row r sits at key position off + r
   const bool active = r < s.S_q;
   const int nv = active ? (off + r + 1) / kBS : 0;  // fully visible blocks
-  const int r_last = min(r0 + kSelWaves, s.S_q) - 1;
+  const int r_last = min(r0 + WAVES, s.S_q) - 1;
   const int nv_max = (off + r_last + 1) / kBS;      // largest nv of the workgroup
   const int nch = (nv_max + CH - 1) / CH;             // pass 2 chunks (every block)
   const int nch1 = ((nv_max + R - 1) / R + CH - 1) / CH;  // pass 1 chunks (every R-th block)
@@ -260,15 +261,16 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_blocks_kernel(const uin
   // chunk loads: loader wave d < kDmaWaves of a chunk moves rows 4d .. 4d+3;
   // lane (sub, slot) fetches 16-byte column slot ^ swz(row) of row 4d + sub
   // into that row's slot (rows past NB - 1 re-read row NB - 1; never used).
-  // With 8 loader waves per chunk, waves 0-7 load the even chunks and waves
-  // 8-15 the odd ones; with 16, every wave loads one row group of each.
-  static_assert(kDmaWaves == 8 || kDmaWaves == 16, "loader waves per chunk");
+  // With 8 loader waves per chunk and 16 waves, waves 0-7 load the even
+  // chunks and waves 8-15 the odd ones; with as many loader waves as waves,
+  // every wave loads one row group of each chunk.
+  static_assert(kDmaWaves == WAVES || 2 * kDmaWaves == WAVES, "loader waves per chunk");
   const int dwave = wave % kDmaWaves;
   const int drow = 4 * dwave + (lane >> 4);
   const uint32_t dcol = static_cast<uint32_t>(((lane & 15) ^ swz(drow)) << 4);
   const int nit = nch1 + nch;  // pass 1 chunks, then pass 2 chunks
   auto stage = [&](int it) {
-    if ((kDmaWaves == kSelWaves || wave / kDmaWaves == (it & 1)) && it < nit) {
+    if ((kDmaWaves == WAVES || wave / kDmaWaves == (it & 1)) && it < nit) {
       const int j = min(it < nch1 ? R * (it * CH + drow) : (it - nch1) * CH + drow, s.NB - 1);
       dma16(kg, static_cast<uint32_t>(j) * kSelRowBytes + dcol,
             ring + (it % kSelSlots) * kSlotBytes + dwave * 1024);
@@ -457,13 +459,14 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_blocks_kernel(const uin
     }
     return;
   }
-  const int nIt = (nC + 63) / 64;  // candidate slots per lane (<= 32)
+  const int nIt = (nC + 63) / 64;  // candidate slots per lane (<= 32 with 16 waves, <= 64 with 8)
   if (nIt <= 1) topk_row<1>(sig + lo, nC, s.topk, lo, out, out_s, lane);
   else if (nIt <= 2) topk_row<2>(sig + lo, nC, s.topk, lo, out, out_s, lane);
   else if (nIt <= 4) topk_row<4>(sig + lo, nC, s.topk, lo, out, out_s, lane);
   else if (nIt <= 8) topk_row<8>(sig + lo, nC, s.topk, lo, out, out_s, lane);
   else if (nIt <= 16) topk_row<16>(sig + lo, nC, s.topk, lo, out, out_s, lane);
-  else topk_row<32>(sig + lo, nC, s.topk, lo, out, out_s, lane);
+  else if (WAVES == kSelWaves || nIt <= 32) topk_row<32>(sig + lo, nC, s.topk, lo, out, out_s, lane);
+  else if constexpr (WAVES != kSelWaves) topk_row<64>(sig + lo, nC, s.topk, lo, out, out_s, lane);
 }
 
 // One query per sequence (decode): the 16 waves of a workgroup share the
@@ -643,6 +646,12 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_decode_kernel(const uin
 template <int R>
 static hipError_t launch_select_r(const uint16_t* q, const uint16_t* k_cmp, int32_t* blk_idx, float* blk_score,
                                   const AttnShape& s, hipStream_t stream) {
+  if (select_lds<32>(s.NB) > kSelLdsMax) {  // 2049 .. 4064 blocks: 8-token workgroups
+    const dim3 grid8((s.S_q + kSelWideWaves - 1) / kSelWideWaves, s.B * s.H_kv);
+    hipLaunchKernelGGL((select_blocks_kernel<32, R, kSelWideWaves>), grid8, dim3(64 * kSelWideWaves),
+                       (select_lds<32, kSelWideWaves>(s.NB)), stream, q, k_cmp, blk_idx, blk_score, s);
+    return hipGetLastError();
+  }
   dim3 grid((s.S_q + kSelWaves - 1) / kSelWaves, s.B * s.H_kv);
   // 64-block chunks where the LDS holds them, else 32 (NB <= 2048 fits)
   if (select_lds<64>(s.NB) <= kSelLdsMax)
@@ -657,7 +666,8 @@ static hipError_t launch_select_r(const uint16_t* q, const uint16_t* k_cmp, int3
 hipError_t launch_select_blocks(const uint16_t* q, const uint16_t* k_cmp, int32_t* blk_idx,
                                 float* blk_score, const AttnShape& s, hipStream_t stream, int lse_stride) {
   if (s.B == 0 || s.S_q == 0) return hipSuccess;
-  if (s.S_q == 1 && lse_stride == 1) {  // one query per sequence: the workgroup splits its blocks
+  if (s.S_q == 1 && lse_stride == 1 && s.NB <= kSelWaves * kDecTiles * 16) {
+    // one query per sequence: the workgroup splits its blocks
     const size_t lds = (static_cast<size_t>(kSelWaves) * kMaxG * 2 + kMaxG + sel_stride(s.NB)) * sizeof(float);
     hipLaunchKernelGGL(select_decode_kernel, dim3(s.B * s.H_kv), dim3(64 * kSelWaves), lds, stream, q, k_cmp,
                        blk_idx, blk_score, s);
