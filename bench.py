@@ -429,8 +429,9 @@ def main():
                     help="only run the sparse attention backward this many times (for profiler runs)")
     ap.add_argument("--profile-kernels", type=int, default=0,
                     help="for counter runs: launch each kernel family of the path this many times at the "
-                         "workload's shape (compress, select, sparse attention, dense attention, backward) and "
-                         "the paged decode step (attention, combine, selection, append), then exit")
+                         "workload's shape (compress, select, sparse attention, dense attention, backward, the "
+                         "compressed branch alone and fused with the sparse attention) and the paged decode step "
+                         "(attention, combine, selection, append), then exit")
     ap.add_argument("--no-bwd", action="store_true", help="skip timing the sparse attention backward")
     ap.add_argument("--no-decode", action="store_true", help="skip timing the paged decode step")
     ap.add_argument("--no-compressed", action="store_true",
@@ -496,8 +497,13 @@ def main():
         dout = seeded_dout(q, torch)
         for _ in range(n):
             tb.sparse_attn_bwd(q, k, v, o, lse, dout, idx, wl.n_init, wl.n_local)
+        vc = tb.compress_v(v)
+        for _ in range(n):
+            tb.compressed_attn_fwd(q, kc, vc, wl.S_k, return_lse=False)
+        for _ in range(n):
+            tb.mixed_attn_fwd(q, k, v, idx, kc, vc, 0.5, 0.5, wl.n_init, wl.n_local, return_lse=False)
         torch.cuda.synchronize()
-        del o, lse, dout, idx, kc
+        del o, lse, dout, idx, kc, vc
         time_decode_paged(torch, tb, workloads, dev, reps=n)
         torch.cuda.synchronize()
         print(json.dumps({"profile_kernels_launches": n, "copy_bytes": 2 * a.numel()}))
