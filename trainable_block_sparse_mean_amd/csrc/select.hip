@@ -8,20 +8,21 @@
 // summary, Technical Mechanism).
 //
 // One workgroup = 16 consecutive query tokens of one KV head, one token per
-// wave.  The compressed keys stream through a 4-slot LDS ring of CH-block
-// chunks (direct-to-LDS loads: while a pair of chunks is read, the next pair
-// is in flight)
-// that all 16 waves read, so each chunk comes from L2 once per workgroup and
-// pass.  The chunks go in pairs, one barrier per pair.  For a token, S = Q k_cmp^T on 16x16x32 bf16 MFMAs puts the 16 heads
-// of the group in the rows and 16 compressed blocks in the columns: lane
-// (column hl, row quad gq) holds heads 4*gq .. 4*gq+3 of block 16*tile + hl.
+// wave (8 tokens and waves past 2048 key blocks).  The compressed keys stream
+// through a 4-slot LDS ring of CH-block chunks by direct-to-LDS loads, in
+// pairs: while one pair is read the next is in flight, one barrier per pair.
+// Every wave reads the same chunk, so each chunk comes from L2 once per
+// workgroup and pass.  For a token, S = Q k_cmp^T on 16x16x32 bf16 MFMAs puts
+// the 16 heads of the group in the rows and 16 compressed blocks in the
+// columns: lane (column hl, row quad gq) holds heads 4*gq .. 4*gq+3 of block
+// 16*tile + hl.
 //   pass 1: each lane keeps, per head, a running max (moved only when a
 //           score exceeds it by 2^8) and a sum of exp2 over its blocks; the 16
 //           lanes of a row are merged at the end -> per-head log-sum-exp
 //           (log2 units).
 //   pass 2: p = exp2(z - lse) per head, the group score of a block is the sum
-//           over the lane's 4 heads and the 4 row quads (two permlane swaps);
-//           it goes to LDS only, never to HBM.
+//           over the lane's 4 heads and the 4 row quads (permlane swaps); it
+//           goes to LDS only, never to HBM.
 // Heads beyond G (G < 16) have zero queries and an infinite log-sum-exp, so
 // they add exactly 0.  The top-k is an exact radix select on the fp32 bit
 // patterns (non-negative floats order like their bits); ties are then taken
