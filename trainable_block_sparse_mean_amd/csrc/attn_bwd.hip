@@ -207,8 +207,7 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(
 
   const uint32_t bit = 1u << (16 + wave);
   const BlockSrc<false> src{kg, vg, nullptr, s.NB, 0, s.H_kv, 0, 0, s.S_k};
-  // 4 of the 16 waves issue the pair loads (16 each): 2.6% faster than all 16
-  stream_pairs<kBwdDqWaves, true, 4>(smem, src, 0, nblk, entry_at, wave, lane,
+  stream_pairs<kBwdDqWaves, true>(smem, src, 0, nblk, entry_at, wave, lane,
                             [&](const unsigned char* const* stg, const int* js, uint32_t cur0, uint32_t cur1) {
                               // one copy of the item code for both blocks of the pair
 #pragma unroll 1
