@@ -67,6 +67,16 @@ __device__ __forceinline__ void lse_merge_row(float& m, float& l) {
   m = mn;
 }
 
+// Maximum (MAX) or sum over the 16 lanes of a DPP row, by rotations of 8, 4,
+// 2 and 1 lanes (dpp = row_ror control).  The maximum ends in every lane of
+// the row; the sum's association differs from lane to lane, so only one
+// lane's value is used.
+template <int DPP, bool MAX>
+__device__ __forceinline__ float row_reduce(float x) {
+  const float o = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), DPP, 0xf, 0xf, false));
+  return MAX ? fmaxf(x, o) : x + o;
+}
+
 // Radix search for the threshold of an exact top-kk over keys x[t] (slot t
 // of lane l holds a key, 0 where empty: every real key has a bit set).  From
 // the state (tt, bit, cnt): tt a prefix of the answer with bits above `bit`
@@ -475,19 +485,22 @@ __global__ __launch_bounds__(WAVES * 64) void select_blocks_kernel(const uint16_
 // on one selection.  Wave w scores the 16-block tiles [w*tpw, (w+1)*tpw), its
 // compressed keys loaded straight into the B operands (each block is read by
 // one wave only, so nothing is staged in LDS), and keeps the scores in
-// registers: the two passes become one pass over the keys.  The waves' (max,
-// sum) per head are merged in LDS into the exact log-sum-exp, each wave turns
-// its own scores into group scores in LDS, and wave 0 takes the top-k as the
-// token-per-wave kernel does.  Same lane layout as that kernel.
+// registers: the two passes become one pass over the keys.  The exact
+// per-head log-sum-exp is formed from each head's maximum over the workgroup
+// and then the sum of exp2 relative to it, both reduced through LDS; each
+// wave turns its own scores into group scores in LDS, and wave 0 takes the
+// top-k as the token-per-wave kernel does.  Same lane layout as that kernel.
 constexpr int kDecTiles = 8;  // tiles per wave: 16 waves x 8 x 16 blocks covers 2048 blocks
+constexpr int kDecQBytes = 4 * 64 * 16;  // the query's A operands, in lane order
 __global__ __launch_bounds__(kSelWaves * 64) void select_decode_kernel(const uint16_t* __restrict__ q,
                                                                        const uint16_t* __restrict__ kc,
                                                                        int32_t* __restrict__ blk_idx,
                                                                        float* __restrict__ blk_score, AttnShape s) {
   extern __shared__ __align__(16) unsigned char dec_smem[];
-  float* part = reinterpret_cast<float*>(dec_smem);              // max, then sum: [2][16 waves][16 heads]
-  float* lse_sh = part + kSelWaves * kMaxG * 2;                     // [16 heads]
-  float* sig = lse_sh + kMaxG;                                       // [NB]
+  unsigned char* qsh = dec_smem;                                     // the query's A operands: [4 k-steps][64 lanes] x 16 B
+  float* pmax = reinterpret_cast<float*>(dec_smem + kDecQBytes);     // [16 waves][16 heads]
+  float* psum = pmax + kSelWaves * kMaxG;                            // [16 waves][16 heads]
+  float* sig = psum + kSelWaves * kMaxG;                             // [NB]
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int hl = lane & 15, gq = lane >> 4;
@@ -509,30 +522,30 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_decode_kernel(const uin
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) kr[ks] = load16(krow + ks * 32);
   };
-  // the query and the first two tiles' keys are loaded together
+  // the first two tiles' keys are loaded first.  The query's A operands (lane:
+  // head hl, dims 8*gq + 32*ks) are the same for every wave: wave 0 loads them
+  // and passes them on through LDS in lane order, so the CU's memory path,
+  // which bounds this phase, carries the query once rather than once per wave.
   u32x4 kra[4], krb[4];
   if (tw0 < tend) kload(0, kra);
   if (tw0 + 1 < tend) kload(1, krb);
-  bf16x8 qa[4];
-  {
+  if (wave == 0) {
     const bool ok = hl < s.G;
     const uint16_t* qrow = q + (static_cast<size_t>(b * s.H_q + g * s.G + hl) * s.S_q) * kD + gq * 8;
     u32x4 raw[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) raw[ks] = ok ? load16(qrow + ks * 32) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qa[ks] = settle(as_bf16x8(raw[ks]));
+    for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<u32x4*>(qsh + (ks * 64 + lane) * 16) = raw[ks];
   }
+  __syncthreads();
+  bf16x8 qa[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) qa[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qsh + (ks * 64 + lane) * 16));
 
   // scores of this wave's tiles (log2 units); blocks >= nv are -inf.  Tiles go
   // in pairs, the next pair's keys loaded under the current pair's products.
   floatx4 z[kDecTiles];
-  float m[4], l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m[i] = -INFINITY;
-    l[i] = 0.f;
-  }
   auto score = [&](const u32x4 (&kr)[4], int t) {
     floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -554,59 +567,54 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_decode_kernel(const uin
       if (t + 3 < kDecTiles && tw0 + t + 3 < tend) kload(t + 3, krb);
     }
   }
+  // The exact per-head log-sum-exp, maximum first: the lane's tiles, the 16
+  // lanes of its row (which hold the head's other blocks), then the waves;
+  // then the sums of exp2 relative to that maximum, reduced the same way
+  // (lane 0 of a row writes its row's sum, waves added in order).  Every wave
+  // forms the result from the 16 waves' values in LDS.
+  float mx[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    mx[i] = -INFINITY;
 #pragma unroll
     for (int t = 0; t < kDecTiles; ++t)
-      if (t < tpw) m[i] = fmaxf(m[i], z[t][i]);  // tiles past tpw are -inf
-    if (m[i] != -INFINITY) {
+      if (t < tpw) mx[i] = fmaxf(mx[i], z[t][i]);  // tiles past tpw are -inf
+    mx[i] = row_reduce<0x128, true>(mx[i]);
+    mx[i] = row_reduce<0x124, true>(mx[i]);
+    mx[i] = row_reduce<0x122, true>(mx[i]);
+    mx[i] = row_reduce<0x121, true>(mx[i]);
+    if (hl == 0) pmax[wave * kMaxG + 4 * gq + i] = mx[i];
+  }
+  __syncthreads();
+  floatx4 hm = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    const floatx4 a = *reinterpret_cast<const floatx4*>(pmax + w * kMaxG + 4 * gq);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hm[i] = fmaxf(hm[i], a[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float sm = 0.f;
+    if (hm[i] != -INFINITY) {
 #pragma unroll
       for (int t = 0; t < kDecTiles; ++t)
-        if (t < tpw) l[i] += __builtin_amdgcn_exp2f(z[t][i] - m[i]);
+        if (t < tpw) sm += __builtin_amdgcn_exp2f(z[t][i] - hm[i]);
     }
-    // the 16 lanes of the row hold the same head's other blocks
-    lse_merge_row<0x128>(m[i], l[i]);
-    lse_merge_row<0x124>(m[i], l[i]);
-    lse_merge_row<0x122>(m[i], l[i]);
-    lse_merge_row<0x121>(m[i], l[i]);
-    if (hl == 0) {
-      part[wave * kMaxG + 4 * gq + i] = m[i];
-      part[(kSelWaves + wave) * kMaxG + 4 * gq + i] = l[i];
-    }
+    sm = row_reduce<0x128, false>(sm);
+    sm = row_reduce<0x124, false>(sm);
+    sm = row_reduce<0x122, false>(sm);
+    sm = row_reduce<0x121, false>(sm);
+    if (hl == 0) psum[wave * kMaxG + 4 * gq + i] = sm;
   }
   __syncthreads();
-  // wave 0 merges the waves' (max, sum) of each head (lane: its 4 heads; each
-  // wave's four values are one 16-byte read) into the log-sum-exp
-  if (wave == 0) {
-    floatx4 mm = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  floatx4 hs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < kSelWaves; ++w) {
-      const floatx4 a = *reinterpret_cast<const floatx4*>(part + w * kMaxG + 4 * gq);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mm[i] = fmaxf(mm[i], a[i]);
-    }
-    floatx4 ll = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < kSelWaves; ++w) {
-      const floatx4 a = *reinterpret_cast<const floatx4*>(part + w * kMaxG + 4 * gq);
-      const floatx4 c = *reinterpret_cast<const floatx4*>(part + (kSelWaves + w) * kMaxG + 4 * gq);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (a[i] != -INFINITY) ll[i] += c[i] * exp2f(a[i] - mm[i]);
-    }
-    if (hl == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)  // heads >= G add nothing
-        lse_sh[4 * gq + i] = 4 * gq + i < s.G && mm[i] != -INFINITY ? mm[i] + log2f(ll[i]) : INFINITY;
-    }
-  }
-  __syncthreads();
+  for (int w = 0; w < kSelWaves; ++w) hs += *reinterpret_cast<const floatx4*>(psum + w * kMaxG + 4 * gq);
   float lse2[4];
-  {
-    const floatx4 a = *reinterpret_cast<const floatx4*>(lse_sh + 4 * gq);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lse2[i] = a[i];
-  }
+  for (int i = 0; i < 4; ++i)  // heads >= G add nothing
+    lse2[i] = 4 * gq + i < s.G && hm[i] != -INFINITY ? hm[i] + log2f(hs[i]) : INFINITY;
   // group scores of this wave's blocks
 #pragma unroll
   for (int t = 0; t < kDecTiles; ++t) {
@@ -669,7 +677,7 @@ hipError_t launch_select_blocks(const uint16_t* q, const uint16_t* k_cmp, int32_
   if (s.B == 0 || s.S_q == 0) return hipSuccess;
   if (s.S_q == 1 && lse_stride == 1 && s.NB <= kSelWaves * kDecTiles * 16) {
     // one query per sequence: the workgroup splits its blocks
-    const size_t lds = (static_cast<size_t>(kSelWaves) * kMaxG * 2 + kMaxG + sel_stride(s.NB)) * sizeof(float);
+    const size_t lds = kDecQBytes + (static_cast<size_t>(kSelWaves) * kMaxG * 2 + sel_stride(s.NB)) * sizeof(float);
     hipLaunchKernelGGL(select_decode_kernel, dim3(s.B * s.H_kv), dim3(64 * kSelWaves), lds, stream, q, k_cmp,
                        blk_idx, blk_score, s);
     return hipGetLastError();
