@@ -185,6 +185,45 @@ def test_decode_full_size_b16_32k():
     log("  attention:", assert_attn_close(out, lse, ref_out, ref_lse, "decode b16 32k"))
 
 
+def test_decode_select_over_512_candidates():
+    """Sequences with more than 512 selection candidates take the top-k over
+    the whole workgroup (a shared digit histogram instead of one wave's radix
+    search); selection checked against the oracle at two top-k sizes."""
+    lens = [64 * 520 + 7, 65600, 131072, 100001]
+    c = paged_cache(lens, 16, 1, seed=17, spare_blocks=0, extra_pages=3)
+    k_cmp = compressed(c)
+    scale = 1 / math.sqrt(128)
+    q64, kc64 = np64(c["q"]), np64(k_cmp)
+    for topk in (64, 250):
+        idx = tb.decode_select(c["q"], k_cmp, c["lens"], topk)
+        torch.cuda.synchronize()
+        gidx = idx.cpu().numpy()
+        counts = dict(exact=0, near_tie=0)
+        for b, L in enumerate(lens):
+            ref_idx, scores = O.select_blocks(q64[b][None, :, None, :], kc64[b][None], L, topk, 1, 2, BS, scale,
+                                              return_scores=True)
+            cnt = check_selection(gidx[b][None, :, None, :], ref_idx, scores, [0], 1, L, topk, 1, 2)
+            for kk in counts:
+                counts[kk] += cnt[kk]
+        log("  top-%d selection rows:" % topk, counts)
+
+
+def test_decode_select_ties_over_512_candidates():
+    """Equal compressed keys give every candidate the same score: the kept
+    blocks are the lowest-index candidates, n_init .. n_init + topk - 1, with
+    more than 512 candidates (the whole-workgroup top-k) as with fewer."""
+    lens = [64 * 700, 64 * 1500 + 3, 64 * 300]
+    c = paged_cache(lens, 16, 1, seed=18, spare_blocks=0)
+    c["kp"].zero_()
+    idx, score = tb.decode_select(c["q"], compressed(c), c["lens"], 100, return_scores=True)
+    torch.cuda.synchronize()
+    expect = np.arange(1, 101, dtype=np.int32)
+    for b in range(len(lens)):
+        assert np.array_equal(idx[b, 0].cpu().numpy(), expect), b
+        sc = score[b, 0].cpu().numpy()
+        assert np.all(sc == sc[0]) and sc[0] > 0, b
+
+
 def test_decode_other_forced_blocks():
     """n_init = 0 and a 3-block window (the defaults elsewhere are 1 and 2)."""
     lens = [4000, 129, 2600, 64 * 30 + 1]

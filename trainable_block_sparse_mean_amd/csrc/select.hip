@@ -480,6 +480,112 @@ __global__ __launch_bounds__(WAVES * 64) void select_blocks_kernel(const uint16_
   else if constexpr (WAVES != kSelWaves) topk_row<64>(sig + lo, nC, s.topk, lo, out, out_s, lane);
 }
 
+// Exact top-kk of nC (<= 2 * 1024) candidates cand[0 .. nC) by all 16 waves
+// of a workgroup, with the same result as topk_row: keys are the fp32 bit
+// patterns with the sign cleared; the kk-th largest key T is found digit by
+// digit (bits 30..23, 22..15, 14..7, 6..0) from a shared 256-bin histogram of
+// the keys that match the digits found so far; the keys above T and the
+// first (lowest-index) ties at T are written to out[0 .. kk) in ascending
+// index order, their positions from workgroup-wide prefix counts.  Thread t
+// holds candidates t and t + 1024.  wsp: 304 words of LDS (the histogram,
+// the digits found and the number of ties still to take, the per-wave
+// counts of a prefix count).  Every thread of the workgroup calls this.
+__device__ __forceinline__ void block_topk(const float* cand, int nC, int kk, int first, int32_t* out,
+                                           float* out_s, uint32_t* wsp, int wave, int lane) {
+  constexpr int NT = kSelWaves * 64;
+  uint32_t* hist = wsp;        // [256]
+  uint32_t* ctl = wsp + 256;   // prefix, ties to take
+  uint32_t* wcnt = wsp + 256 + 16;  // [2][16 waves]
+  const int t = threadIdx.x;
+  uint32_t x[2];
+  bool v[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    v[u] = t + u * NT < nC;
+    x[u] = v[u] ? __float_as_uint(cand[t + u * NT]) & 0x7fffffffu : 0u;
+  }
+  uint32_t pre = 0u;
+  int need = kk;  // the answer is the need-th largest key with the digits found so far
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int sh = r < 3 ? 23 - 8 * r : 0;
+    const uint32_t dmask = r < 3 ? 0xffu : 0x7fu;
+    const uint32_t hmask = ~((1u << (sh + (r < 3 ? 8 : 7))) - 1u);  // the digits above this one
+    if (t < 256) hist[t] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (v[u] && (x[u] & hmask) == pre) atomicAdd(&hist[(x[u] >> sh) & dmask], 1u);
+    __syncthreads();
+    if (wave == 0) {
+      // lane: digits 4*lane .. 4*lane+3; c_i = keys with a digit >= 4*lane + i
+      const u32x4 h = *reinterpret_cast<const u32x4*>(hist + 4 * lane);
+      const uint32_t s4 = h[0] + h[1] + h[2] + h[3];
+      uint32_t suf = s4;  // sum over lanes >= this one
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = static_cast<uint32_t>(__shfl_down(static_cast<int>(suf), d, 64));
+        if (lane + d < 64) suf += o;
+      }
+      const uint32_t c3 = suf - s4 + h[3], c2 = c3 + h[2], c1 = c2 + h[1], c0 = c1 + h[0];
+      const uint32_t nd = static_cast<uint32_t>(need);
+      // the largest digit D with at least `need` keys at or above it
+      const int D = __popcll(__ballot(c0 >= nd)) + __popcll(__ballot(c1 >= nd)) + __popcll(__ballot(c2 >= nd)) +
+                    __popcll(__ballot(c3 >= nd)) - 1;
+      const int d1 = D + 1;  // keys with a larger digit: c_(d1 % 4) of lane d1 / 4 (none past the last digit)
+      const uint32_t mine = (d1 & 3) == 0 ? c0 : (d1 & 3) == 1 ? c1 : (d1 & 3) == 2 ? c2 : c3;
+      const uint32_t above = d1 < 256 ? static_cast<uint32_t>(__shfl(static_cast<int>(mine), d1 >> 2, 64)) : 0u;
+      if (lane == 0) {
+        ctl[0] = pre | (static_cast<uint32_t>(D) << sh);
+        ctl[1] = nd - above;
+      }
+    }
+    __syncthreads();
+    pre = ctl[0];
+    need = static_cast<int>(ctl[1]);
+  }
+  // positions in index order (candidates 0 .. 1023 by thread, then 1024 ..):
+  // workgroup-wide exclusive prefix counts of a flag
+  auto prefix = [&](bool f0, bool f1, int& r0, int& r1) {
+    const uint64_t b0 = __ballot(f0), b1 = __ballot(f1);
+    if (lane == 0) {
+      wcnt[wave] = static_cast<uint32_t>(__popcll(b0));
+      wcnt[kSelWaves + wave] = static_cast<uint32_t>(__popcll(b1));
+    }
+    __syncthreads();
+    int p0 = 0, all0 = 0, p1 = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+      const int c0 = static_cast<int>(wcnt[w]), c1 = static_cast<int>(wcnt[kSelWaves + w]);
+      all0 += c0;
+      if (w < wave) {
+        p0 += c0;
+        p1 += c1;
+      }
+    }
+    r0 = p0 + mask_rank(b0);
+    r1 = all0 + p1 + mask_rank(b1);
+    __syncthreads();  // the counts are free for the next prefix
+  };
+  bool eq[2], sel[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) eq[u] = v[u] && x[u] == pre;
+  int e0, e1;
+  prefix(eq[0], eq[1], e0, e1);
+  sel[0] = (v[0] && x[0] > pre) || (eq[0] && e0 < need);
+  sel[1] = (v[1] && x[1] > pre) || (eq[1] && e1 < need);
+  int q0, q1;
+  prefix(sel[0], sel[1], q0, q1);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int pos = u == 0 ? q0 : q1;
+    if (sel[u] && pos < kk) {
+      out[pos] = first + t + u * NT;
+      if (out_s) out_s[pos] = __uint_as_float(x[u]);
+    }
+  }
+}
+
 // One query per sequence (decode): the 16 waves of a workgroup share the
 // token and split its visible compressed blocks, so the whole workgroup works
 // on one selection.  Wave w scores the 16-block tiles [w*tpw, (w+1)*tpw), its
@@ -628,7 +734,7 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_decode_kernel(const uin
     }
   }
   __syncthreads();
-  if (wave != 0 || s.topk == 0) return;
+  if (s.topk == 0) return;
 
   const int qb = pos / kBS;
   const int lo = s.n_init;
@@ -637,19 +743,27 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_decode_kernel(const uin
   int32_t* out = blk_idx + static_cast<size_t>(b * s.H_kv + g) * s.S_q * s.topk;
   float* out_s = blk_score ? blk_score + static_cast<size_t>(b * s.H_kv + g) * s.S_q * s.topk : nullptr;
   if (nC <= s.topk) {
-    for (int e = lane; e < s.topk; e += 64) {
-      out[e] = e < nC ? lo + e : -1;
-      if (out_s) out_s[e] = e < nC ? sig[lo + e] : 0.f;
+    if (wave == 0) {
+      for (int e = lane; e < s.topk; e += 64) {
+        out[e] = e < nC ? lo + e : -1;
+        if (out_s) out_s[e] = e < nC ? sig[lo + e] : 0.f;
+      }
     }
     return;
   }
   const int nIt = (nC + 63) / 64;
+  if (nIt > 8) {
+    // more than 512 candidates: the whole workgroup (pmax / psum are free
+    // again).  At 16 sequences of 128k keys this took the kernel from 31.6
+    // to 27.4 us; at 512 candidates one wave's radix search is faster.
+    block_topk(sig + lo, nC, s.topk, lo, out, out_s, reinterpret_cast<uint32_t*>(pmax), wave, lane);
+    return;
+  }
+  if (wave != 0) return;
   if (nIt <= 1) topk_row<1>(sig + lo, nC, s.topk, lo, out, out_s, lane);
   else if (nIt <= 2) topk_row<2>(sig + lo, nC, s.topk, lo, out, out_s, lane);
   else if (nIt <= 4) topk_row<4>(sig + lo, nC, s.topk, lo, out, out_s, lane);
-  else if (nIt <= 8) topk_row<8>(sig + lo, nC, s.topk, lo, out, out_s, lane);
-  else if (nIt <= 16) topk_row<16>(sig + lo, nC, s.topk, lo, out, out_s, lane);
-  else topk_row<32>(sig + lo, nC, s.topk, lo, out, out_s, lane);
+  else topk_row<8>(sig + lo, nC, s.topk, lo, out, out_s, lane);
 }
 
 template <int R>
