@@ -179,6 +179,12 @@ __device__ __forceinline__ void topk_row(float* cand, int nC, int topk, int firs
       tt = a & ~((2u << bit) - 1u);
     }
   }
+  // The search state is the same in every lane; in scalar registers the
+  // rounds below are a scalar loop (otherwise the compiler keeps it in vector
+  // registers and runs the loop under an exec mask).
+  tt = __builtin_amdgcn_readfirstlane(tt);
+  bit = __builtin_amdgcn_readfirstlane(bit);
+  cnt = __builtin_amdgcn_readfirstlane(cnt);
   if constexpr (NS >= 8) {
     constexpr int S2 = NS / 4;
     constexpr int cap = 64 * S2;
