@@ -68,9 +68,10 @@ __device__ __forceinline__ void lse_merge_row(float& m, float& l) {
 }
 
 // Maximum (MAX) or sum over the 16 lanes of a DPP row, by rotations of 8, 4,
-// 2 and 1 lanes (dpp = row_ror control).  The maximum ends in every lane of
-// the row; the sum's association differs from lane to lane, so only one
-// lane's value is used.
+// 2 and 1 lanes (dpp = row_ror control).  Called with the four rotations in
+// that order, it leaves the result in every lane of the row, bit-identical:
+// each step combines two values that the lanes involved already agree on,
+// and both maximum and sum are commutative.
 template <int DPP, bool MAX>
 __device__ __forceinline__ float row_reduce(float x) {
   const float o = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), DPP, 0xf, 0xf, false));
@@ -384,14 +385,22 @@ __global__ __launch_bounds__(WAVES * 64) void select_blocks_kernel(const uint16_
   // its ring slot
   auto chunk = [&](int it) {
     if (it == nch1) {
-      // end of pass 1: merge the 16 lanes of each row (one head per register i)
+      // end of pass 1: merge the 16 lanes of each row (one head per register
+      // i), maximum first, then the lanes' sums rescaled to it: one
+      // exponential per head instead of two per merge step
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        lse_merge_row<0x128>(m[i], l[i]);
-        lse_merge_row<0x124>(m[i], l[i]);
-        lse_merge_row<0x122>(m[i], l[i]);
-        lse_merge_row<0x121>(m[i], l[i]);
-        lse2[i] = 4 * gq + i < s.G ? m[i] + log2f(l[i]) : INFINITY;
+        float mm = m[i];
+        mm = row_reduce<0x128, true>(mm);
+        mm = row_reduce<0x124, true>(mm);
+        mm = row_reduce<0x122, true>(mm);
+        mm = row_reduce<0x121, true>(mm);
+        float ll = m[i] == -INFINITY ? 0.f : l[i] * exp2f(m[i] - mm);
+        ll = row_reduce<0x128, false>(ll);
+        ll = row_reduce<0x124, false>(ll);
+        ll = row_reduce<0x122, false>(ll);
+        ll = row_reduce<0x121, false>(ll);
+        lse2[i] = 4 * gq + i < s.G ? mm + log2f(ll) : INFINITY;
       }
     }
     const unsigned char* buf = sel_smem + (it % kSelSlots) * kSlotBytes;
