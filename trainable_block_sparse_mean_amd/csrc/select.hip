@@ -320,8 +320,10 @@ __global__ __launch_bounds__(WAVES * 64) void select_blocks_kernel(const uint16_
   };
   // pass 1 update over NT tiles; masked scores (-inf) add nothing.  The
   // running max m (log2 units) only moves when a score exceeds it by more
-  // than kSelSlack (decided per wave), so most chunks need no rescaling; the
-  // sum stays below 2^8 per term.
+  // than kSelSlack (decided per wave), so most chunks need no rescaling (the
+  // branch is marked unlikely, or the compiler computes the rescale on every
+  // chunk); the sum stays below 2^8 per term.  Maxima are IEEE maximum
+  // (v_maximum3), which needs no quieting of its inputs first.
   auto lse_update = [&](const floatx4* acc, auto nt_c) {
     constexpr int NT = decltype(nt_c)::value;
     float mx[4];
@@ -330,14 +332,14 @@ __global__ __launch_bounds__(WAVES * 64) void select_blocks_kernel(const uint16_
     for (int i = 0; i < 4; ++i) {
       mx[i] = acc[0][i];
 #pragma unroll
-      for (int t = 1; t < NT; ++t) mx[i] = fmaxf(mx[i], acc[t][i]);
+      for (int t = 1; t < NT; ++t) mx[i] = __builtin_elementwise_maximum(mx[i], acc[t][i]);
       mx[i] *= sl2;
       need |= mx[i] > m[i] + kSelSlack;
     }
-    if (__ballot(need) != 0) {
+    if (__builtin_expect(__ballot(need) != 0, 0)) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float mn = fmaxf(m[i], mx[i]);
+        const float mn = __builtin_elementwise_maximum(m[i], mx[i]);
         l[i] = mn == -INFINITY ? 0.f : l[i] * __builtin_amdgcn_exp2f(m[i] - mn);
         m[i] = mn;
       }
