@@ -176,6 +176,16 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(
           dpa[x] = mfma_16x16x32(vf[x], df[ks], ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : dpa[x]);
         }
       }
+      // keys past the token (only in its own block): -inf scores, so p = 0.
+      // A branch marked unlikely: otherwise the compiler tests every key of
+      // every block.
+      if (__builtin_expect(need_mask, 0)) {
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (16 * (2 * s2 + x) + e > first) sacc[x][e] = -INFINITY;
+      }
       uint32_t w[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -184,8 +194,7 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(
 #pragma unroll
         for (int y = 0; y < 2; ++y) {
           const int e = e0 + y;
-          float p = __builtin_amdgcn_exp2f(fmaf(sacc[x][e], sl2, -lse2));
-          if (need_mask && 16 * (2 * s2 + x) + e > first) p = 0.f;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[x][e], sl2, -lse2));
           d2[y] = p * (dpa[x][e] - Dh);
         }
         w[c] = pack_bf16x2(d2[0], d2[1]);
