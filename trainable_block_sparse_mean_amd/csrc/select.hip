@@ -615,6 +615,7 @@ __device__ __forceinline__ void block_topk(const float* cand, int nC, int kk, in
 // top-k as the token-per-wave kernel does.  Same lane layout as that kernel.
 constexpr int kDecTiles = 8;  // tiles per wave: 16 waves x 8 x 16 blocks covers 2048 blocks
 constexpr int kDecQBytes = 4 * 64 * 16;  // the query's A operands, in lane order
+static_assert(2 * kSelWaves * kMaxG >= 256 + 16 + 2 * kSelWaves, "block_topk's words fit in pmax and psum");
 __global__ __launch_bounds__(kSelWaves * 64) void select_decode_kernel(const uint16_t* __restrict__ q,
                                                                        const uint16_t* __restrict__ kc,
                                                                        int32_t* __restrict__ blk_idx,
