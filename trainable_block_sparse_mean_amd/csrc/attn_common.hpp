@@ -271,6 +271,9 @@ template <int WAVES, bool FRESH_DMA = false, int ISSUERS = WAVES, typename Src, 
 __device__ __forceinline__ void stream_pairs(unsigned char* smem, const Src& src, int e_lo, int e_hi,
                                              Entry entry_at, int wave, int lane, F&& on_pair) {
   static_assert(kStages == 4, "two pairs of stages");
+  // the wave index in a scalar register: the stage addresses the loads write
+  // to (M0) are then scalar arithmetic, not a vector value read back per load
+  wave = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t ring = lds_addr(smem);
   const bool issuer = wave < ISSUERS;
   const DmaLane<ISSUERS> dl_kept = dma_lane<ISSUERS>(wave % ISSUERS, lane);
