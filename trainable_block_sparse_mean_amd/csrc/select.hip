@@ -8,7 +8,8 @@
 // summary, Technical Mechanism).
 //
 // One workgroup = 16 consecutive query tokens of one KV head, one token per
-// wave (8 tokens and waves past 2048 key blocks).  The compressed keys stream
+// wave (8 tokens and waves up to 512 key blocks, two workgroups per CU, and
+// past 2048 key blocks).  The compressed keys stream
 // through a 4-slot LDS ring of CH-block chunks by direct-to-LDS loads, in
 // pairs: while one pair is read the next is in flight, one barrier per pair.
 // Every wave reads the same chunk, so each chunk comes from L2 once per
@@ -48,9 +49,11 @@ template <int CH, int WAVES = kSelWaves>
 constexpr size_t select_lds(int NB) {
   return static_cast<size_t>(kSelSlots) * CH * kSelRowBytes + static_cast<size_t>(WAVES) * sel_stride(NB) * 4;
 }
-// Past 2048 blocks the score rows of 16 tokens no longer fit beside the ring:
-// workgroups of 8 tokens (8 waves) with 32-block chunks take up to 4064.
+// Workgroups of 8 tokens (8 waves): up to 512 blocks two of them (64-block
+// chunks) share a CU; past 2048 blocks, where the score rows of 16 tokens no
+// longer fit beside the ring, one of them (32-block chunks) takes up to 4064.
 constexpr int kSelWideWaves = 8;
+static_assert(select_lds<64, kSelWideWaves>(512) <= kSelLdsMax / 2, "two 8-token workgroups of 512 blocks fit");
 static_assert(select_lds<32, kSelWideWaves>(kMaxSparseBlocks) <= kSelLdsMax, "8 score rows of 4064 blocks fit");
 static_assert(select_lds<32>(2048) <= kSelLdsMax, "16 score rows of 2048 blocks fit");
 
@@ -230,9 +233,11 @@ __device__ __forceinline__ void topk_row(float* cand, int nC, int topk, int firs
 // infv2_select_blocks_strided_lse - pass 1 scores only every R-th visible
 // compressed block, each standing for the R blocks of its group (the last
 // group for its visible count), so it streams 1/R of the compressed keys.
-// WAVES: tokens per workgroup (16, or 8 past 2048 blocks).
-template <int CH, int R, int WAVES = kSelWaves>
-__global__ __launch_bounds__(WAVES * 64) void select_blocks_kernel(const uint16_t* __restrict__ q,
+// WAVES: tokens per workgroup (16 or 8).  MINB: workgroups a CU holds at
+// once (2 holds the registers of a wave to 128, so that two 8-wave
+// workgroups share a CU and one's top-k overlaps the other's passes).
+template <int CH, int R, int WAVES = kSelWaves, int MINB = 1>
+__global__ __launch_bounds__(WAVES * 64, MINB) void select_blocks_kernel(const uint16_t* __restrict__ q,
                                                                        const uint16_t* __restrict__ kc,
                                                                        int32_t* __restrict__ blk_idx,
                                                                        float* __restrict__ blk_score,
@@ -281,17 +286,23 @@ __global__ __launch_bounds__(WAVES * 64) void select_blocks_kernel(const uint16_
   // into that row's slot (rows past NB - 1 re-read row NB - 1; never used).
   // With 8 loader waves per chunk and 16 waves, waves 0-7 load the even
   // chunks and waves 8-15 the odd ones; with as many loader waves as waves,
-  // every wave loads one row group of each chunk.
-  static_assert(kDmaWaves == WAVES || 2 * kDmaWaves == WAVES, "loader waves per chunk");
+  // every wave loads one row group of each chunk; with 16 row groups and 8
+  // waves, wave d loads groups d and d + 8 (rows 32 further: same swizzle).
+  static_assert(kDmaWaves == WAVES || 2 * kDmaWaves == WAVES || kDmaWaves == 2 * WAVES, "loader waves per chunk");
   const int dwave = wave % kDmaWaves;
   const int drow = 4 * dwave + (lane >> 4);
   const uint32_t dcol = static_cast<uint32_t>(((lane & 15) ^ swz(drow)) << 4);
   const int nit = nch1 + nch;  // pass 1 chunks, then pass 2 chunks
   auto stage = [&](int it) {
-    if ((kDmaWaves == WAVES || wave / kDmaWaves == (it & 1)) && it < nit) {
+    if ((kDmaWaves >= WAVES || wave / kDmaWaves == (it & 1)) && it < nit) {
       const int j = min(it < nch1 ? R * (it * CH + drow) : (it - nch1) * CH + drow, s.NB - 1);
       dma16(kg, static_cast<uint32_t>(j) * kSelRowBytes + dcol,
             ring + (it % kSelSlots) * kSlotBytes + dwave * 1024);
+      if constexpr (kDmaWaves == 2 * WAVES) {
+        const int j2 = min(it < nch1 ? R * (it * CH + drow + 32) : (it - nch1) * CH + drow + 32, s.NB - 1);
+        dma16(kg, static_cast<uint32_t>(j2) * kSelRowBytes + dcol,
+              ring + (it % kSelSlots) * kSlotBytes + (dwave + WAVES) * 1024);
+      }
     }
   };
   // B-operand read offsets (row = block within the tile, k-step ks)
@@ -493,8 +504,8 @@ __global__ __launch_bounds__(WAVES * 64) void select_blocks_kernel(const uint16_
   else if (nIt <= 4) topk_row<4>(sig + lo, nC, s.topk, lo, out, out_s, lane);
   else if (nIt <= 8) topk_row<8>(sig + lo, nC, s.topk, lo, out, out_s, lane);
   else if (nIt <= 16) topk_row<16>(sig + lo, nC, s.topk, lo, out, out_s, lane);
-  else if (WAVES == kSelWaves || nIt <= 32) topk_row<32>(sig + lo, nC, s.topk, lo, out, out_s, lane);
-  else if constexpr (WAVES != kSelWaves) topk_row<64>(sig + lo, nC, s.topk, lo, out, out_s, lane);
+  else if (WAVES == kSelWaves || MINB > 1 || nIt <= 32) topk_row<32>(sig + lo, nC, s.topk, lo, out, out_s, lane);
+  else if constexpr (WAVES != kSelWaves && MINB == 1) topk_row<64>(sig + lo, nC, s.topk, lo, out, out_s, lane);
 }
 
 // Exact top-kk of nC (<= 2 * 1024) candidates cand[0 .. nC) by all 16 waves
@@ -787,20 +798,22 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_decode_kernel(const uin
 template <int R>
 static hipError_t launch_select_r(const uint16_t* q, const uint16_t* k_cmp, int32_t* blk_idx, float* blk_score,
                                   const AttnShape& s, hipStream_t stream) {
-  if (select_lds<32>(s.NB) > kSelLdsMax) {  // 2049 .. 4064 blocks: 8-token workgroups
-    const dim3 grid8((s.S_q + kSelWideWaves - 1) / kSelWideWaves, s.B * s.H_kv);
-    hipLaunchKernelGGL((select_blocks_kernel<32, R, kSelWideWaves>), grid8, dim3(64 * kSelWideWaves),
+  auto grid = [&](int tok) { return dim3((s.S_q + tok - 1) / tok, s.B * s.H_kv); };
+  if (select_lds<64, kSelWideWaves>(s.NB) <= kSelLdsMax / 2) {
+    // up to 512 blocks: 8-token workgroups, two per CU (32k: 0.329 -> 0.287 ms)
+    hipLaunchKernelGGL((select_blocks_kernel<64, R, kSelWideWaves, 2>), grid(kSelWideWaves),
+                       dim3(64 * kSelWideWaves), (select_lds<64, kSelWideWaves>(s.NB)), stream, q, k_cmp, blk_idx,
+                       blk_score, s);
+  } else if (select_lds<64>(s.NB) <= kSelLdsMax) {  // 16-token workgroups, 64-block chunks
+    hipLaunchKernelGGL((select_blocks_kernel<64, R>), grid(kSelWaves), dim3(64 * kSelWaves), select_lds<64>(s.NB),
+                       stream, q, k_cmp, blk_idx, blk_score, s);
+  } else if (select_lds<32>(s.NB) <= kSelLdsMax) {  // up to 2048 blocks: 32-block chunks
+    hipLaunchKernelGGL((select_blocks_kernel<32, R>), grid(kSelWaves), dim3(64 * kSelWaves), select_lds<32>(s.NB),
+                       stream, q, k_cmp, blk_idx, blk_score, s);
+  } else {  // 2049 .. 4064 blocks: 8-token workgroups, one per CU
+    hipLaunchKernelGGL((select_blocks_kernel<32, R, kSelWideWaves>), grid(kSelWideWaves), dim3(64 * kSelWideWaves),
                        (select_lds<32, kSelWideWaves>(s.NB)), stream, q, k_cmp, blk_idx, blk_score, s);
-    return hipGetLastError();
   }
-  dim3 grid((s.S_q + kSelWaves - 1) / kSelWaves, s.B * s.H_kv);
-  // 64-block chunks where the LDS holds them, else 32 (NB <= 2048 fits)
-  if (select_lds<64>(s.NB) <= kSelLdsMax)
-    hipLaunchKernelGGL((select_blocks_kernel<64, R>), grid, dim3(64 * kSelWaves), select_lds<64>(s.NB), stream, q,
-                       k_cmp, blk_idx, blk_score, s);
-  else
-    hipLaunchKernelGGL((select_blocks_kernel<32, R>), grid, dim3(64 * kSelWaves), select_lds<32>(s.NB), stream, q,
-                       k_cmp, blk_idx, blk_score, s);
   return hipGetLastError();
 }
 
