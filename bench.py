@@ -170,7 +170,8 @@ def seeded_dout(q, torch):
 def time_decode_paged(torch, tb, workloads, dev, reps=50):
     """One generation step of the decode workload (16 sequences, 32 q / 2 kv
     heads, top-64) over a paged cache: append the compressed key of any block
-    the new token completes, select, attend.  The 16 sequences hold 32768 - 37 b
+    the new token completes, then select and attend in one launch (also timed
+    as separate selection and attention calls).  The 16 sequences hold 32768 - 37 b
     keys (ragged) in 64-key pages handed out in a random order.  Returns
     {paged step ms, its parts, the contiguous path's step at one length}."""
     wl = workloads.DECODE_32K
@@ -196,7 +197,11 @@ def time_decode_paged(torch, tb, workloads, dev, reps=50):
     k_cmp = torch.zeros(B, H_kv, max_blocks, D, dtype=torch.bfloat16, device=dev)
     tb.decode_compress_append(kp, table, torch.zeros_like(cur), cur, k_cmp, max_blocks)
 
-    def step():
+    def step():  # selection and attention in one launch (infv2_decode_select_attn)
+        tb.decode_compress_append(kp, table, cur, nxt, k_cmp, 1)
+        return tb.decode_select_attn(q, k_cmp, kp, vp, table, nxt, wl.topk, wl.n_init, wl.n_local)
+
+    def step_three_calls():  # the same step through the separate selection and attention calls
         tb.decode_compress_append(kp, table, cur, nxt, k_cmp, 1)
         idx = tb.decode_select(q, k_cmp, nxt, wl.topk, wl.n_init, wl.n_local)
         return tb.decode_attn(q, kp, vp, table, nxt, idx, wl.n_init, wl.n_local)
@@ -229,10 +234,13 @@ def time_decode_paged(torch, tb, workloads, dev, reps=50):
         graph_ms = f"capture failed: {e}"
 
     res = {"paged_step_ms": timed(step, reps),
+           "paged_step_three_calls_ms": timed(step_three_calls, reps),
            "append_ms": timed(lambda: tb.decode_compress_append(kp, table, cur, nxt, k_cmp, 1), reps)}
     idx = tb.decode_select(q, k_cmp, nxt, wl.topk, wl.n_init, wl.n_local)
     res["select_ms"] = timed(lambda: tb.decode_select(q, k_cmp, nxt, wl.topk, wl.n_init, wl.n_local), reps)
     res["attn_ms"] = timed(lambda: tb.decode_attn(q, kp, vp, table, nxt, idx, wl.n_init, wl.n_local), reps)
+    res["select_attn_fused_ms"] = timed(
+        lambda: tb.decode_select_attn(q, k_cmp, kp, vp, table, nxt, wl.topk, wl.n_init, wl.n_local), reps)
     # the contiguous path at one length (every sequence 32768 keys): it
     # compresses the whole cache each step
     x = workloads.make_inputs(wl)

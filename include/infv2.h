@@ -307,6 +307,23 @@ int infv2_decode_attn(const void* q, const void* k_pages, const void* v_pages,
                       float softmax_scale,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* infv2_decode_select followed by infv2_decode_attn, in one launch (plus the
+ * merge of the split partials): the same blk_idx and blk_score (blk_score
+ * may be null), out and lse (may be null), bit for bit.  Each of the
+ * workgroups that share a sequence's KV head repeats that head's selection
+ * on its own CU and attends its share of the selected blocks at once, so
+ * the selection's result never goes through device memory on its way to the
+ * attention.  Same arguments and limits as those two calls (max_blocks <=
+ * 2048); workspace as for infv2_decode_attn. */
+int infv2_decode_select_attn(const void* q, const void* k_cmp, const void* k_pages,
+                             const void* v_pages, const int32_t* block_table,
+                             const int32_t* seqlens, int32_t* blk_idx, float* blk_score,
+                             void* out, float* lse,
+                             int B, int H_q, int H_kv, int D, int block_size,
+                             int max_blocks, int num_pages, int topk, int n_init, int n_local,
+                             float softmax_scale,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Compressed-attention branch and the mix of patterns (skill page, Step 2,
  * compressed_attention: queries attend block means of the keys and values;

@@ -35,7 +35,7 @@ def test_header_declares_expected_entry_points():
               "infv2_attn_fwd", "infv2_sparse_attn_bwd", "infv2_status_string", "infv2_decode_compress_append",
               "infv2_decode_select", "infv2_decode_attn", "infv2_compress_v", "infv2_compressed_attn_fwd",
               "infv2_decode_compressed_attn", "infv2_mixed_attn_fwd", "infv2_attn_path",
-              "infv2_attn_fwd_noalloc"]:
+              "infv2_attn_fwd_noalloc", "infv2_decode_select_attn"]:
         assert n in names
 
 
@@ -200,6 +200,38 @@ def _dec_attn(lib, **kw):
     return lib.infv2_decode_attn(a["q"], a["kp"], a["vp"], a["table"], a["lens"], a["idx"], a["out"], a["lse"],
                                  a["B"], a["H_q"], a["H_kv"], a["D"], a["bs"], a["max_blocks"], a["num_pages"],
                                  a["topk"], a["n_init"], a["n_local"], a["scale"], a["ws"], a["wsb"], a["stream"])
+
+
+def _dec_fused(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, kp=FAKE, vp=FAKE, table=FAKE, lens=FAKE, idx=FAKE, score=None, out=FAKE, lse=FAKE,
+             B=16, H_q=32, H_kv=2, D=128, bs=64, max_blocks=512, num_pages=8192, topk=64, n_init=1, n_local=2,
+             scale=0.0, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.infv2_decode_select_attn(a["q"], a["kc"], a["kp"], a["vp"], a["table"], a["lens"], a["idx"],
+                                        a["score"], a["out"], a["lse"], a["B"], a["H_q"], a["H_kv"], a["D"], a["bs"],
+                                        a["max_blocks"], a["num_pages"], a["topk"], a["n_init"], a["n_local"],
+                                        a["scale"], a["ws"], a["wsb"], a["stream"])
+
+
+@no_gpu
+def test_decode_select_attn_validation_codes():
+    """The fused decode call refuses what the selection or the attention
+    call would refuse, before any launch."""
+    lib = tb.load_library()
+    assert _dec_fused(lib, H_q=31) == tb.ERR_INVALID               # H_q % H_kv
+    assert _dec_fused(lib, kc=None) == tb.ERR_INVALID
+    assert _dec_fused(lib, table=None) == tb.ERR_INVALID
+    assert _dec_fused(lib, lens=FAKE + 2) == tb.ERR_INVALID        # int32 arrays must be 4-byte aligned
+    assert _dec_fused(lib, idx=None) == tb.ERR_INVALID             # topk > 0 needs the selection's output
+    assert _dec_fused(lib, score=FAKE + 4) == tb.ERR_INVALID       # scores must be 16-byte aligned
+    assert _dec_fused(lib, num_pages=0) == tb.ERR_INVALID
+    assert _dec_fused(lib, n_local=0) == tb.ERR_INVALID
+    assert _dec_fused(lib, D=64) == tb.ERR_UNSUPPORTED
+    assert _dec_fused(lib, max_blocks=2049) == tb.ERR_UNSUPPORTED  # the decode selection's limit
+    assert _dec_fused(lib, topk=257) == tb.ERR_UNSUPPORTED
+    assert _dec_fused(lib, ws=None) == tb.ERR_WORKSPACE
+    assert _dec_fused(lib, wsb=1024) == tb.ERR_WORKSPACE
+    assert _dec_fused(lib, B=0) == tb.OK
 
 
 @no_gpu

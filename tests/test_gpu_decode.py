@@ -245,3 +245,44 @@ def test_decode_other_forced_blocks():
         ob, lb = O.sparse_attn(qb, kb, vb, gidx[b][None, :, None, :], BS, 0, 3, scale)
         ref_out[b], ref_lse[b] = ob[0, :, 0], lb[0, :, 0]
     log("  n_init 0, n_local 3:", assert_attn_close(out, lse, ref_out, ref_lse, "decode forced blocks"))
+
+
+FUSED_CASES = LEN_CASES + [
+    ("b16_32k", [32768 - 37 * b for b in range(16)], 32, 2, 64),
+    ("over_512_candidates", [64 * 520 + 7, 65600, 131072, 100001], 16, 1, 250),
+    ("topk0", [3000, 70, 129], 8, 2, 0),
+]
+
+
+@pytest.mark.parametrize("name,lens,H_q,H_kv,topk", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_decode_select_attn_fused_equals_two_calls(name, lens, H_q, H_kv, topk):
+    """infv2_decode_select_attn (selection and attention in one launch) gives
+    bit for bit the indices, scores, outputs and LSE of infv2_decode_select
+    followed by infv2_decode_attn (which the tests above check against the
+    oracle), and the same bits again on a second call."""
+    log("decode fused", name, lens[:4], "topk", topk)
+    c = paged_cache(lens, H_q, H_kv, seed=21, extra_pages=8, spare_blocks=0 if max(lens) > 64 * 2040 else 2)
+    k_cmp = compressed(c)
+    if topk > 0:
+        idx, score = tb.decode_select(c["q"], k_cmp, c["lens"], topk, return_scores=True)
+    else:
+        idx = torch.empty(len(lens), H_kv, 0, dtype=torch.int32, device=DEV)
+    out, lse = tb.decode_attn(c["q"], c["kp"], c["vp"], c["table"], c["lens"], idx)
+    runs = [tb.decode_select_attn(c["q"], k_cmp, c["kp"], c["vp"], c["table"], c["lens"], topk, return_scores=True)
+            for _ in range(2)]
+    torch.cuda.synchronize()
+    for fo, fl, fi, fs in runs:
+        assert np.array_equal(bits_np(fo), bits_np(out))
+        assert torch.equal(fl, lse)
+        if topk > 0:
+            assert torch.equal(fi, idx)
+            assert torch.equal(fs, score)
+    for n in (4, 5):  # the other forced blocks
+        if topk == 0:
+            break
+        i2 = tb.decode_select(c["q"], k_cmp, c["lens"], topk, n_init=n - 4, n_local=n - 2)
+        o2, l2 = tb.decode_attn(c["q"], c["kp"], c["vp"], c["table"], c["lens"], i2, n_init=n - 4, n_local=n - 2)
+        fo, fl, fi = tb.decode_select_attn(c["q"], k_cmp, c["kp"], c["vp"], c["table"], c["lens"], topk,
+                                           n_init=n - 4, n_local=n - 2)
+        torch.cuda.synchronize()
+        assert torch.equal(fi, i2) and torch.equal(fl, l2) and np.array_equal(bits_np(fo), bits_np(o2))

@@ -52,7 +52,8 @@ def test_decode_step_graph_replays_match_eager():
         idx = tb.decode_select(c["q"], k_cmp, nxt, 16)
         out, lse = tb.decode_attn(c["q"], c["kp"], c["vp"], c["table"], nxt, idx)
         mixed, _ = tb.decode_compressed_attn(c["q"], k_cmp, v_cmp, nxt, o_sparse=out, w_sparse=0.75, w_cmp=0.25)
-        return idx, out, lse, mixed
+        fo, fl, fi = tb.decode_select_attn(c["q"], k_cmp, c["kp"], c["vp"], c["table"], nxt, 16)
+        return idx, out, lse, mixed, fo, fl, fi
 
     eager = [t.clone() for t in step()]
     g, outs = capture(step)
@@ -62,7 +63,7 @@ def test_decode_step_graph_replays_match_eager():
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for name, got, want in zip(("idx", "out", "lse", "mixed"), outs, eager):
+        for name, got, want in zip(("idx", "out", "lse", "mixed", "fused out", "fused lse", "fused idx"), outs, eager):
             assert torch.equal(got, want), f"replay {rep}: {name} differs from the eager step"
         # eager work between replays
         tb.decode_select(c["q"], k_cmp, nxt, 8)

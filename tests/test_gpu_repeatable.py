@@ -74,8 +74,9 @@ def test_paged_decode_entry_points_repeat_bitwise():
         idx = tb.decode_select(c["q"], k_cmp, nxt, 16)
         out, lse = tb.decode_attn(c["q"], c["kp"], c["vp"], c["table"], nxt, idx)
         mixed, mlse = tb.decode_compressed_attn(c["q"], k_cmp, v_cmp, nxt, o_sparse=out, w_sparse=0.7, w_cmp=0.3)
+        fo, fl, fi = tb.decode_select_attn(c["q"], k_cmp, c["kp"], c["vp"], c["table"], nxt, 16)
         torch.cuda.synchronize()
-        return [t.clone() for t in (k_cmp, v_cmp, idx, out, lse, mixed, mlse)]
+        return [t.clone() for t in (k_cmp, v_cmp, idx, out, lse, mixed, mlse, fo, fl, fi)]
 
     first = run()
     for _ in range(2):

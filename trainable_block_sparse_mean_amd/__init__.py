@@ -48,6 +48,7 @@ SIGNATURES = {
     "infv2_decode_select": (_c_int, [_vp] * 5 + [_c_int] * 9 + [_c_float, _vp]),
     "infv2_decode_attn_workspace_bytes": (_c_size, [_c_int] * 7),
     "infv2_decode_attn": (_c_int, [_vp] * 8 + [_c_int] * 10 + [_c_float, _vp, _c_size, _vp]),
+    "infv2_decode_select_attn": (_c_int, [_vp] * 10 + [_c_int] * 10 + [_c_float, _vp, _c_size, _vp]),
     "infv2_compress_v": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
     "infv2_compressed_attn_fwd": (_c_int, [_vp] * 6 + [_c_int] * 7 + [_c_float] * 3 + [_vp]),
     "infv2_decode_compressed_attn": (_c_int, [_vp] * 7 + [_c_int] * 6 + [_c_float] * 3 + [_vp]),
@@ -271,6 +272,34 @@ def decode_attn(q, k_pages, v_pages, block_table, seqlens, blk_idx, n_init: int 
           _ptr(blk_idx), _ptr(out), _ptr(lse), B, H_q, H_kv, D, block_size, max_blocks, num_pages, topk, n_init,
           n_local, _scale(softmax_scale), _ptr(ws), ws.numel(), _stream())
     return out, lse
+
+
+def decode_select_attn(q, k_cmp, k_pages, v_pages, block_table, seqlens, topk: int, n_init: int = 1,
+                       n_local: int = 2, softmax_scale=None, block_size: int = 64, return_scores: bool = False):
+    """decode_select then decode_attn in one launch (the same results).
+    Returns (out bf16 [B,H_q,D], lse fp32 [B,H_q], blk_idx int32 [B,H_kv,topk]
+    [, blk_score fp32 [B,H_kv,topk]])."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cmp, "k_cmp", torch.bfloat16, 4)
+    for t, n in ((k_pages, "k_pages"), (v_pages, "v_pages")):
+        _need(t, n, torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seqlens, "seqlens", torch.int32, 1)
+    B, H_q, D = q.shape
+    num_pages, H_kv = k_pages.shape[0], k_pages.shape[1]
+    max_blocks = block_table.shape[1]
+    if k_cmp.shape[2] != max_blocks:
+        raise ValueError("k_cmp and block_table must hold the same number of blocks per sequence")
+    idx = torch.empty(B, H_kv, topk, dtype=torch.int32, device=q.device)
+    score = torch.empty(B, H_kv, topk, dtype=torch.float32, device=q.device) if return_scores else None
+    out = torch.empty_like(q)
+    lse = torch.empty(B, H_q, dtype=torch.float32, device=q.device)
+    nbytes = load_library().infv2_decode_attn_workspace_bytes(B, H_q, H_kv, D, block_size, max_blocks, topk)
+    ws = _workspace(nbytes, q.device)
+    _call("infv2_decode_select_attn", _ptr(q), _ptr(k_cmp), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+          _ptr(seqlens), _ptr(idx), _ptr(score), _ptr(out), _ptr(lse), B, H_q, H_kv, D, block_size, max_blocks,
+          num_pages, topk, n_init, n_local, _scale(softmax_scale), _ptr(ws), ws.numel(), _stream())
+    return (out, lse, idx, score) if return_scores else (out, lse, idx)
 
 
 def compress_v(v: torch.Tensor, block_size: int = 64) -> torch.Tensor:

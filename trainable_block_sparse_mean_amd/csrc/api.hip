@@ -19,7 +19,7 @@ constexpr int kMaxTopk = 256;
 // prefill queries (as many as the sparse kernels take), 2048 for one-query
 // decode selection (a wave holds at most 8 tiles of 16 blocks).
 constexpr int kMaxSelectBlocks = infv2::kMaxSparseBlocks;
-constexpr int kMaxDecodeSelectBlocks = 2048;
+using infv2::kMaxDecodeSelectBlocks;
 // the sparse kernels keep a member mask and a list entry (8 bytes) per key
 // block in LDS beside the 128 KB K/V ring (kernels.hpp)
 using infv2::kMaxSparseBlocks;
@@ -455,6 +455,34 @@ int infv2_decode_attn(const void* q, const void* k_pages, const void* v_pages, c
   return hip_status(infv2::launch_sparse_attn(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pages), static_cast<const uint16_t*>(v_pages),
       blk_idx, static_cast<uint16_t*>(out), lse, s, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int infv2_decode_select_attn(const void* q, const void* k_cmp, const void* k_pages, const void* v_pages,
+                             const int32_t* block_table, const int32_t* seqlens, int32_t* blk_idx, float* blk_score,
+                             void* out, float* lse, int B, int H_q, int H_kv, int D, int block_size, int max_blocks,
+                             int num_pages, int topk, int n_init, int n_local, float softmax_scale, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  int st = check_decode(B, H_q, H_kv, D, block_size, max_blocks);
+  if (st != INFV2_OK) return st;
+  st = check_sparse_params(block_size, topk, n_init, n_local);
+  if (st != INFV2_OK) return st;
+  if (max_blocks > kMaxDecodeSelectBlocks) return INFV2_ERR_UNSUPPORTED;
+  if (num_pages < 1) return INFV2_ERR_INVALID;
+  if (B == 0) return INFV2_OK;
+  if (!tensor_ok(q) || !tensor_ok(k_cmp) || !tensor_ok(k_pages) || !tensor_ok(v_pages) || !tensor_ok(out) ||
+      !ints_ok(block_table) || !ints_ok(seqlens))
+    return INFV2_ERR_INVALID;
+  if (topk > 0 && !tensor_ok(blk_idx)) return INFV2_ERR_INVALID;
+  if ((blk_score && !aligned(blk_score, 16)) || (lse && !aligned(lse, 16))) return INFV2_ERR_INVALID;
+  const size_t need = infv2_decode_attn_workspace_bytes(B, H_q, H_kv, D, block_size, max_blocks, topk);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return INFV2_ERR_WORKSPACE;
+  if (workspace && !aligned(workspace, 256)) return INFV2_ERR_INVALID;
+  const AttnShape s = decode_shape(B, H_q, H_kv, max_blocks, topk, n_init, n_local, scale_log2(softmax_scale, D),
+                                   seqlens, block_table, num_pages);
+  return hip_status(infv2::launch_decode_select_attn(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cmp), static_cast<const uint16_t*>(k_pages),
+      static_cast<const uint16_t*>(v_pages), blk_idx, blk_score, static_cast<uint16_t*>(out), lse, s, workspace,
+      static_cast<hipStream_t>(stream)));
 }
 
 int infv2_compress_v(const void* v, void* v_cmp, int B, int H_kv, int S_k, int D, int block_size, void* stream) {

@@ -13,6 +13,9 @@ namespace infv2 {
 // and the window's union list (8 bytes per block, plus 16) fit in the 160 KB
 // of LDS of a workgroup.
 constexpr int kMaxSparseBlocks = 4064;
+// Key blocks of a decode sequence (one query) the decode selection takes: 16
+// waves of 8 tiles of 16 blocks hold every score in registers.
+constexpr int kMaxDecodeSelectBlocks = 2048;
 
 struct AttnShape {
   int B, H_q, H_kv, S_q, S_k, G, NB;
@@ -77,6 +80,17 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16
                               const int32_t* blk_idx, uint16_t* out, float* lse,
                               const AttnShape& s, void* workspace, hipStream_t stream);
 
+// merge the split-KV partials of the sparse kernels (s.nsplit splits) into
+// out and lse
+hipError_t launch_combine_splits(const float* part, uint16_t* out, float* lse, const AttnShape& s,
+                                 hipStream_t stream);
+// Decode (one query per sequence and KV head, S_q = 1, at most 2048 key
+// blocks): the exact selection and the block-sparse attention in one launch
+// (plus the merge of the split partials); blk_idx [B][H_kv][1][topk] (and
+// blk_score, if not null) receive the selection.
+hipError_t launch_decode_select_attn(const uint16_t* q, const uint16_t* k_cmp, const uint16_t* k, const uint16_t* v,
+                                     int32_t* blk_idx, float* blk_score, uint16_t* out, float* lse,
+                                     const AttnShape& s, void* workspace, hipStream_t stream);
 hipError_t launch_dense_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                              uint16_t* out, float* lse, const AttnShape& s, void* workspace,
                              hipStream_t stream);

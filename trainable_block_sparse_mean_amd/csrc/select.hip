@@ -31,6 +31,7 @@
 // ballot.
 #include <type_traits>
 
+#include "attn_common.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -627,11 +628,14 @@ __device__ __forceinline__ void block_topk(const float* cand, int nC, int kk, in
 constexpr int kDecTiles = 8;  // tiles per wave: 16 waves x 8 x 16 blocks covers 2048 blocks
 constexpr int kDecQBytes = 4 * 64 * 16;  // the query's A operands, in lane order
 static_assert(2 * kSelWaves * kMaxG >= 256 + 16 + 2 * kSelWaves, "block_topk's words fit in pmax and psum");
-__global__ __launch_bounds__(kSelWaves * 64) void select_decode_kernel(const uint16_t* __restrict__ q,
-                                                                       const uint16_t* __restrict__ kc,
-                                                                       int32_t* __restrict__ blk_idx,
-                                                                       float* __restrict__ blk_score, AttnShape s) {
-  extern __shared__ __align__(16) unsigned char dec_smem[];
+// The selection of (batch, KV head) bgi's one query, for a workgroup of 16
+// waves, with dec_smem its LDS (decode_select_lds bytes); the kk indices and
+// scores go to out / out_s (device or LDS memory; out_s may be null).  Every
+// thread calls it; it ends without a barrier (only wave 0 writes the result
+// when a wave's search takes the top-k).
+__device__ __forceinline__ void select_decode_body(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+                                                   int32_t* out, float* out_s, const AttnShape& s, int bgi,
+                                                   unsigned char* dec_smem) {
   unsigned char* qsh = dec_smem;                                     // the query's A operands: [4 k-steps][64 lanes] x 16 B
   float* pmax = reinterpret_cast<float*>(dec_smem + kDecQBytes);     // [16 waves][16 heads]
   float* psum = pmax + kSelWaves * kMaxG;                            // [16 waves][16 heads]
@@ -639,8 +643,8 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_decode_kernel(const uin
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int hl = lane & 15, gq = lane >> 4;
-  const int g = blockIdx.x % s.H_kv;
-  const int b = blockIdx.x / s.H_kv;
+  const int g = bgi % s.H_kv;
+  const int b = bgi / s.H_kv;
   const int pos = seq_keys(s, b) - 1;      // the query is the last key
   const int nv = (pos + 1) / kBS;          // fully visible blocks
   const int ntile = (nv + 15) / 16;
@@ -769,8 +773,6 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_decode_kernel(const uin
   const int lo = s.n_init;
   const int hi = qb - s.n_local;
   const int nC = hi >= lo ? hi - lo + 1 : 0;
-  int32_t* out = blk_idx + static_cast<size_t>(b * s.H_kv + g) * s.S_q * s.topk;
-  float* out_s = blk_score ? blk_score + static_cast<size_t>(b * s.H_kv + g) * s.S_q * s.topk : nullptr;
   if (nC <= s.topk) {
     if (wave == 0) {
       for (int e = lane; e < s.topk; e += 64) {
@@ -793,6 +795,144 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_decode_kernel(const uin
   else if (nIt <= 2) topk_row<2>(sig + lo, nC, s.topk, lo, out, out_s, lane);
   else if (nIt <= 4) topk_row<4>(sig + lo, nC, s.topk, lo, out, out_s, lane);
   else topk_row<8>(sig + lo, nC, s.topk, lo, out, out_s, lane);
+}
+
+__host__ __device__ constexpr size_t decode_select_lds(int NB) {
+  return kDecQBytes + (static_cast<size_t>(kSelWaves) * kMaxG * 2 + sel_stride(NB)) * sizeof(float);
+}
+
+__global__ __launch_bounds__(kSelWaves * 64) void select_decode_kernel(const uint16_t* __restrict__ q,
+                                                                       const uint16_t* __restrict__ kc,
+                                                                       int32_t* __restrict__ blk_idx,
+                                                                       float* __restrict__ blk_score, AttnShape s) {
+  extern __shared__ __align__(16) unsigned char dec_smem[];
+  const size_t row = static_cast<size_t>(blockIdx.x) * s.S_q * s.topk;
+  select_decode_body(q, kc, blk_idx + row, blk_score ? blk_score + row : nullptr, s, blockIdx.x, dec_smem);
+}
+
+// ---------------------------------------------------------------------------
+// Decode selection and block-sparse attention in one launch (news summary,
+// Performance Evaluation: the method also serves decoding).  Workgroup
+// (bg, split) first selects the top-k blocks of (batch, KV head) bg exactly
+// as select_decode_kernel does, into LDS: the nsplit workgroups of bg repeat
+// that selection, each on its own CU, rather than wait for a separate launch
+// on 32 CUs and read its result back.  Then it attends split `split` of the
+// token's union of blocks, as the split-KV sparse kernel does (the same item
+// code, list and partials), and split 0 also stores the selection for the
+// caller.  LDS: the 4-stage ring, the union list, then the top-k (indices and
+// scores); the selection's own scratch overlays the ring.
+// ---------------------------------------------------------------------------
+static_assert(decode_select_lds(kMaxDecodeSelectBlocks) <= static_cast<size_t>(kStages) * kStageBytes,
+              "the selection's scratch fits in the ring");
+
+template <bool PAGED>
+__global__ __launch_bounds__(kSelWaves * 64, 1) void decode_select_attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int32_t* __restrict__ blk_idx, float* __restrict__ blk_score,
+    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part, AttnShape s) {
+  extern __shared__ __align__(1024) unsigned char smem[];
+  const size_t list_off = static_cast<size_t>(kStages) * kStageBytes;
+  uint32_t* bmask = reinterpret_cast<uint32_t*>(smem + list_off);  // [NB]
+  int* blist = reinterpret_cast<int*>(bmask + s.NB);                // [NB]
+  int* n_list = blist + s.NB;
+  int32_t* tk = reinterpret_cast<int32_t*>(smem + list_off + sparse_list_bytes(s.NB));  // [topk]
+  float* ts = reinterpret_cast<float*>(tk + s.topk);                                     // [topk]
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int hl = lane & 15, gq = lane >> 4;
+  const int bg_i = blockIdx.x;
+  const int g = bg_i % s.H_kv;
+  const int b = bg_i / s.H_kv;
+  const int split = blockIdx.y;
+
+  // ---- the selection, into LDS ----------------------------------------------
+  if (s.topk > 0) select_decode_body(q, kc, tk, ts, s, bg_i, smem);
+  __syncthreads();
+  if (split == 0) {
+    const size_t row = static_cast<size_t>(bg_i) * s.topk;  // one query row
+    for (int e = threadIdx.x; e < s.topk; e += kSelWaves * 64) {
+      blk_idx[row + e] = tk[e];
+      if (blk_score) blk_score[row + e] = ts[e];
+    }
+  }
+
+  // ---- this split's share of the token's blocks ------------------------------
+  const int S_k = seq_keys(s, b);
+  const int off = S_k - 1;  // the query is the last key
+  const int qb = off / kBS;
+  const uint16_t* kg = PAGED ? k : k + static_cast<size_t>(bg_i) * s.S_k * kD;
+  const uint16_t* vg = PAGED ? v : v + static_cast<size_t>(bg_i) * s.S_k * kD;
+  const BlockSrc<PAGED> src{kg, vg, s.block_table, s.NB, s.num_pages, s.H_kv, b, g, S_k};
+  const float sl2 = s.scale_log2;
+  SparseState st;  // wave 0 holds the token; the other waves only stream
+  {
+    const bool valid = wave == 0 && hl < s.G;
+    const uint16_t* qrow = q + (static_cast<size_t>(b * s.H_q + g * s.G + hl) * s.S_q) * kD + gq * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) st.qf[ks] = valid ? as_bf16x8(load16(qrow + ks * 32)) : bf16x8{};
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) st.o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    st.m = -INFINITY;
+    st.l = 0.f;
+    st.lim = off;
+  }
+  // the selection in LDS stands in for the token's row of block indices
+  const int nblk = build_union_list<kSelWaves * 64>(bmask, blist, n_list, tk, 0, 0, off, qb, s, wave, lane);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) st.qf[ks] = settle(st.qf[ks]);
+  const int e_lo = static_cast<int>(static_cast<long long>(split) * nblk / s.nsplit);
+  const int e_hi = static_cast<int>(static_cast<long long>(split + 1) * nblk / s.nsplit);
+  const SparseLane spl = sparse_lane(hl, gq);
+  auto entry_at = [&](int e) -> uint32_t { return e < nblk ? static_cast<uint32_t>(blist[e]) : 0u; };
+  stream_pairs<kSelWaves, false, 8>(smem, src, e_lo, e_hi, entry_at, wave, lane,
+                                    [&](const unsigned char* const* stg, const int* js, uint32_t cur0, uint32_t cur1) {
+    const uint32_t bit = 1u << (16 + wave);  // only wave 0's token is a member
+    attend_pair(st, spl, stg, js, (cur0 & bit) != 0u, (cur1 & bit) != 0u, lane, sl2);
+  });
+
+  const float l = sum_xor32(sum_xor16(st.l));
+  if (wave != 0 || hl >= s.G) return;
+  const int h = g * s.G + hl;
+  const size_t row = static_cast<size_t>(b * s.H_q + h) * s.S_q;
+  if (s.nsplit > 1) {  // unnormalised partial of this split, merged by the combine kernel
+    float* pr = part + (static_cast<size_t>(split) * s.B * s.H_q * s.S_q + row) * kPartFloats;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<floatx4*>(pr + 16 * dt + 4 * gq) = st.o[dt];
+    if (gq == 0) {
+      pr[128] = st.m;
+      pr[129] = l;
+    }
+    return;
+  }
+  const float inv = 1.f / l;
+  uint16_t* orow = out + row * kD + 4 * gq;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+    *reinterpret_cast<u32x2*>(orow + 16 * dt) = u32x2{pack_bf16x2(st.o[dt][0] * inv, st.o[dt][1] * inv),
+                                                     pack_bf16x2(st.o[dt][2] * inv, st.o[dt][3] * inv)};
+  if (lse && gq == 0) lse[row] = (st.m + log2f(l)) * kLn2;
+}
+
+hipError_t launch_decode_select_attn(const uint16_t* q, const uint16_t* k_cmp, const uint16_t* k, const uint16_t* v,
+                                     int32_t* blk_idx, float* blk_score, uint16_t* out, float* lse,
+                                     const AttnShape& s_in, void* workspace, hipStream_t stream) {
+  if (s_in.B == 0) return hipSuccess;
+  AttnShape s = s_in;
+  s.nsplit = sparse_splits(s.B, s.H_kv, s.S_q, s.topk);
+  float* part = s.nsplit > 1 ? static_cast<float*>(workspace) : nullptr;
+  const size_t lds = static_cast<size_t>(kStages) * kStageBytes + sparse_list_bytes(s.NB) +
+                     static_cast<size_t>(s.topk) * 8;
+  const dim3 grid(s.B * s.H_kv, s.nsplit);
+  if (s.block_table)
+    hipLaunchKernelGGL(decode_select_attn_kernel<true>, grid, dim3(kSelWaves * 64), lds, stream, q, k_cmp, k, v,
+                       blk_idx, blk_score, out, lse, part, s);
+  else
+    hipLaunchKernelGGL(decode_select_attn_kernel<false>, grid, dim3(kSelWaves * 64), lds, stream, q, k_cmp, k, v,
+                       blk_idx, blk_score, out, lse, part, s);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || s.nsplit == 1) return err;
+  return launch_combine_splits(part, out, lse, s, stream);
 }
 
 template <int R>
@@ -822,7 +962,7 @@ hipError_t launch_select_blocks(const uint16_t* q, const uint16_t* k_cmp, int32_
   if (s.B == 0 || s.S_q == 0) return hipSuccess;
   if (s.S_q == 1 && lse_stride == 1 && s.NB <= kSelWaves * kDecTiles * 16) {
     // one query per sequence: the workgroup splits its blocks
-    const size_t lds = kDecQBytes + (static_cast<size_t>(kSelWaves) * kMaxG * 2 + sel_stride(s.NB)) * sizeof(float);
+    const size_t lds = decode_select_lds(s.NB);
     hipLaunchKernelGGL(select_decode_kernel, dim3(s.B * s.H_kv), dim3(64 * kSelWaves), lds, stream, q, k_cmp,
                        blk_idx, blk_score, s);
     return hipGetLastError();
