@@ -317,6 +317,16 @@ int infv2_attn_fwd(const void* q, const void* k, const void* v, void* out, float
 
   st = infv2_compress_k(k, k_cmp, B, H_kv, S_k, D, block_size, stream);
   if (st != INFV2_OK) return st;
+  if (S_q == 1 && topk > 0 && num_blocks(S_k, block_size) <= kMaxDecodeSelectBlocks) {
+    // one query row per KV head (decode): selection and attention in one
+    // launch, the same results as the two calls below
+    const AttnShape s = make_shape(B, H_q, H_kv, S_q, S_k, block_size, topk, n_init, n_local,
+                                   scale_log2(softmax_scale, D), 1);
+    return hip_status(infv2::launch_decode_select_attn(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cmp), static_cast<const uint16_t*>(k),
+        static_cast<const uint16_t*>(v), idx, nullptr, static_cast<uint16_t*>(out), lse, s, rest,
+        static_cast<hipStream_t>(stream)));
+  }
   if (topk > 0) {
     st = infv2_select_blocks(q, k_cmp, idx, nullptr, B, H_q, H_kv, S_q, S_k, D, block_size, topk, n_init,
                              n_local, softmax_scale, stream);
