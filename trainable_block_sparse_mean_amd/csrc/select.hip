@@ -8,8 +8,8 @@
 // summary, Technical Mechanism).
 //
 // One workgroup = 16 consecutive query tokens of one KV head, one token per
-// wave (8 tokens and waves up to 512 key blocks, two workgroups per CU, and
-// past 2048 key blocks).  The compressed keys stream
+// wave (8 tokens and waves up to 512 key blocks and from 1537 to 2048, two
+// workgroups per CU, and past 2048 key blocks).  The compressed keys stream
 // through a 4-slot LDS ring of CH-block chunks by direct-to-LDS loads, in
 // pairs: while one pair is read the next is in flight, one barrier per pair.
 // Every wave reads the same chunk, so each chunk comes from L2 once per
@@ -46,17 +46,18 @@ constexpr float kSelSlack = 8.f;         // log2 units a running max may lag
 // floats per token row of block scores in LDS
 __host__ __device__ constexpr int sel_stride(int NB) { return (NB + 3) & ~3; }
 
-template <int CH, int WAVES = kSelWaves>
+template <int CH, int WAVES = kSelWaves, int SL = kSelSlots>
 constexpr size_t select_lds(int NB) {
-  return static_cast<size_t>(kSelSlots) * CH * kSelRowBytes + static_cast<size_t>(WAVES) * sel_stride(NB) * 4;
+  return static_cast<size_t>(SL) * CH * kSelRowBytes + static_cast<size_t>(WAVES) * sel_stride(NB) * 4;
 }
 // Workgroups of 8 tokens (8 waves): up to 512 blocks two of them (64-block
-// chunks) share a CU; past 2048 blocks, where the score rows of 16 tokens no
+// chunks) share a CU, and from 1537 to 2048 blocks two of them with a ring of
+// two 32-block chunks; past 2048 blocks, where the score rows of 16 tokens no
 // longer fit beside the ring, one of them (32-block chunks) takes up to 4064.
 constexpr int kSelWideWaves = 8;
 static_assert(select_lds<64, kSelWideWaves>(512) <= kSelLdsMax / 2, "two 8-token workgroups of 512 blocks fit");
+static_assert(select_lds<32, kSelWideWaves, 2>(2048) <= kSelLdsMax / 2, "two 8-token workgroups of 2048 blocks fit");
 static_assert(select_lds<32, kSelWideWaves>(kMaxSparseBlocks) <= kSelLdsMax, "8 score rows of 4064 blocks fit");
-static_assert(select_lds<32>(2048) <= kSelLdsMax, "16 score rows of 2048 blocks fit");
 
 // (max, sum of exp2 relative to the max) of the lanes l and l ^ mask within
 // a 16-lane DPP row; dpp = row_ror control.  Both partners compute the same
@@ -236,8 +237,10 @@ __device__ __forceinline__ void topk_row(float* cand, int nC, int topk, int firs
 // group for its visible count), so it streams 1/R of the compressed keys.
 // WAVES: tokens per workgroup (16 or 8).  MINB: workgroups a CU holds at
 // once (2 holds the registers of a wave to 128, so that two 8-wave
-// workgroups share a CU and one's top-k overlaps the other's passes).
-template <int CH, int R, int WAVES = kSelWaves, int MINB = 1>
+// workgroups share a CU and one's top-k overlaps the other's passes).  SL:
+// chunk slots in the ring (4: pairs of chunks, one barrier per pair; 2: one
+// chunk at a time, to fit two workgroups' score rows of up to 2048 blocks).
+template <int CH, int R, int WAVES = kSelWaves, int MINB = 1, int SL = kSelSlots>
 __global__ __launch_bounds__(WAVES * 64, MINB) void select_blocks_kernel(const uint16_t* __restrict__ q,
                                                                        const uint16_t* __restrict__ kc,
                                                                        int32_t* __restrict__ blk_idx,
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void select_blocks_kernel(const u
   constexpr int kDmaWaves = CH / 4;             // each moves 4 rows (1 KB) of a chunk
   extern __shared__ __align__(16) unsigned char sel_smem[];
   const uint32_t ring = lds_addr(sel_smem);
-  float* sig_all = reinterpret_cast<float*>(sel_smem + kSelSlots * kSlotBytes);
+  float* sig_all = reinterpret_cast<float*>(sel_smem + SL * kSlotBytes);
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar) from here on
   const int lane = threadIdx.x & 63;
@@ -298,11 +301,11 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void select_blocks_kernel(const u
     if ((kDmaWaves >= WAVES || wave / kDmaWaves == (it & 1)) && it < nit) {
       const int j = min(it < nch1 ? R * (it * CH + drow) : (it - nch1) * CH + drow, s.NB - 1);
       dma16(kg, static_cast<uint32_t>(j) * kSelRowBytes + dcol,
-            ring + (it % kSelSlots) * kSlotBytes + dwave * 1024);
+            ring + (it % SL) * kSlotBytes + dwave * 1024);
       if constexpr (kDmaWaves == 2 * WAVES) {
         const int j2 = min(it < nch1 ? R * (it * CH + drow + 32) : (it - nch1) * CH + drow + 32, s.NB - 1);
         dma16(kg, static_cast<uint32_t>(j2) * kSelRowBytes + dcol,
-              ring + (it % kSelSlots) * kSlotBytes + (dwave + WAVES) * 1024);
+              ring + (it % SL) * kSlotBytes + (dwave + WAVES) * 1024);
       }
     }
   };
@@ -417,7 +420,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void select_blocks_kernel(const u
         lse2[i] = 4 * gq + i < s.G ? mm + log2f(ll) : INFINITY;
       }
     }
-    const unsigned char* buf = sel_smem + (it % kSelSlots) * kSlotBytes;
+    const unsigned char* buf = sel_smem + (it % SL) * kSlotBytes;
     if (it < nch1) {
       // pass 1 over rows jc .. jc + CH - 1 of the sampled sequence: sampled
       // row x is block R * x, standing for blocks R*x .. R*x + R-1 that are
@@ -471,15 +474,25 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void select_blocks_kernel(const u
     }
   };
 
-  stage(0);
-  stage(1);
-  for (int it = 0; it < nit; it += 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // chunks it, it + 1 are in LDS; every wave is done with it - 2, it - 1
-    stage(it + 2);    // into the slots chunks it - 2, it - 1 used
-    stage(it + 3);
-    chunk(it);
-    if (it + 1 < nit) chunk(it + 1);
+  if constexpr (SL == 2) {  // one chunk at a time (two workgroups per CU cover the waits)
+    stage(0);
+    for (int it = 0; it < nit; ++it) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // chunk it is in LDS; every wave is done with it - 1
+      stage(it + 1);    // into the slot chunk it - 1 used
+      chunk(it);
+    }
+  } else {  // pairs of chunks, one barrier per pair
+    stage(0);
+    stage(1);
+    for (int it = 0; it < nit; it += 2) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // chunks it, it + 1 are in LDS; every wave is done with it - 2, it - 1
+      stage(it + 2);    // into the slots chunks it - 2, it - 1 used
+      stage(it + 3);
+      chunk(it);
+      if (it + 1 < nit) chunk(it + 1);
+    }
   }
 
   if (!active || s.topk == 0) return;  // no barriers below
@@ -947,9 +960,12 @@ static hipError_t launch_select_r(const uint16_t* q, const uint16_t* k_cmp, int3
   } else if (select_lds<64>(s.NB) <= kSelLdsMax) {  // 16-token workgroups, 64-block chunks
     hipLaunchKernelGGL((select_blocks_kernel<64, R>), grid(kSelWaves), dim3(64 * kSelWaves), select_lds<64>(s.NB),
                        stream, q, k_cmp, blk_idx, blk_score, s);
-  } else if (select_lds<32>(s.NB) <= kSelLdsMax) {  // up to 2048 blocks: 32-block chunks
-    hipLaunchKernelGGL((select_blocks_kernel<32, R>), grid(kSelWaves), dim3(64 * kSelWaves), select_lds<32>(s.NB),
-                       stream, q, k_cmp, blk_idx, blk_score, s);
+  } else if (select_lds<32, kSelWideWaves, 2>(s.NB) <= kSelLdsMax / 2) {
+    // up to 2048 blocks: 8-token workgroups, two per CU, one 32-block chunk at
+    // a time (128k: 3.68 -> 3.44 ms against 16-token workgroups of chunk pairs)
+    hipLaunchKernelGGL((select_blocks_kernel<32, R, kSelWideWaves, 2, 2>), grid(kSelWideWaves),
+                       dim3(64 * kSelWideWaves), (select_lds<32, kSelWideWaves, 2>(s.NB)), stream, q, k_cmp, blk_idx,
+                       blk_score, s);
   } else {  // 2049 .. 4064 blocks: 8-token workgroups, one per CU
     hipLaunchKernelGGL((select_blocks_kernel<32, R, kSelWideWaves>), grid(kSelWideWaves), dim3(64 * kSelWideWaves),
                        (select_lds<32, kSelWideWaves>(s.NB)), stream, q, k_cmp, blk_idx, blk_score, s);
