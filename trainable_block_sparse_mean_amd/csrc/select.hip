@@ -7,13 +7,14 @@
 // selected_attention (top-k per query position) at block granularity (news
 // summary, Technical Mechanism).
 //
-// One workgroup = 16 consecutive query tokens of one KV head, one token per
-// wave (8 tokens and waves up to 512 key blocks and from 1537 to 2048, two
-// workgroups per CU, and past 2048 key blocks).  The compressed keys stream
-// through a 4-slot LDS ring of CH-block chunks by direct-to-LDS loads, in
-// pairs: while one pair is read the next is in flight, one barrier per pair.
-// Every wave reads the same chunk, so each chunk comes from L2 once per
-// workgroup and pass.  For a token, S = Q k_cmp^T on 16x16x32 bf16 MFMAs puts
+// One workgroup = 8 consecutive query tokens of one KV head, one token per
+// wave; two workgroups share a CU up to 2048 key blocks (one past that), so
+// that one's top-k, a scalar loop on one wave per token, overlaps the other's
+// score passes.  The compressed keys stream through an LDS ring of CH-block
+// chunks by direct-to-LDS loads: 4 slots in pairs (while one pair is read the
+// next is in flight, one barrier per pair) where two workgroups' score rows
+// leave room for it, else 2 slots, one chunk at a time.  Every wave reads
+// the same chunk, so each chunk comes from L2 once per workgroup and pass.  For a token, S = Q k_cmp^T on 16x16x32 bf16 MFMAs puts
 // the 16 heads of the group in the rows and 16 compressed blocks in the
 // columns: lane (column hl, row quad gq) holds heads 4*gq .. 4*gq+3 of block
 // 16*tile + hl.
@@ -37,7 +38,7 @@
 
 namespace infv2 {
 
-constexpr int kSelWaves = 16;           // = tokens per workgroup
+constexpr int kSelWaves = 16;           // waves of the decode selection (the prefill kernel takes WAVES)
 constexpr int kSelSlots = 4;            // LDS ring: the pair of chunks being read + the next pair
 constexpr int kSelRowBytes = kD * 2;    // one compressed block
 constexpr size_t kSelLdsMax = 160 * 1024;
@@ -50,12 +51,14 @@ template <int CH, int WAVES = kSelWaves, int SL = kSelSlots>
 constexpr size_t select_lds(int NB) {
   return static_cast<size_t>(SL) * CH * kSelRowBytes + static_cast<size_t>(WAVES) * sel_stride(NB) * 4;
 }
-// Workgroups of 8 tokens (8 waves): up to 512 blocks two of them (64-block
-// chunks) share a CU, and from 1537 to 2048 blocks two of them with a ring of
-// two 32-block chunks; past 2048 blocks, where the score rows of 16 tokens no
-// longer fit beside the ring, one of them (32-block chunks) takes up to 4064.
+// Workgroups of 8 tokens (8 waves), two per CU up to 2048 blocks: up to 512
+// blocks with a ring of 64-block chunk pairs, up to 1536 with one 64-block
+// chunk at a time, up to 2048 with one 32-block chunk at a time, so that both
+// workgroups' score rows fit; past 2048 blocks one workgroup per CU (32-block
+// chunk pairs) takes up to 4064.
 constexpr int kSelWideWaves = 8;
 static_assert(select_lds<64, kSelWideWaves>(512) <= kSelLdsMax / 2, "two 8-token workgroups of 512 blocks fit");
+static_assert(select_lds<64, kSelWideWaves, 2>(1536) <= kSelLdsMax / 2, "two 8-token workgroups of 1536 blocks fit");
 static_assert(select_lds<32, kSelWideWaves, 2>(2048) <= kSelLdsMax / 2, "two 8-token workgroups of 2048 blocks fit");
 static_assert(select_lds<32, kSelWideWaves>(kMaxSparseBlocks) <= kSelLdsMax, "8 score rows of 4064 blocks fit");
 
@@ -957,9 +960,13 @@ static hipError_t launch_select_r(const uint16_t* q, const uint16_t* k_cmp, int3
     hipLaunchKernelGGL((select_blocks_kernel<64, R, kSelWideWaves, 2>), grid(kSelWideWaves),
                        dim3(64 * kSelWideWaves), (select_lds<64, kSelWideWaves>(s.NB)), stream, q, k_cmp, blk_idx,
                        blk_score, s);
-  } else if (select_lds<64>(s.NB) <= kSelLdsMax) {  // 16-token workgroups, 64-block chunks
-    hipLaunchKernelGGL((select_blocks_kernel<64, R>), grid(kSelWaves), dim3(64 * kSelWaves), select_lds<64>(s.NB),
-                       stream, q, k_cmp, blk_idx, blk_score, s);
+  } else if (select_lds<64, kSelWideWaves, 2>(s.NB) <= kSelLdsMax / 2) {
+    // up to 1536 blocks: the same with one 64-block chunk at a time, so that
+    // two workgroups' score rows fit (64k: 1.00 -> 0.94 ms against 16-token
+    // workgroups of chunk pairs)
+    hipLaunchKernelGGL((select_blocks_kernel<64, R, kSelWideWaves, 2, 2>), grid(kSelWideWaves),
+                       dim3(64 * kSelWideWaves), (select_lds<64, kSelWideWaves, 2>(s.NB)), stream, q, k_cmp, blk_idx,
+                       blk_score, s);
   } else if (select_lds<32, kSelWideWaves, 2>(s.NB) <= kSelLdsMax / 2) {
     // up to 2048 blocks: 8-token workgroups, two per CU, one 32-block chunk at
     // a time (128k: 3.68 -> 3.44 ms against 16-token workgroups of chunk pairs)
