@@ -57,6 +57,11 @@ SELECT_CASES = [
     ("switch_4k_g16", workloads.SWITCH_SPARSE.with_(S_q=4096, S_k=4096, switch_len=0), np.arange(0, 4096, 5)),
     ("ragged_sq37_sk3000", workloads.TINY.with_(H_q=32, H_kv=2, S_q=37, S_k=3000, topk=9), None),
     ("g4_topk40", workloads.TINY.with_(H_q=8, H_kv=2, S_q=1500, S_k=1500, topk=40, n_init=2, n_local=3), None),
+    # 513-1536 blocks: 8-token workgroups two per CU, one 64-block chunk at a
+    # time (ragged last workgroup and chunk; 11 slots per lane in the top-k)
+    ("mid_650blk_sq45", workloads.TINY.with_(H_q=32, H_kv=2, S_q=45, S_k=650 * 64 + 17, topk=64), None),
+    # 1537-2048 blocks: the same with one 32-block chunk at a time
+    ("mid_1700blk_sq30", workloads.TINY.with_(H_q=16, H_kv=1, S_q=30, S_k=1700 * 64 + 5, topk=100, n_init=2), None),
     # past 2048 blocks: the 8-token workgroups (ragged last workgroup), up to
     # 2100 candidates per row (33 slots per lane in the top-k)
     ("wide_2100blk_sq700", workloads.TINY.with_(H_q=32, H_kv=2, S_q=700, S_k=2100 * 64, topk=64), None),

@@ -31,6 +31,9 @@ CASES = [
     ("switch_4k_g16", workloads.SWITCH_SPARSE.with_(S_q=4096, S_k=4096, switch_len=0), np.arange(0, 4096, 7)),
     ("ragged_sq37_sk3000", workloads.TINY.with_(H_q=32, H_kv=2, S_q=37, S_k=3000, topk=9), None),
     ("wide_2100blk_sq70", workloads.TINY.with_(H_q=32, H_kv=2, S_q=70, S_k=2100 * 64, topk=64), None),
+    # the two-slot rings of 64- and 32-block chunks (513-1536 and 1537-2048 blocks)
+    ("mid_900blk_sq21", workloads.TINY.with_(H_q=32, H_kv=2, S_q=21, S_k=900 * 64 + 3, topk=64), None),
+    ("mid_1800blk_sq19", workloads.TINY.with_(H_q=16, H_kv=1, S_q=19, S_k=1800 * 64 + 40, topk=64), None),
 ]
 
 
