@@ -251,6 +251,8 @@ FUSED_CASES = LEN_CASES + [
     ("b16_32k", [32768 - 37 * b for b in range(16)], 32, 2, 64),
     ("over_512_candidates", [64 * 520 + 7, 65600, 131072, 100001], 16, 1, 250),
     ("topk0", [3000, 70, 129], 8, 2, 0),
+    # 64 sequences x 2 KV heads: one split per head, the output written directly
+    ("b64_one_split", [400 + 23 * b for b in range(64)], 8, 2, 8),
 ]
 
 
