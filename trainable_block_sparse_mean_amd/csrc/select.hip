@@ -47,7 +47,7 @@ constexpr float kSelSlack = 8.f;         // log2 units a running max may lag
 // floats per token row of block scores in LDS
 __host__ __device__ constexpr int sel_stride(int NB) { return (NB + 3) & ~3; }
 
-template <int CH, int WAVES = kSelWaves, int SL = kSelSlots>
+template <int CH, int WAVES, int SL = kSelSlots>
 constexpr size_t select_lds(int NB) {
   return static_cast<size_t>(SL) * CH * kSelRowBytes + static_cast<size_t>(WAVES) * sel_stride(NB) * 4;
 }
@@ -243,7 +243,7 @@ __device__ __forceinline__ void topk_row(float* cand, int nC, int topk, int firs
 // workgroups share a CU and one's top-k overlaps the other's passes).  SL:
 // chunk slots in the ring (4: pairs of chunks, one barrier per pair; 2: one
 // chunk at a time, to fit two workgroups' score rows of up to 2048 blocks).
-template <int CH, int R, int WAVES = kSelWaves, int MINB = 1, int SL = kSelSlots>
+template <int CH, int R, int WAVES, int MINB = 1, int SL = kSelSlots>
 __global__ __launch_bounds__(WAVES * 64, MINB) void select_blocks_kernel(const uint16_t* __restrict__ q,
                                                                        const uint16_t* __restrict__ kc,
                                                                        int32_t* __restrict__ blk_idx,
@@ -288,20 +288,18 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void select_blocks_kernel(const u
   }
   const uint16_t* kg = kc + static_cast<size_t>(b * s.H_kv + g) * s.NB * kD;
 
-  // chunk loads: loader wave d < kDmaWaves of a chunk moves rows 4d .. 4d+3;
+  // chunk loads: row group d < kDmaWaves of a chunk is rows 4d .. 4d+3;
   // lane (sub, slot) fetches 16-byte column slot ^ swz(row) of row 4d + sub
   // into that row's slot (rows past NB - 1 re-read row NB - 1; never used).
-  // With 8 loader waves per chunk and 16 waves, waves 0-7 load the even
-  // chunks and waves 8-15 the odd ones; with as many loader waves as waves,
-  // every wave loads one row group of each chunk; with 16 row groups and 8
-  // waves, wave d loads groups d and d + 8 (rows 32 further: same swizzle).
-  static_assert(kDmaWaves == WAVES || 2 * kDmaWaves == WAVES || kDmaWaves == 2 * WAVES, "loader waves per chunk");
+  // Wave d loads group d of every chunk, and with 16 groups (64-block chunks)
+  // and 8 waves also group d + 8 (rows 32 further: the same swizzle).
+  static_assert(kDmaWaves == WAVES || kDmaWaves == 2 * WAVES, "loader waves per chunk");
   const int dwave = wave % kDmaWaves;
   const int drow = 4 * dwave + (lane >> 4);
   const uint32_t dcol = static_cast<uint32_t>(((lane & 15) ^ swz(drow)) << 4);
   const int nit = nch1 + nch;  // pass 1 chunks, then pass 2 chunks
   auto stage = [&](int it) {
-    if ((kDmaWaves >= WAVES || wave / kDmaWaves == (it & 1)) && it < nit) {
+    if (it < nit) {
       const int j = min(it < nch1 ? R * (it * CH + drow) : (it - nch1) * CH + drow, s.NB - 1);
       dma16(kg, static_cast<uint32_t>(j) * kSelRowBytes + dcol,
             ring + (it % SL) * kSlotBytes + dwave * 1024);
@@ -515,14 +513,14 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void select_blocks_kernel(const u
     }
     return;
   }
-  const int nIt = (nC + 63) / 64;  // candidate slots per lane (<= 32 with 16 waves, <= 64 with 8)
+  const int nIt = (nC + 63) / 64;  // candidate slots per lane (<= 32 up to 2048 blocks, <= 64 past)
   if (nIt <= 1) topk_row<1>(sig + lo, nC, s.topk, lo, out, out_s, lane);
   else if (nIt <= 2) topk_row<2>(sig + lo, nC, s.topk, lo, out, out_s, lane);
   else if (nIt <= 4) topk_row<4>(sig + lo, nC, s.topk, lo, out, out_s, lane);
   else if (nIt <= 8) topk_row<8>(sig + lo, nC, s.topk, lo, out, out_s, lane);
   else if (nIt <= 16) topk_row<16>(sig + lo, nC, s.topk, lo, out, out_s, lane);
-  else if (WAVES == kSelWaves || MINB > 1 || nIt <= 32) topk_row<32>(sig + lo, nC, s.topk, lo, out, out_s, lane);
-  else if constexpr (WAVES != kSelWaves && MINB == 1) topk_row<64>(sig + lo, nC, s.topk, lo, out, out_s, lane);
+  else if (MINB > 1 || nIt <= 32) topk_row<32>(sig + lo, nC, s.topk, lo, out, out_s, lane);
+  else if constexpr (MINB == 1) topk_row<64>(sig + lo, nC, s.topk, lo, out, out_s, lane);
 }
 
 // Exact top-kk of nC (<= 2 * 1024) candidates cand[0 .. nC) by all 16 waves
