@@ -833,8 +833,8 @@ __global__ __launch_bounds__(kSelWaves * 64) void select_decode_kernel(const uin
 // on 32 CUs and read its result back.  Then it attends split `split` of the
 // token's union of blocks, as the split-KV sparse kernel does (the same item
 // code, list and partials), and split 0 also stores the selection for the
-// caller.  LDS: the 4-stage ring, the union list, then the top-k (indices and
-// scores); the selection's own scratch overlays the ring.
+// caller.  LDS: the 4-stage ring, then the top-k (indices and scores); the
+// selection's own scratch overlays the ring.
 // ---------------------------------------------------------------------------
 static_assert(decode_select_lds(kMaxDecodeSelectBlocks) <= static_cast<size_t>(kStages) * kStageBytes,
               "the selection's scratch fits in the ring");
@@ -845,12 +845,8 @@ __global__ __launch_bounds__(kSelWaves * 64, 1) void decode_select_attn_kernel(
     const uint16_t* __restrict__ v, int32_t* __restrict__ blk_idx, float* __restrict__ blk_score,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part, AttnShape s) {
   extern __shared__ __align__(1024) unsigned char smem[];
-  const size_t list_off = static_cast<size_t>(kStages) * kStageBytes;
-  uint32_t* bmask = reinterpret_cast<uint32_t*>(smem + list_off);  // [NB]
-  int* blist = reinterpret_cast<int*>(bmask + s.NB);                // [NB]
-  int* n_list = blist + s.NB;
-  int32_t* tk = reinterpret_cast<int32_t*>(smem + list_off + sparse_list_bytes(s.NB));  // [topk]
-  float* ts = reinterpret_cast<float*>(tk + s.topk);                                     // [topk]
+  int32_t* tk = reinterpret_cast<int32_t*>(smem + static_cast<size_t>(kStages) * kStageBytes);  // [topk]
+  float* ts = reinterpret_cast<float*>(tk + s.topk);                                            // [topk]
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -891,14 +887,27 @@ __global__ __launch_bounds__(kSelWaves * 64, 1) void decode_select_attn_kernel(
     st.l = 0.f;
     st.lim = off;
   }
-  // the selection in LDS stands in for the token's row of block indices
-  const int nblk = build_union_list<kSelWaves * 64>(bmask, blist, n_list, tk, 0, 0, off, qb, s, wave, lane);
+  // The token's attended blocks in ascending order, without a list: the
+  // initial blocks 0 .. n_i-1, then the selection (ascending, distinct, all
+  // in n_init .. qb - n_local, so apart from the forced blocks), then the
+  // window blocks w0 .. qb (those not already initial blocks): the union the
+  // separate attention call builds from the same indices, in the same order.
+  const int n_i = min(s.n_init, qb + 1);
+  const int w0 = max(s.n_init, qb - s.n_local + 1);
+  const int n_w = max(0, qb - w0 + 1);
+  const int nC = max(0, qb - s.n_local - s.n_init + 1);  // the selection's candidates
+  const int n_t = min(s.topk, nC);                      // and its valid entries
+  const int nblk = n_i + n_t + n_w;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) st.qf[ks] = settle(st.qf[ks]);
   const int e_lo = static_cast<int>(static_cast<long long>(split) * nblk / s.nsplit);
   const int e_hi = static_cast<int>(static_cast<long long>(split + 1) * nblk / s.nsplit);
   const SparseLane spl = sparse_lane(hl, gq);
-  auto entry_at = [&](int e) -> uint32_t { return e < nblk ? static_cast<uint32_t>(blist[e]) : 0u; };
+  auto entry_at = [&](int e) -> uint32_t {  // block | wave 0's token as its one member
+    if (e >= nblk) return 0u;
+    const int j = e < n_i ? e : e < n_i + n_t ? tk[e - n_i] : w0 + (e - n_i - n_t);
+    return static_cast<uint32_t>(j) | (1u << 16);
+  };
   stream_pairs<kSelWaves, false, 8>(smem, src, e_lo, e_hi, entry_at, wave, lane,
                                     [&](const unsigned char* const* stg, const int* js, uint32_t cur0, uint32_t cur1) {
     const uint32_t bit = 1u << (16 + wave);  // only wave 0's token is a member
@@ -935,8 +944,7 @@ hipError_t launch_decode_select_attn(const uint16_t* q, const uint16_t* k_cmp, c
   AttnShape s = s_in;
   s.nsplit = sparse_splits(s.B, s.H_kv, s.S_q, s.topk);
   float* part = s.nsplit > 1 ? static_cast<float*>(workspace) : nullptr;
-  const size_t lds = static_cast<size_t>(kStages) * kStageBytes + sparse_list_bytes(s.NB) +
-                     static_cast<size_t>(s.topk) * 8;
+  const size_t lds = static_cast<size_t>(kStages) * kStageBytes + static_cast<size_t>(s.topk) * 8;
   const dim3 grid(s.B * s.H_kv, s.nsplit);
   if (s.block_table)
     hipLaunchKernelGGL(decode_select_attn_kernel<true>, grid, dim3(kSelWaves * 64), lds, stream, q, k_cmp, k, v,
