@@ -279,12 +279,14 @@ def test_decode_select_attn_fused_equals_two_calls(name, lens, H_q, H_kv, topk):
         if topk > 0:
             assert torch.equal(fi, idx)
             assert torch.equal(fs, score)
-    for n in (4, 5):  # the other forced blocks
+    # the other forced blocks; (3, 1) gives sequences shorter than their
+    # initial blocks and (2, 5) windows that reach below block 0 (short_mix)
+    for ni, nl in ((0, 2), (1, 3), (3, 1), (2, 5)):
         if topk == 0:
             break
-        i2 = tb.decode_select(c["q"], k_cmp, c["lens"], topk, n_init=n - 4, n_local=n - 2)
-        o2, l2 = tb.decode_attn(c["q"], c["kp"], c["vp"], c["table"], c["lens"], i2, n_init=n - 4, n_local=n - 2)
+        i2 = tb.decode_select(c["q"], k_cmp, c["lens"], topk, n_init=ni, n_local=nl)
+        o2, l2 = tb.decode_attn(c["q"], c["kp"], c["vp"], c["table"], c["lens"], i2, n_init=ni, n_local=nl)
         fo, fl, fi = tb.decode_select_attn(c["q"], k_cmp, c["kp"], c["vp"], c["table"], c["lens"], topk,
-                                           n_init=n - 4, n_local=n - 2)
+                                           n_init=ni, n_local=nl)
         torch.cuda.synchronize()
         assert torch.equal(fi, i2) and torch.equal(fl, l2) and np.array_equal(bits_np(fo), bits_np(o2))
